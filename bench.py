@@ -1,0 +1,260 @@
+"""Throughput of the TokenGate gated-prefill hot path on one MI355X.
+
+One step = one pass of the whole path over one prompt (batch 1):
+    tg_gate_score -> tg_select_topk -> tg_compact -> tg_rope (q, k) -> tg_gated_attention
+at the Qwen3-1.7B-shaped gate layer: d_model 2048, scorer 2048->256->1,
+N = 16384 tokens (last 64 forced-keep), K = 2048 kept, 16 q / 8 kv heads,
+head_dim 128, one upper layer of token-gated attention.  Inputs are seeded
+synthetic tensors already resident in HBM; the residual is rotated over six
+copies (384 MB > the 256 MB MALL) so the scorer reads it from HBM.
+
+Prints one JSON line.  `value` = N / (ms_per_step) in tokens/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "gated-prefill tokens/s at N=16k Qwen3-1.7B shape; attn MFMA % of bf16 peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+N_RESID_COPIES = 6
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="n16k",
+                   choices=["n16k", "n32k-k1024", "n32k-k4096", "n32k-k8192", "n128k", "full16k", "tiny"])
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="also run one plain device copy of this many MiB (counter calibration)")
+    return p.parse_args()
+
+
+def workload(name):
+    from learned_token_pruning_mlp_amd import synth
+    base = synth.QWEN3_1P7B_N16K
+    if name == "n16k":
+        return base, "qwen3-1.7b gate layer, N=16384, F=64, K=2048, 1 upper layer"
+    if name.startswith("n32k"):
+        k = int(name.split("k")[-1])
+        shp = synth.GateShape(**{**base.__dict__, "n": 32768, "k": k})
+        return shp, f"qwen3-1.7b gate layer, N=32768, F=64, K={k}, 1 upper layer"
+    if name == "n128k":
+        return synth.QWEN3_1P7B_N128K, "qwen3-1.7b gate layer, N=131072, F=128, K=8192, 1 upper layer"
+    if name == "full16k":
+        shp = synth.GateShape(**{**base.__dict__, "k": base.n})
+        return shp, "qwen3-1.7b gate layer, N=16384, K=N (no pruning), 1 upper layer"
+    return synth.TINY, "tiny gate layer, N=512, d=256, K=128"
+
+
+def attn_flops(shp):
+    return 4.0 * shp.hq * shp.head_dim * shp.k * (shp.k + 1) / 2.0
+
+
+def gate_bytes(shp):
+    # residual read once, W1 once, b1/w2 tiny, raw + normalised scores written/read
+    return shp.n * shp.d * 2 + shp.hd * shp.d * 2 + shp.n * 4 * 3
+
+
+def compact_bytes(shp):
+    # kept residual rows read + written, index, position and score per kept row
+    return shp.k * (shp.d * 2 * 2 + 4 * 4)
+
+
+def source_sha(name):
+    path = os.path.join(ROOT, "learned_token_pruning_mlp_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel_file, workload_name):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+        ent = data.get(workload_name, {}).get(kernel_file)
+        if not ent or ent.get("source_sha") != source_sha(kernel_file):
+            return None
+        return ent["hbm_bytes_per_launch"]
+    except Exception:
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build runs on a single MI355X "
+              "(see the sharding notes in the design document); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from learned_token_pruning_mlp_amd import binding as tg
+    from learned_token_pruning_mlp_amd import synth
+
+    tg.load()
+    dev = torch.device("cuda:0")
+    shp, desc = workload(args.workload)
+    seed = 2
+
+    def bf(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---- inputs, resident in HBM before timing
+    inp = synth.gate_inputs(shp, seed)
+    resid = [bf(inp.resid)]
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    for _ in range(N_RESID_COPIES - 1):
+        resid.append(torch.randn(resid[0].shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16))
+    w1, w2 = bf(inp.w1), bf(inp.w2)
+    forced = torch.from_numpy(inp.forced).to(dev)
+    pos = torch.from_numpy(inp.pos).to(dev)
+    n, k = shp.n, shp.k
+    a = synth.attn_inputs(k, shp.hq, shp.hkv, shp.head_dim, seed)
+    q, kk, vv = bf(a.q), bf(a.k), bf(a.v)
+    gains = torch.from_numpy(a.gains).to(dev)
+    # outputs and workspace
+    s_norm = torch.empty(n, dtype=torch.float32, device=dev)
+    ws = tg.workspace(n, dev)
+    kept = torch.empty(k, dtype=torch.int32, device=dev)
+    resid_k = torch.empty((k, shp.d), dtype=torch.bfloat16, device=dev)
+    pos_k = torch.empty(k, dtype=torch.int32, device=dev)
+    score_k = torch.empty(k, dtype=torch.float32, device=dev)
+    out = torch.empty((k, shp.hq, shp.head_dim), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    stages = ["gate_score", "select_topk", "compact", "rope", "gated_attention"]
+
+    def step(i, ev=None):
+        r = resid[i % N_RESID_COPIES]
+        if ev is not None:
+            ev[0].record(stream)
+        tg.tg_gate_score(r, w1, None, w2, 0.0, 1e-6, 1e-6, s_norm, None, ws)
+        if ev is not None:
+            ev[1].record(stream)
+        tg.tg_select_topk(s_norm, forced, shp.n_forced, k, kept, None, ws)
+        if ev is not None:
+            ev[2].record(stream)
+        tg.tg_compact(kept, n, r, resid_k, pos, pos_k, s_norm, score_k)
+        if ev is not None:
+            ev[3].record(stream)
+        tg.tg_rope(q, pos_k, shp.rope_theta)
+        tg.tg_rope(kk, pos_k, shp.rope_theta)
+        if ev is not None:
+            ev[4].record(stream)
+        tg.tg_gated_attention(q, kk, vv, score_k, gains, shp.temp_coef, pos_k, out)
+        if ev is not None:
+            ev[5].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` steps, synchronised on both sides
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    per_stage = {s: 0.0 for s in stages}
+    for e in evs:
+        for j, s in enumerate(stages):
+            per_stage[s] += e[j].elapsed_time(e[j + 1])
+    per_stage = {s: v / args.steps for s, v in per_stage.items()}  # ms per launch (rope: both calls)
+    event_ms = sum(per_stage.values())
+
+    # ---- roofline of the dominant kernel
+    dom = max(per_stage, key=per_stage.get)
+    if dom == "gated_attention":
+        achieved = attn_flops(shp) / (per_stage[dom] * 1e-3) / 1e12
+        roof = {"kernel": "gated_attn", "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": traffic_for("k_attn.hip", args.workload)}
+    elif dom == "gate_score":
+        achieved = gate_bytes(shp) / (per_stage[dom] * 1e-3) / 1e9
+        roof = {"kernel": "gate_mlp+gate_seqnorm", "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                "traffic": traffic_for("k_gate.hip", args.workload)}
+    else:
+        achieved = compact_bytes(shp) / (per_stage[dom] * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": None}
+    attn_tflops = attn_flops(shp) / (per_stage["gated_attention"] * 1e-3) / 1e12
+    gate_gbs = gate_bytes(shp) / (per_stage["gate_score"] * 1e-3) / 1e9
+
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    result = {
+        "metric": METRIC,
+        "value": n / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; random-init scorer weights, N(0,1) residual and q/k/v)",
+        "config": {"workload": desc, "n_tokens": n, "kept": k, "forced": shp.n_forced, "d_model": shp.d,
+                   "scorer_hidden": shp.hd, "q_heads": shp.hq, "kv_heads": shp.hkv, "head_dim": shp.head_dim,
+                   "batch": 1},
+        "attn_mfma_pct": 100.0 * attn_tflops / PEAK_BF16_TFLOPS,
+        "stage_us": {s: round(v * 1e3, 3) for s, v in per_stage.items()},
+        "stage_event_sum_ms": event_ms,
+        "attn_tflops": attn_tflops,
+        "gate_hbm_gbs": gate_gbs,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(shp, seed, inp, a)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(shp, seed, inp, a):
+    """The fp64 oracle, as it stands, over one full step of the same workload."""
+    from oracle import oracle
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    s_norm, _ = oracle.gate_score(inp.resid, inp.w1, inp.b1, inp.w2, inp.b2, nthreads=threads)
+    kept = oracle.select_topk(s_norm, inp.forced, shp.k)
+    oracle.gather_rows(inp.resid, kept)
+    qr = oracle.rope(a.q, kept, shp.rope_theta)
+    kr = oracle.rope(a.k, kept, shp.rope_theta)
+    oracle.gated_attention(qr, kr, a.v, s_norm[kept], a.gains, shp.temp_coef, kept, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": shp.n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"one full step of the same workload (N={shp.n}, K={shp.k}), fp64, {dt:.2f} s"}
+
+
+if __name__ == "__main__":
+    main()

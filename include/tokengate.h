@@ -1,0 +1,174 @@
+/*
+ * tokengate.h -- C ABI of the TokenGate gated-prefill hot path on MI355X (gfx950).
+ *
+ * The path runs at the gate layer L of a decoder and in the layers above it:
+ *   tg_gate_score      -> a small MLP scores every token's normalised residual,
+ *                         and the scores are RMS-normalised along the sequence;
+ *   tg_select_topk     -> forced-keep top-K picks the tokens that continue;
+ *   tg_compact         -> the kept rows, their original positions, their scores
+ *                         and any extra per-token streams (KV rows) are gathered;
+ *   tg_rope            -> (auxiliary) rotary embedding at the original positions;
+ *   tg_gated_attention -> causal attention over the kept tokens only, with a
+ *                         per-key importance bias and a per-query temperature.
+ *
+ * Sources (web pages on the method; cited by the key in brackets):
+ *  [P1] fluxbbs.com, "TokenGate 长上下文预填充提速 11.3 倍，斯坦福伯克利开源门控剪枝":
+ *       section "门控到底插在模型的哪个位置" (where the gate sits) and section
+ *       "端到端训练的关键在 token 门控注意力" (token-gated attention).
+ *  [P2] slinene.github.io paper digest, "TokenGate: Adapting LLMs for Fast and
+ *       Memory-Efficient Prefill with Learned Token Pruning": "方法关键点".
+ *  [P3] news.farwalk.ai, "斯坦福与 UC Berkeley 提出 TokenGate ...": "How does
+ *       TokenGate learned token pruning work?", "What is token-gated attention?",
+ *       "How do you deploy TokenGate?".
+ *  [P5] aiwillknow.com, "TokenGate：让模型学会跳读，而不只压缩 KV 缓存":
+ *       Figure 1(a)(b) and Figure 1(c) descriptions.
+ *
+ * Conventions for every entry point:
+ *  - bf16 tensors are passed as uint16_t bit patterns (tg_bf16).
+ *  - Every tensor pointer is DEVICE memory owned by the caller; the library
+ *    allocates nothing, keeps no state between calls, never synchronises the
+ *    stream and never reads device data back to the host.  Work is enqueued on
+ *    `stream` (a hipStream_t passed as void*; NULL = the null stream) and is
+ *    complete when the stream reaches that point.
+ *  - Arguments are checked on the host before anything is enqueued; a
+ *    negative status means nothing was enqueued (except TG_EDEVICE, which
+ *    reports a launch failure).
+ *  - Layouts are row-major and dense unless a stride is given.
+ *  - Batch size is 1 (one prompt per call), as in the pages' measurements.
+ */
+#ifndef TOKENGATE_H
+#define TOKENGATE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t tg_bf16;
+
+/* Status codes. */
+#define TG_OK 0
+#define TG_EINVAL (-1)        /* a size, budget or required pointer is invalid */
+#define TG_EUNSUPPORTED (-2)  /* a shape the kernels do not implement */
+#define TG_EALIGN (-3)        /* a pointer, row size or stride is not 16-byte aligned */
+#define TG_EWORKSPACE (-4)    /* workspace missing or smaller than tg_workspace_bytes */
+#define TG_EDEVICE (-5)       /* the HIP runtime rejected a launch */
+
+/* Bits written to the optional device status word of tg_select_topk. */
+#define TG_STATUS_FORCED_MISMATCH 1  /* forced-mask count differs from n_forced */
+#define TG_STATUS_FORCED_OVER_K 2    /* more forced tokens than k: only k kept */
+
+/* Upper limit on extra gather streams in one tg_compact call. */
+#define TG_MAX_GATHER 16
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char* tg_status_string(int status);
+
+/* ABI version of this header (incremented on incompatible change). */
+int tg_abi_version(void);
+
+/* Bytes of device workspace that tg_gate_score and tg_select_topk need for a
+ * prompt of n tokens.  Both take the same size; one buffer may serve both
+ * (not concurrently).  Alignment: 256 bytes. */
+size_t tg_workspace_bytes(int64_t n);
+
+/*
+ * tg_gate_score -- gate scoring network plus sequence RMSNorm
+ * [P1 gate][P2 method][P3 how][P5 Fig 1(a)(b)].
+ *   r_i  = 1 / sqrt(mean_k resid_ik^2 + eps_row)
+ *   a_ij = r_i * sum_k resid_ik w1_jk + b1_j
+ *   s_i  = sum_j w2_j GELU(a_ij) + b2              (GELU: exact erf form)
+ *   score_norm_i = s_i / sqrt(mean_i s_i^2 + eps_seq)
+ * resid      [n, d] bf16: post-attention residual of layer L (row stride d).
+ * w1         [hd, d] bf16: first scorer layer, with the elementwise weight of
+ *            the normalisation folded in by the caller (w1_jk * gamma_k).
+ * b1         [hd] bf16 or NULL (= 0).   w2 [hd] bf16.   b2: output bias.
+ * score_norm [n] fp32 out: normalised scores.
+ * score_raw  [n] fp32 out: raw scores s, or NULL.
+ * Supported: d % 64 == 0, hd in {64, 128, 256}; resid, w1 16-byte aligned.
+ * n == 0 is a no-op.  Workspace: tg_workspace_bytes(n).
+ * Results are deterministic (fixed reduction order, no float atomics).
+ */
+int tg_gate_score(const tg_bf16* resid, const tg_bf16* w1, const tg_bf16* b1, const tg_bf16* w2,
+                  float b2, int64_t n, int32_t d, int32_t hd, float eps_row, float eps_seq,
+                  float* score_norm, float* score_raw, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/*
+ * tg_select_topk -- forced-keep top-K [P1 gate][P2 method][P3 how][P5 Fig 1(a)(b)].
+ * Keeps every token with forced[i] != 0 and, among the others, the
+ * k - F with the largest score (ties to the lower index; -0.0 equals +0.0;
+ * NaN ranks below -inf).  k counts all kept tokens, forced ones included.
+ * score    [n] fp32.  forced [n] uint8 or NULL (no forced tokens).
+ * n_forced host-known number of forced tokens F (checked: 0 <= F <= k <= n, k >= 1).
+ * kept_idx [k] int32 out: kept indices in ascending order.
+ * dev_status optional device int32: receives TG_STATUS_* bits (0 = consistent).
+ *   The kernels use the forced count they find on the device; if it exceeds
+ *   k, the first k forced tokens are kept and TG_STATUS_FORCED_OVER_K is set.
+ * Workspace: tg_workspace_bytes(n).
+ */
+int tg_select_topk(const float* score, const uint8_t* forced, int64_t n, int64_t n_forced,
+                   int64_t k, int32_t* kept_idx, int32_t* dev_status, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* One extra per-token row stream for tg_compact: dst row t = src row kept_idx[t]. */
+typedef struct tg_gather {
+    const void* src;     /* device, src_stride bytes between rows, >= n rows */
+    void* dst;           /* device, dst_stride bytes between rows, >= k rows */
+    int64_t row_bytes;   /* bytes copied per row (multiple of 16) */
+    int64_t src_stride;  /* multiple of 16 */
+    int64_t dst_stride;  /* multiple of 16 */
+} tg_gather;
+
+/*
+ * tg_compact -- residual truncation and compaction [P1 gate][P3 how][P5 Fig 1(a)(b)]:
+ * pruned tokens stop at layer L; the kept ones continue with their original
+ * position ids, and KV rows are kept for them only.
+ *   resid_out[t] = resid[kept_idx[t]]   ([k, d] bf16; skipped if resid is NULL)
+ *   pos_out[t]   = pos[kept_idx[t]]     (pos NULL = identity: pos_out[t] = kept_idx[t])
+ *   score_out[t] = score[kept_idx[t]]   (skipped if score is NULL)
+ *   extra[e]: row gather as described by tg_gather (host array of n_extra <= 16).
+ * kept_idx values must lie in [0, n); a row whose index does not is left unwritten.
+ * Copies are bit-exact.  k == 0 is a no-op.
+ */
+int tg_compact(const int32_t* kept_idx, int64_t k, int64_t n, const tg_bf16* resid,
+               tg_bf16* resid_out, int32_t d, const int32_t* pos, int32_t* pos_out,
+               const float* score, float* score_out, const tg_gather* extra, int32_t n_extra,
+               void* stream);
+
+/*
+ * tg_rope -- rotary embedding at original positions, in place (auxiliary;
+ * [P5 Fig 1(a)(b)]: kept tokens keep their original position encoding).
+ * x [rows, heads, head_dim] bf16, pos [rows] int32 >= 0.  Half-split pairs
+ * (j, j + head_dim/2), angle pos * theta^(-2j/head_dim), evaluated in fp64 and
+ * rounded to bf16 (nearest-even) once.  head_dim even, <= 256.
+ */
+int tg_rope(tg_bf16* x, const int32_t* pos, int64_t rows, int32_t heads, int32_t head_dim,
+            double theta, void* stream);
+
+/*
+ * tg_gated_attention -- token-gated causal attention over the kept list, one
+ * upper layer [P1 tga][P2 method][P3 tga][P5 Fig 1(c)].  For q head h (kv head
+ * h / (hq/hkv)), query row t and keys j <= t:
+ *   z_tj     = lambda_t * (q_t . k_j / sqrt(head_dim) + gains[h] * key_score[j])
+ *   lambda_t = 1 + temp_coef * ln((t + 1) / (pos[t] + 1))
+ *   out_t    = sum_j softmax_j(z_tj) v_j
+ * q [n_kept, hq, head_dim], k / v [n_kept, hkv, head_dim] bf16 (16-byte aligned);
+ * key_score [n_kept] fp32 (normalised score of each kept token); gains [hq] fp32;
+ * pos [n_kept] int32 original positions (>= 0, increasing).
+ * out [n_kept, hq, head_dim]: bf16 if out_dtype == 0, fp32 if out_dtype == 1.
+ * Supported: head_dim in {64, 128}, hq % hkv == 0.  n_kept == 0 is a no-op.
+ * bf16 matrix-core products with fp32 accumulation; softmax in fp32.
+ */
+int tg_gated_attention(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v,
+                       const float* key_score, const float* gains, float temp_coef,
+                       const int32_t* pos, int64_t n_kept, int32_t hq, int32_t hkv,
+                       int32_t head_dim, void* out, int32_t out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOKENGATE_H */

@@ -1,0 +1,217 @@
+"""Thin Python binding of libtokengate.so: argument marshalling only.
+
+Each function has the name of the C entry point it calls and takes torch
+tensors that already live on the GPU; it checks dtypes and shapes, turns the
+tensors into device pointers and passes torch's current HIP stream.  Every
+step of the path runs in the library's HIP kernels; there is no other code
+path.  A missing or unloadable library raises immediately.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtokengate.so")
+
+TG_OK = 0
+TG_EINVAL = -1
+TG_EUNSUPPORTED = -2
+TG_EALIGN = -3
+TG_EWORKSPACE = -4
+TG_EDEVICE = -5
+TG_STATUS_FORCED_MISMATCH = 1
+TG_STATUS_FORCED_OVER_K = 2
+TG_MAX_GATHER = 16
+
+EXPORTS = ("tg_status_string", "tg_abi_version", "tg_workspace_bytes", "tg_gate_score",
+           "tg_select_topk", "tg_compact", "tg_rope", "tg_gated_attention")
+
+
+class TgGather(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_void_p), ("dst", ctypes.c_void_p), ("row_bytes", ctypes.c_int64),
+                ("src_stride", ctypes.c_int64), ("dst_stride", ctypes.c_int64)]
+
+
+class TokenGateError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status} ({status_string(status)})")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = _LIB_PATH) -> ctypes.CDLL:
+    """Load the library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m learned_token_pruning_mlp_amd.build`")
+    L = ctypes.CDLL(path)
+    P, I64, I32, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+    L.tg_status_string.argtypes = [ctypes.c_int]
+    L.tg_status_string.restype = ctypes.c_char_p
+    L.tg_abi_version.argtypes = []
+    L.tg_abi_version.restype = ctypes.c_int
+    L.tg_workspace_bytes.argtypes = [I64]
+    L.tg_workspace_bytes.restype = ctypes.c_size_t
+    L.tg_gate_score.argtypes = [P, P, P, P, F, I64, I32, I32, F, F, P, P, P, ctypes.c_size_t, P]
+    L.tg_gate_score.restype = ctypes.c_int
+    L.tg_select_topk.argtypes = [P, P, I64, I64, I64, P, P, P, ctypes.c_size_t, P]
+    L.tg_select_topk.restype = ctypes.c_int
+    L.tg_compact.argtypes = [P, I64, I64, P, P, I32, P, P, P, P, P, I32, P]
+    L.tg_compact.restype = ctypes.c_int
+    L.tg_rope.argtypes = [P, P, I64, I32, I32, ctypes.c_double, P]
+    L.tg_rope.restype = ctypes.c_int
+    L.tg_gated_attention.argtypes = [P, P, P, P, P, F, P, I64, I32, I32, I32, P, I32, P]
+    L.tg_gated_attention.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return load().tg_status_string(int(status)).decode()
+
+
+def tg_status_string(status: int) -> str:
+    return status_string(status)
+
+
+def tg_abi_version() -> int:
+    return int(load().tg_abi_version())
+
+
+def tg_workspace_bytes(n: int) -> int:
+    return int(load().tg_workspace_bytes(int(n)))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t: Optional[torch.Tensor], name: str, dtype, shape=None, optional=False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _check(fn: str, status: int):
+    if status != TG_OK:
+        raise TokenGateError(fn, status)
+
+
+def workspace(n: int, device=None) -> torch.Tensor:
+    """A workspace tensor of tg_workspace_bytes(n) bytes."""
+    return torch.empty(max(1, tg_workspace_bytes(n)), dtype=torch.uint8, device=device or "cuda")
+
+
+def tg_gate_score(resid: torch.Tensor, w1: torch.Tensor, b1: Optional[torch.Tensor], w2: torch.Tensor,
+                  b2: float, eps_row: float, eps_seq: float, score_norm: torch.Tensor,
+                  score_raw: Optional[torch.Tensor], ws: torch.Tensor, stream=None) -> None:
+    n, d = resid.shape
+    hd = w1.shape[0]
+    _need(resid, "resid", torch.bfloat16, (n, d))
+    _need(w1, "w1", torch.bfloat16, (hd, d))
+    _need(b1, "b1", torch.bfloat16, (hd,), optional=True)
+    _need(w2, "w2", torch.bfloat16, (hd,))
+    _need(score_norm, "score_norm", torch.float32, (n,))
+    _need(score_raw, "score_raw", torch.float32, (n,), optional=True)
+    _need(ws, "ws", torch.uint8)
+    _check("tg_gate_score", load().tg_gate_score(
+        _ptr(resid), _ptr(w1), _ptr(b1), _ptr(w2), float(b2), n, d, hd, float(eps_row), float(eps_seq),
+        _ptr(score_norm), _ptr(score_raw), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def tg_select_topk(score: torch.Tensor, forced: Optional[torch.Tensor], n_forced: int, k: int,
+                   kept_idx: torch.Tensor, dev_status: Optional[torch.Tensor], ws: torch.Tensor,
+                   stream=None) -> None:
+    n = score.shape[0]
+    _need(score, "score", torch.float32, (n,))
+    _need(forced, "forced", torch.uint8, (n,), optional=True)
+    _need(kept_idx, "kept_idx", torch.int32, (k,))
+    _need(dev_status, "dev_status", torch.int32, (1,), optional=True)
+    _need(ws, "ws", torch.uint8)
+    _check("tg_select_topk", load().tg_select_topk(
+        _ptr(score), _ptr(forced), n, int(n_forced), int(k), _ptr(kept_idx), _ptr(dev_status), _ptr(ws),
+        ws.numel(), _stream(stream)))
+
+
+def tg_compact(kept_idx: torch.Tensor, n: int, resid: Optional[torch.Tensor], resid_out: Optional[torch.Tensor],
+               pos: Optional[torch.Tensor], pos_out: Optional[torch.Tensor], score: Optional[torch.Tensor],
+               score_out: Optional[torch.Tensor],
+               extra: Sequence[tuple] = (), stream=None) -> None:
+    """extra: (src, dst) tensor pairs whose first dim is the token; rows are
+    copied as raw bytes (src row stride = dst row stride = bytes per row)."""
+    k = kept_idx.shape[0]
+    _need(kept_idx, "kept_idx", torch.int32, (k,))
+    d = 0
+    if resid is not None:
+        d = resid.shape[1]
+        _need(resid, "resid", torch.bfloat16, (n, d))
+        _need(resid_out, "resid_out", torch.bfloat16, (k, d))
+    _need(pos, "pos", torch.int32, (n,), optional=True)
+    _need(pos_out, "pos_out", torch.int32, (k,), optional=True)
+    _need(score, "score", torch.float32, (n,), optional=True)
+    _need(score_out, "score_out", torch.float32, (k,), optional=True)
+    if len(extra) > TG_MAX_GATHER:
+        raise ValueError("too many extra streams")
+    arr = (TgGather * max(1, len(extra)))()
+    for e, (src, dst) in enumerate(extra):
+        if not (src.is_cuda and dst.is_cuda and src.is_contiguous() and dst.is_contiguous()):
+            raise ValueError("extra streams must be contiguous GPU tensors")
+        if src.shape[0] != n or dst.shape[0] != k or src.dtype != dst.dtype or src.shape[1:] != dst.shape[1:]:
+            raise ValueError("extra stream shapes do not match")
+        rb = src[0].numel() * src.element_size()
+        arr[e] = TgGather(src.data_ptr(), dst.data_ptr(), rb, rb, rb)
+    _check("tg_compact", load().tg_compact(
+        _ptr(kept_idx), k, int(n), _ptr(resid), _ptr(resid_out), d, _ptr(pos), _ptr(pos_out), _ptr(score),
+        _ptr(score_out), arr if extra else None, len(extra), _stream(stream)))
+
+
+def tg_rope(x: torch.Tensor, pos: torch.Tensor, theta: float, stream=None) -> None:
+    rows, heads, hd = x.shape
+    _need(x, "x", torch.bfloat16)
+    _need(pos, "pos", torch.int32, (rows,))
+    _check("tg_rope", load().tg_rope(_ptr(x), _ptr(pos), rows, heads, hd, float(theta), _stream(stream)))
+
+
+def tg_gated_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_score: torch.Tensor,
+                       gains: torch.Tensor, temp_coef: float, pos: torch.Tensor, out: torch.Tensor,
+                       stream=None) -> None:
+    nk, hq, D = q.shape
+    hkv = k.shape[1]
+    _need(q, "q", torch.bfloat16, (nk, hq, D))
+    _need(k, "k", torch.bfloat16, (nk, hkv, D))
+    _need(v, "v", torch.bfloat16, (nk, hkv, D))
+    _need(key_score, "key_score", torch.float32, (nk,))
+    _need(gains, "gains", torch.float32, (hq,))
+    _need(pos, "pos", torch.int32, (nk,))
+    if out.dtype == torch.bfloat16:
+        od = 0
+    elif out.dtype == torch.float32:
+        od = 1
+    else:
+        raise ValueError("out must be bfloat16 or float32")
+    _need(out, "out", out.dtype, (nk, hq, D))
+    _check("tg_gated_attention", load().tg_gated_attention(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(key_score), _ptr(gains), float(temp_coef), _ptr(pos), nk, hq, hkv, D,
+        _ptr(out), od, _stream(stream)))

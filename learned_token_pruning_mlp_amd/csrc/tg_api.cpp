@@ -1,0 +1,125 @@
+// tg_api.cpp -- the C ABI entry points: argument checks, then the launchers.
+//
+// Every check runs on the host before anything touches the HIP runtime, so
+// an invalid call returns a negative status with nothing enqueued.
+#include <stdint.h>
+
+#include "tg_internal.h"
+#include "tokengate.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+inline bool finite_nonneg(float x) { return x >= 0.0f && x <= 3.4e38f; }
+constexpr int64_t kMaxRows = 0x7fffffffLL;
+
+}  // namespace
+
+extern "C" {
+
+const char* tg_status_string(int status) {
+    switch (status) {
+        case TG_OK: return "ok";
+        case TG_EINVAL: return "invalid argument (size, budget or required pointer)";
+        case TG_EUNSUPPORTED: return "unsupported shape";
+        case TG_EALIGN: return "pointer, row size or stride not 16-byte aligned";
+        case TG_EWORKSPACE: return "workspace missing or too small";
+        case TG_EDEVICE: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int tg_abi_version(void) { return kAbiVersion; }
+
+size_t tg_workspace_bytes(int64_t n) { return tgi::workspace_bytes(n < 0 ? 0 : n); }
+
+int tg_gate_score(const tg_bf16* resid, const tg_bf16* w1, const tg_bf16* b1, const tg_bf16* w2, float b2,
+                  int64_t n, int32_t d, int32_t hd, float eps_row, float eps_seq, float* score_norm,
+                  float* score_raw, void* workspace, size_t workspace_bytes, void* stream) {
+    if (n < 0 || n > kMaxRows) return TG_EINVAL;
+    if (!finite_nonneg(eps_row) || !finite_nonneg(eps_seq)) return TG_EINVAL;
+    if (d <= 0 || d % 64 != 0) return TG_EUNSUPPORTED;
+    if (hd != 64 && hd != 128 && hd != 256) return TG_EUNSUPPORTED;
+    if (n == 0) return TG_OK;
+    if (!resid || !w1 || !w2 || !score_norm) return TG_EINVAL;
+    if (!aligned(resid, 16) || !aligned(w1, 16) || !aligned(score_norm, 4) ||
+        (score_raw && !aligned(score_raw, 4)) || (b1 && !aligned(b1, 2)) || !aligned(w2, 2))
+        return TG_EALIGN;
+    if (!workspace || workspace_bytes < tgi::workspace_bytes(n)) return TG_EWORKSPACE;
+    if (!aligned(workspace, 16)) return TG_EALIGN;
+    return tgi::launch_gate_score(resid, w1, b1, w2, b2, n, d, hd, eps_row, eps_seq, score_norm, score_raw,
+                                  workspace, stream);
+}
+
+int tg_select_topk(const float* score, const uint8_t* forced, int64_t n, int64_t n_forced, int64_t k,
+                   int32_t* kept_idx, int32_t* dev_status, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+    if (n < 1 || n > kMaxRows || k < 1 || k > n || n_forced < 0 || n_forced > k) return TG_EINVAL;
+    if (!forced && n_forced != 0) return TG_EINVAL;
+    if (!score || !kept_idx) return TG_EINVAL;
+    if (!aligned(score, 4) || !aligned(kept_idx, 4) || (dev_status && !aligned(dev_status, 4)))
+        return TG_EALIGN;
+    if (!workspace || workspace_bytes < tgi::workspace_bytes(n)) return TG_EWORKSPACE;
+    if (!aligned(workspace, 16)) return TG_EALIGN;
+    return tgi::launch_select_topk(score, forced, n, n_forced, k, kept_idx, dev_status, workspace, stream);
+}
+
+int tg_compact(const int32_t* kept_idx, int64_t k, int64_t n, const tg_bf16* resid, tg_bf16* resid_out,
+               int32_t d, const int32_t* pos, int32_t* pos_out, const float* score, float* score_out,
+               const tg_gather* extra, int32_t n_extra, void* stream) {
+    if (k < 0 || k > kMaxRows || n < 1 || n > kMaxRows) return TG_EINVAL;
+    if (n_extra < 0 || n_extra > TG_MAX_GATHER || (n_extra > 0 && !extra)) return TG_EINVAL;
+    if (!kept_idx) return TG_EINVAL;
+    if (resid) {
+        if (!resid_out || d <= 0) return TG_EINVAL;
+        if (d % 8 != 0) return TG_EALIGN;
+        if (!aligned(resid, 16) || !aligned(resid_out, 16)) return TG_EALIGN;
+    }
+    if (score_out && !score) return TG_EINVAL;
+    if (!aligned(kept_idx, 4) || (pos && !aligned(pos, 4)) || (pos_out && !aligned(pos_out, 4)) ||
+        (score && !aligned(score, 4)) || (score_out && !aligned(score_out, 4)))
+        return TG_EALIGN;
+    for (int e = 0; e < n_extra; ++e) {
+        const tg_gather& g = extra[e];
+        if (g.row_bytes < 0) return TG_EINVAL;
+        if (g.row_bytes == 0) continue;
+        if (!g.src || !g.dst || g.src_stride < g.row_bytes || g.dst_stride < g.row_bytes) return TG_EINVAL;
+        if (g.row_bytes % 16 || g.src_stride % 16 || g.dst_stride % 16 || !aligned(g.src, 16) ||
+            !aligned(g.dst, 16))
+            return TG_EALIGN;
+    }
+    if (k == 0) return TG_OK;
+    return tgi::launch_compact(kept_idx, k, n, resid, resid_out, d, pos, pos_out, score, score_out, extra,
+                               n_extra, stream);
+}
+
+int tg_rope(tg_bf16* x, const int32_t* pos, int64_t rows, int32_t heads, int32_t head_dim, double theta,
+            void* stream) {
+    if (rows < 0 || rows > kMaxRows || heads < 1 || head_dim < 2 || head_dim > 256 || head_dim % 2 != 0)
+        return TG_EINVAL;
+    if (!(theta > 0.0) || theta > 1e300) return TG_EINVAL;
+    if (rows == 0) return TG_OK;
+    if (!x || !pos) return TG_EINVAL;
+    if (!aligned(x, 2) || !aligned(pos, 4)) return TG_EALIGN;
+    return tgi::launch_rope(x, pos, rows, heads, head_dim, theta, stream);
+}
+
+int tg_gated_attention(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, const float* key_score,
+                       const float* gains, float temp_coef, const int32_t* pos, int64_t n_kept, int32_t hq,
+                       int32_t hkv, int32_t head_dim, void* out, int32_t out_dtype, void* stream) {
+    if (n_kept < 0 || n_kept > kMaxRows || hq < 1 || hkv < 1 || hq % hkv != 0) return TG_EINVAL;
+    if (out_dtype != 0 && out_dtype != 1) return TG_EINVAL;
+    if (!(temp_coef == temp_coef) || temp_coef > 3.4e38f || temp_coef < -3.4e38f) return TG_EINVAL;
+    if (head_dim != 64 && head_dim != 128) return TG_EUNSUPPORTED;
+    if (n_kept == 0) return TG_OK;
+    if (!q || !k || !v || !key_score || !gains || !pos || !out) return TG_EINVAL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(key_score, 4) ||
+        !aligned(gains, 4) || !aligned(pos, 4))
+        return TG_EALIGN;
+    return tgi::launch_gated_attention(q, k, v, key_score, gains, temp_coef, pos, n_kept, hq, hkv, head_dim, out,
+                                       out_dtype, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// tg_internal.h -- host-side interface between the C ABI entry points
+// (tg_api.cpp: argument checks) and the kernel launchers (*.hip).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "tokengate.h"
+
+namespace tgi {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Rows of the residual handled by one scorer workgroup (fixed for every hd).
+constexpr int kGateRowsPerBlock = 64;
+
+// Workspace layout, shared by tg_gate_score and tg_select_topk:
+//   [0, gate_bytes)        per-block sums of squared raw scores (fp32)
+//   [select_off, ...)      select: histograms, counters, per-chunk counts
+inline int64_t gate_blocks(int64_t n) { return (n + kGateRowsPerBlock - 1) / kGateRowsPerBlock; }
+inline size_t gate_bytes(int64_t n) { return align_up(sizeof(float) * (size_t)(gate_blocks(n) > 0 ? gate_blocks(n) : 1)); }
+
+constexpr int kSelectChunk = 4096;  // keys per select workgroup
+inline int64_t select_chunks(int64_t n) { return (n + kSelectChunk - 1) / kSelectChunk; }
+// 4 radix rounds x 256 bins of u32, control words, then 2 x u32 per chunk.
+inline size_t select_bytes(int64_t n) {
+    return align_up(sizeof(uint32_t) * (4 * 256 + 64)) +
+           align_up(sizeof(uint32_t) * 2 * (size_t)(select_chunks(n) > 0 ? select_chunks(n) : 1));
+}
+inline size_t workspace_bytes(int64_t n) { return gate_bytes(n) + select_bytes(n); }
+
+// Launchers: return 0 on success, TG_EDEVICE on a launch error.
+int launch_gate_score(const uint16_t* resid, const uint16_t* w1, const uint16_t* b1,
+                      const uint16_t* w2, float b2, int64_t n, int d, int hd, float eps_row,
+                      float eps_seq, float* score_norm, float* score_raw, void* ws, void* stream);
+
+int launch_select_topk(const float* score, const uint8_t* forced, int64_t n, int64_t n_forced,
+                       int64_t k, int32_t* kept_idx, int32_t* dev_status, void* ws, void* stream);
+
+int launch_compact(const int32_t* kept_idx, int64_t k, int64_t n, const uint16_t* resid,
+                   uint16_t* resid_out, int d, const int32_t* pos, int32_t* pos_out,
+                   const float* score, float* score_out, const tg_gather* extra, int n_extra,
+                   void* stream);
+
+int launch_rope(uint16_t* x, const int32_t* pos, int64_t rows, int heads, int head_dim,
+                double theta, void* stream);
+
+int launch_gated_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           const float* key_score, const float* gains, float temp_coef,
+                           const int32_t* pos, int64_t n_kept, int hq, int hkv, int head_dim,
+                           void* out, int out_dtype, void* stream);
+
+}  // namespace tgi

@@ -1,0 +1,159 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and
+rejects invalid arguments on the host before anything reaches the GPU.
+
+No call here enqueues GPU work: each one either fails a host-side check or is
+a documented no-op (empty input).  Fake pointers are never dereferenced,
+because every check runs before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from learned_token_pruning_mlp_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tokengate.h")
+
+A = 1 << 20  # a 16-byte-aligned fake address (never dereferenced)
+M = A + 2    # a misaligned one
+WS = 1 << 24  # generous workspace size claimed for the fake buffer
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tg_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(binding.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_version_status_and_workspace(lib):
+    assert binding.tg_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5):
+        assert binding.tg_status_string(code) != "unknown status"
+    assert binding.tg_status_string(12345) == "unknown status"
+    sizes = [binding.tg_workspace_bytes(n) for n in (0, 1, 512, 16384, 131072, 1 << 20)]
+    assert all(s > 0 and s % 256 == 0 for s in sizes)
+    assert sizes == sorted(sizes)
+
+
+def _gate(lib, **kw):
+    a = dict(resid=A, w1=A, b1=None, w2=A, b2=0.0, n=512, d=256, hd=64, eps_row=1e-6, eps_seq=1e-6,
+             score_norm=A, score_raw=None, ws=A, ws_bytes=WS, stream=None)
+    a.update(kw)
+    return lib.tg_gate_score(a["resid"], a["w1"], a["b1"], a["w2"], a["b2"], a["n"], a["d"], a["hd"],
+                             a["eps_row"], a["eps_seq"], a["score_norm"], a["score_raw"], a["ws"],
+                             a["ws_bytes"], a["stream"])
+
+
+def test_gate_score_checks(lib):
+    E = binding
+    assert _gate(lib, n=0) == E.TG_OK  # empty prompt: no-op
+    assert _gate(lib, n=-1) == E.TG_EINVAL
+    assert _gate(lib, d=200) == E.TG_EUNSUPPORTED
+    assert _gate(lib, hd=96) == E.TG_EUNSUPPORTED
+    assert _gate(lib, resid=None) == E.TG_EINVAL
+    assert _gate(lib, score_norm=None) == E.TG_EINVAL
+    assert _gate(lib, resid=M) == E.TG_EALIGN
+    assert _gate(lib, w1=M) == E.TG_EALIGN
+    assert _gate(lib, ws=None) == E.TG_EWORKSPACE
+    assert _gate(lib, ws_bytes=binding.tg_workspace_bytes(512) - 1) == E.TG_EWORKSPACE
+    assert _gate(lib, eps_row=-1.0) == E.TG_EINVAL
+    assert _gate(lib, eps_seq=float("nan")) == E.TG_EINVAL
+
+
+def _sel(lib, **kw):
+    a = dict(score=A, forced=A, n=1000, nf=10, k=100, kept=A, st=None, ws=A, ws_bytes=WS, stream=None)
+    a.update(kw)
+    return lib.tg_select_topk(a["score"], a["forced"], a["n"], a["nf"], a["k"], a["kept"], a["st"], a["ws"],
+                              a["ws_bytes"], a["stream"])
+
+
+def test_select_checks(lib):
+    E = binding
+    assert _sel(lib, k=0) == E.TG_EINVAL
+    assert _sel(lib, k=1001) == E.TG_EINVAL
+    assert _sel(lib, n=0, k=0) == E.TG_EINVAL
+    assert _sel(lib, nf=101) == E.TG_EINVAL  # more forced than the budget
+    assert _sel(lib, nf=-1) == E.TG_EINVAL
+    assert _sel(lib, forced=None) == E.TG_EINVAL  # forced count without a mask
+    assert _sel(lib, score=None) == E.TG_EINVAL
+    assert _sel(lib, kept=None) == E.TG_EINVAL
+    assert _sel(lib, score=A + 1) == E.TG_EALIGN
+    assert _sel(lib, ws=None) == E.TG_EWORKSPACE
+    assert _sel(lib, ws_bytes=16) == E.TG_EWORKSPACE
+
+
+def _cmp(lib, **kw):
+    a = dict(idx=A, k=64, n=512, resid=A, resid_out=A, d=256, pos=None, pos_out=A, score=A, score_out=A,
+             extra=None, n_extra=0, stream=None)
+    a.update(kw)
+    return lib.tg_compact(a["idx"], a["k"], a["n"], a["resid"], a["resid_out"], a["d"], a["pos"], a["pos_out"],
+                          a["score"], a["score_out"], a["extra"], a["n_extra"], a["stream"])
+
+
+def test_compact_checks(lib):
+    E = binding
+    assert _cmp(lib, k=0) == E.TG_OK  # nothing kept: no-op
+    assert _cmp(lib, k=-1) == E.TG_EINVAL
+    assert _cmp(lib, n=0) == E.TG_EINVAL
+    assert _cmp(lib, idx=None) == E.TG_EINVAL
+    assert _cmp(lib, resid_out=None) == E.TG_EINVAL
+    assert _cmp(lib, d=100) == E.TG_EALIGN  # 200-byte rows
+    assert _cmp(lib, resid=M) == E.TG_EALIGN
+    assert _cmp(lib, score=None) == E.TG_EINVAL  # score_out without score
+    assert _cmp(lib, n_extra=17) == E.TG_EINVAL
+    assert _cmp(lib, n_extra=1, extra=None) == E.TG_EINVAL
+    bad = (binding.TgGather * 1)(binding.TgGather(A, A, 24, 32, 32))
+    assert _cmp(lib, n_extra=1, extra=bad) == E.TG_EALIGN
+    bad = (binding.TgGather * 1)(binding.TgGather(A, A, 64, 32, 64))
+    assert _cmp(lib, n_extra=1, extra=bad) == E.TG_EINVAL  # stride shorter than a row
+    bad = (binding.TgGather * 1)(binding.TgGather(None, A, 64, 64, 64))
+    assert _cmp(lib, n_extra=1, extra=bad) == E.TG_EINVAL
+    bad = (binding.TgGather * 1)(binding.TgGather(A + 8, A, 64, 64, 64))
+    assert _cmp(lib, n_extra=1, extra=bad) == E.TG_EALIGN
+
+
+def test_rope_checks(lib):
+    E = binding
+    assert lib.tg_rope(A, A, 0, 8, 128, 1e6, None) == E.TG_OK
+    assert lib.tg_rope(A, A, 10, 8, 127, 1e6, None) == E.TG_EINVAL
+    assert lib.tg_rope(A, A, 10, 8, 512, 1e6, None) == E.TG_EINVAL
+    assert lib.tg_rope(A, A, 10, 0, 128, 1e6, None) == E.TG_EINVAL
+    assert lib.tg_rope(A, A, 10, 8, 128, 0.0, None) == E.TG_EINVAL
+    assert lib.tg_rope(None, A, 10, 8, 128, 1e6, None) == E.TG_EINVAL
+    assert lib.tg_rope(A + 1, A, 10, 8, 128, 1e6, None) == E.TG_EALIGN
+
+
+def _att(lib, **kw):
+    a = dict(q=A, k=A, v=A, ks=A, g=A, c=0.1, pos=A, nk=128, hq=4, hkv=2, D=64, out=A, od=0, stream=None)
+    a.update(kw)
+    return lib.tg_gated_attention(a["q"], a["k"], a["v"], a["ks"], a["g"], a["c"], a["pos"], a["nk"], a["hq"],
+                                  a["hkv"], a["D"], a["out"], a["od"], a["stream"])
+
+
+def test_attention_checks(lib):
+    E = binding
+    assert _att(lib, nk=0) == E.TG_OK  # nothing kept: no-op
+    assert _att(lib, nk=-5) == E.TG_EINVAL
+    assert _att(lib, hq=6, hkv=4) == E.TG_EINVAL
+    assert _att(lib, hkv=0) == E.TG_EINVAL
+    assert _att(lib, D=96) == E.TG_EUNSUPPORTED
+    assert _att(lib, od=2) == E.TG_EINVAL
+    assert _att(lib, c=float("nan")) == E.TG_EINVAL
+    assert _att(lib, q=None) == E.TG_EINVAL
+    assert _att(lib, pos=None) == E.TG_EINVAL
+    assert _att(lib, q=M) == E.TG_EALIGN
+    assert _att(lib, out=A + 8) == E.TG_EALIGN

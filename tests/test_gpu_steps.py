@@ -1,0 +1,233 @@
+"""GPU parity of each step of the path against the fp64 oracle, through the C ABI.
+
+Sizes are ones the oracle finishes in seconds, chosen to span several tiles
+and a ragged tail; the full-size workloads are in test_gpu_workloads.py.
+Integer outputs (kept indices, gathered rows, positions) must match
+bit-exactly; floating-point outputs within the stated tolerances.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as gu
+from learned_token_pruning_mlp_amd import binding as tg
+from learned_token_pruning_mlp_amd import synth
+from oracle import gap, oracle
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------- gate score
+
+def _gate_case(n, d, hd, seed, with_b1=False, b2=0.0, w1_zero=False):
+    shp = synth.GateShape(n=n, d=d, hd=hd, n_forced=0, k=1, hq=1, hkv=1, head_dim=64)
+    inp = synth.gate_inputs(shp, seed, with_b1=with_b1, w1_zero=w1_zero)
+    inp.b2 = b2
+    return inp
+
+
+def _run_gate(inp, eps_row=1e-6, eps_seq=1e-6, raw=True):
+    n, d = inp.resid.shape
+    s_norm = torch.empty(n, dtype=torch.float32, device=gu.dev())
+    s_raw = torch.empty(n, dtype=torch.float32, device=gu.dev()) if raw else None
+    ws = tg.workspace(n)
+    tg.tg_gate_score(gu.bf16(inp.resid), gu.bf16(inp.w1), None if inp.b1 is None else gu.bf16(inp.b1),
+                     gu.bf16(inp.w2), inp.b2, eps_row, eps_seq, s_norm, s_raw, ws)
+    return gu.host(s_norm), (gu.host(s_raw) if raw else None)
+
+
+@pytest.mark.parametrize("n,d,hd,b1,b2", [(512, 256, 64, False, 0.0), (1000, 256, 64, True, 0.3),
+                                          (777, 512, 128, True, -0.2), (333, 2048, 256, False, 0.0),
+                                          (1, 128, 64, True, 0.0)])
+def test_gate_score(n, d, hd, b1, b2):
+    gu.say(f"gate_score n={n} d={d} hd={hd}")
+    inp = _gate_case(n, d, hd, seed=11, with_b1=b1, b2=b2)
+    ref_norm, ref_raw = oracle.gate_score(inp.resid, inp.w1, inp.b1, inp.w2, inp.b2)
+    got_norm, got_raw = _run_gate(inp)
+    assert np.max(np.abs(got_raw - ref_raw)) <= gu.SCORE_ABS
+    assert np.max(np.abs(got_norm - ref_norm)) <= gu.SCORE_ABS
+    # without a raw buffer the normalised scores are the same
+    again, _ = _run_gate(inp, raw=False)
+    assert np.array_equal(again, got_norm)
+
+
+def test_gate_score_zero_weights_all_equal():
+    gu.say("gate_score W1=0")
+    inp = _gate_case(1000, 256, 64, seed=12, w1_zero=True)
+    got, raw = _run_gate(inp)
+    assert np.all(raw == 0.0) and np.all(got == 0.0)
+
+
+# ------------------------------------------------------------- select
+
+def _run_select(score_f32, forced, k, n_forced=None):
+    n = score_f32.size
+    kept = torch.empty(k, dtype=torch.int32, device=gu.dev())
+    st = torch.full((1,), -7, dtype=torch.int32, device=gu.dev())
+    nf = int(forced.sum()) if (forced is not None and n_forced is None) else (n_forced or 0)
+    tg.tg_select_topk(gu.f32(score_f32), None if forced is None else gu.u8(forced), nf, k, kept, st,
+                      tg.workspace(n))
+    return gu.host(kept), int(gu.host(st)[0])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_select_small_with_ties(seed):
+    g = np.random.default_rng(100 + seed)
+    n = int(g.integers(1, 3000))
+    score = (g.integers(-4, 5, size=n) * 0.25).astype(np.float32)
+    forced = (g.random(n) < 0.1).astype(np.uint8)
+    f = int(forced.sum())
+    k = int(g.integers(max(f, 1), n + 1))
+    gu.say(f"select ties n={n} k={k} F={f}")
+    got, st = _run_select(score, forced, k)
+    assert st == 0
+    assert np.array_equal(got, oracle.select_topk(score, forced, k))
+
+
+@pytest.mark.parametrize("n,k,f", [(16384, 2048, 64), (32768, 4096, 64), (40000, 9000, 100),
+                                   (131072, 8192, 128)])
+def test_select_gaussian(n, k, f):
+    gu.say(f"select n={n} k={k}")
+    g = np.random.default_rng(n)
+    score = g.standard_normal(n).astype(np.float32)
+    forced = np.zeros(n, np.uint8)
+    forced[g.choice(n, size=f, replace=False)] = 1
+    got, st = _run_select(score, forced, k)
+    assert st == 0
+    assert np.array_equal(got, oracle.select_topk(score, forced, k))
+
+
+def test_select_all_equal_closed_form():
+    n, k, f = 16384, 1024, 64
+    gu.say("select all-equal")
+    forced = np.zeros(n, np.uint8)
+    forced[-f:] = 1
+    got, st = _run_select(np.zeros(n, np.float32), forced, k)
+    assert st == 0
+    assert np.array_equal(got, np.concatenate([np.arange(k - f), np.arange(n - f, n)]))
+
+
+def test_select_extremes_and_specials():
+    gu.say("select extremes")
+    g = np.random.default_rng(5)
+    n = 5000
+    score = g.standard_normal(n).astype(np.float32)
+    forced = np.zeros(n, np.uint8)
+    forced[[0, 17, 4999]] = 1
+    assert np.array_equal(_run_select(score, forced, n)[0], np.arange(n))
+    assert np.array_equal(_run_select(score, forced, 3)[0], np.array([0, 17, 4999]))
+    assert np.array_equal(_run_select(score, None, 1)[0], np.array([np.argmax(score)]))
+    sp = np.array([np.nan, -0.0, 0.0, -np.inf, 1.0, np.nan, np.inf, -1.0], np.float32)
+    for k in range(1, sp.size + 1):
+        assert np.array_equal(_run_select(sp, None, k)[0], oracle.select_topk(sp, None, k)), k
+
+
+def test_select_forced_count_status():
+    gu.say("select status")
+    n = 2000
+    score = np.random.default_rng(6).standard_normal(n).astype(np.float32)
+    forced = np.zeros(n, np.uint8)
+    forced[-50:] = 1
+    got, st = _run_select(score, forced, 100, n_forced=40)  # caller's F is wrong
+    assert st == tg.TG_STATUS_FORCED_MISMATCH
+    assert np.array_equal(got, oracle.select_topk(score, forced, 100))
+    got, st = _run_select(score, forced, 45, n_forced=45)  # 50 forced > k = 45
+    assert st == tg.TG_STATUS_FORCED_MISMATCH | tg.TG_STATUS_FORCED_OVER_K
+    assert np.array_equal(got, np.arange(n - 50, n - 5))
+
+
+# ------------------------------------------------------------- compaction
+
+@pytest.mark.parametrize("n,k,d", [(512, 128, 256), (16384, 2048, 2048), (3001, 1999, 64)])
+def test_compact(n, k, d):
+    gu.say(f"compact n={n} k={k} d={d}")
+    g = np.random.default_rng(k)
+    resid = g.integers(0, 65536, size=(n, d), dtype=np.uint16)
+    idx = np.sort(g.choice(n, size=k, replace=False)).astype(np.int32)
+    pos = (np.arange(n) * 3 + 7).astype(np.int32)
+    score = g.standard_normal(n).astype(np.float32)
+    kv_k = g.integers(0, 65536, size=(n, 8, 128), dtype=np.uint16)
+    kv_v = g.integers(0, 65536, size=(n, 2, 64), dtype=np.uint16)
+    d_resid, d_kk, d_vv = gu.bf16(resid), gu.bf16(kv_k), gu.bf16(kv_v)
+    out = torch.empty((k, d), dtype=torch.bfloat16, device=gu.dev())
+    ok_, ov_ = (torch.empty((k, 8, 128), dtype=torch.bfloat16, device=gu.dev()),
+                torch.empty((k, 2, 64), dtype=torch.bfloat16, device=gu.dev()))
+    pos_out = torch.empty(k, dtype=torch.int32, device=gu.dev())
+    s_out = torch.empty(k, dtype=torch.float32, device=gu.dev())
+    tg.tg_compact(gu.i32(idx), n, d_resid, out, gu.i32(pos), pos_out, gu.f32(score), s_out,
+                  extra=[(d_kk, ok_), (d_vv, ov_)])
+    torch.cuda.synchronize()
+    assert np.array_equal(gu.bits(out), oracle.gather_rows(resid, idx))
+    assert np.array_equal(gu.bits(ok_), oracle.gather_rows(kv_k, idx))
+    assert np.array_equal(gu.bits(ov_), oracle.gather_rows(kv_v, idx))
+    assert np.array_equal(gu.host(pos_out), oracle.gather_rows(pos, idx))
+    assert np.array_equal(gu.host(s_out).view(np.uint32), oracle.gather_rows(score, idx).view(np.uint32))
+    # default positions are the kept indices themselves
+    tg.tg_compact(gu.i32(idx), n, None, None, None, pos_out, None, None)
+    assert np.array_equal(gu.host(pos_out), idx)
+
+
+# ------------------------------------------------------------- RoPE
+
+@pytest.mark.parametrize("rows,heads,D", [(300, 4, 64), (2048, 24, 128), (5, 1, 2)])
+def test_rope(rows, heads, D):
+    gu.say(f"rope rows={rows} heads={heads} D={D}")
+    g = np.random.default_rng(rows)
+    x = synth.normal_bf16(rows, 1, (rows, heads, D))
+    pos = np.sort(g.choice(131072, size=rows, replace=False)).astype(np.int32)
+    t = gu.bf16(x)
+    tg.tg_rope(t, gu.i32(pos), 1.0e6)
+    got = gu.bits(t)
+    want = oracle.rope(x, pos, 1.0e6)
+    # identical bf16 except where a last-bit difference of the fp64 angle
+    # crosses a rounding boundary: at most one unit in the last place
+    diff = np.abs(got.astype(np.int32) - want.astype(np.int32))
+    assert diff.max() <= 1
+    assert np.mean(diff != 0) < 1e-3
+
+
+# ------------------------------------------------------------- attention
+
+def _run_attn(a, out_dtype=torch.float32):
+    nk, hq, D = a.q.shape
+    out = torch.empty((nk, hq, D), dtype=out_dtype, device=gu.dev())
+    tg.tg_gated_attention(gu.bf16(a.q), gu.bf16(a.k), gu.bf16(a.v), gu.f32(a.key_score), gu.f32(a.gains),
+                          a.temp_coef, gu.i32(a.pos), out)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("nk,hq,hkv,D", [(128, 4, 2, 64), (200, 4, 2, 64), (333, 8, 1, 128),
+                                         (257, 6, 6, 128), (96, 16, 2, 64), (1, 4, 2, 128),
+                                         (1000, 16, 8, 128)])
+def test_attention(nk, hq, hkv, D):
+    gu.say(f"attention nk={nk} hq={hq} hkv={hkv} D={D}")
+    a = synth.attn_inputs(nk, hq, hkv, D, seed=nk + hq)
+    ref = oracle.gated_attention(a.q, a.k, a.v, a.key_score, a.gains, a.temp_coef, a.pos)
+    out32 = _run_attn(a, torch.float32)
+    gu.check_attention(gu.host(out32), ref, "fp32 out")
+    out16 = _run_attn(a, torch.bfloat16)
+    # the bf16 output is the nearest-even rounding of the fp32 result
+    assert np.array_equal(gu.bits(out16), oracle.to_bf16(gu.host(out32).astype(np.float64)))
+
+
+def test_attention_large_temperature_and_bias():
+    # heavy-tailed scores (biases up to ~40) and a temperature coefficient
+    # large enough to make lambda negative for early rows
+    gu.say("attention heavy-tailed scores, negative lambda")
+    nk = 700
+    ks = synth.student_t_scores(nk, 3)
+    pos = np.sort(np.random.default_rng(77).choice(50 * nk, size=nk, replace=False)).astype(np.int32)
+    a = synth.attn_inputs(nk, 4, 2, 128, seed=77, key_score=ks, temp_coef=0.6, pos=pos)
+    lam = 1 + 0.6 * np.log((np.arange(nk) + 1) / (a.pos + 1.0))
+    assert lam.min() < 0
+    ref = oracle.gated_attention(a.q, a.k, a.v, a.key_score, a.gains, a.temp_coef, a.pos)
+    gu.check_attention(gu.host(_run_attn(a)), ref, "heavy tails")
+
+
+def test_attention_deterministic():
+    gu.say("attention determinism")
+    a = synth.attn_inputs(1500, 16, 8, 128, seed=3)
+    o1 = gu.host(_run_attn(a))
+    o2 = gu.host(_run_attn(a))
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
