@@ -101,7 +101,8 @@ int tg_gate_score(const tg_bf16* resid, const tg_bf16* w1, const tg_bf16* b1, co
  * Keeps every token with forced[i] != 0 and, among the others, the
  * k - F with the largest score (ties to the lower index; -0.0 equals +0.0;
  * NaN ranks below -inf).  k counts all kept tokens, forced ones included.
- * score    [n] fp32.  forced [n] uint8 or NULL (no forced tokens).
+ * score    [n] fp32, 16-byte aligned.  forced [n] uint8 (4-byte aligned) or NULL
+ *          (no forced tokens).
  * n_forced host-known number of forced tokens F (checked: 0 <= F <= k <= n, k >= 1).
  * kept_idx [k] int32 out: kept indices in ascending order.
  * dev_status optional device int32: receives TG_STATUS_* bits (0 = consistent).

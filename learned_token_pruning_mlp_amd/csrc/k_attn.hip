@@ -17,19 +17,29 @@
 //    and 16 keys per 32x32 block: lambda_t, the running max and the running
 //    sum are per-lane scalars, and the max needs one exchange between the
 //    two half-waves.
-//  * The accumulator of S^T starts at sqrt(D) * g_h * s_j (from LDS), so the
-//    matrix core adds the key bias for free; the logit in the exp2 domain is
-//    then a single multiply by lambda_t * log2(e) / sqrt(D) per element.
-//  * The S^T accumulator layout is exactly the B-operand layout of the
-//    O^T = V^T . P^T product (keys along k), so P goes from registers to the
-//    matrix core with only a conversion to bf16; V is stored transposed in
-//    LDS to serve the A operand.
-//  * A workgroup is 4 waves of 32 query rows each; when the q heads of a GQA
-//    group allow it, the waves of one workgroup cover 2 or 4 heads of the
-//    same kv head so every K/V tile in LDS is used by all of them.
+//  * The accumulator of S^T starts at sqrt(D) * g_h * s_j, so the matrix core
+//    adds the key bias; each probability is then one FMA and one exp2:
+//    p = 2^(a_t * S - m) with a_t = lambda_t * log2(e) / sqrt(D).
+//  * The S^T accumulator layout is the B-operand layout of O^T = V^T . P^T
+//    (keys along k), so P goes from registers to the matrix core with one
+//    hardware bf16 conversion per pair.
+//  * Work split: a workgroup owns one GQA kv head, HPW of its q heads and a
+//    pair of 32-row query blocks (b, last - b), so every workgroup carries the
+//    same causal work.  The keys of a query block are streamed as super-tiles
+//    of NS x 32 keys; wave (head, split) takes the split-th 32 keys of each
+//    super-tile for its head, keeping its own running max and sum, and the
+//    NS partial results of a head are merged through LDS at the end of the
+//    block.  HPW heads share every K/V super-tile in LDS.  With 2 heads x 4
+//    splits a 2048-key prompt still gives two waves per SIMD.
+//  * K and V super-tiles go from memory straight into LDS with 16-byte
+//    direct loads, double-buffered (the next super-tile is in flight while
+//    this one is multiplied).  Rows are stored with their 16-byte pieces
+//    XOR-permuted by rotl(row), which keeps the K-operand reads and the
+//    transposing V reads (ds_read_b64_tr_b16, which hands each lane four keys
+//    of one head_dim column) free of bank conflicts.
 //  * Work items are laid out so all workgroups of one kv head run on the same
 //    XCD (workgroups go round-robin over the 8 XCDs), keeping that head's K/V
-//    in one L2; within an XCD the longest (latest) query tiles start first.
+//    in one L2.
 #include <hip/hip_runtime.h>
 
 #include "tg_device.h"
@@ -41,249 +51,390 @@ using tgd::f32x16;
 using tgd::u32x2;
 using tgd::u32x4;
 
-constexpr int kThreads = 256;  // 4 waves
-constexpr int kBK = 64;        // keys per LDS tile
+#define TG_LDS __attribute__((address_space(3)))
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+
 constexpr int kXcds = 8;
 constexpr float kLog2e = 1.44269504088896340736f;
 
-template <int D, int HPW>
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+#define TG_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+
+template <int D, int HPW, int RB, int NS, int KB>
 struct AttnCfg {
-    static constexpr int RB = 4 / HPW;        // 32-row blocks per workgroup
-    static constexpr int QROWS = 32 * RB;     // query rows per workgroup
-    static constexpr int LDK = D + 8;         // K tile row (bf16), padded
-    static constexpr int LDV = kBK + 8;       // V^T tile row (bf16), padded
-    static constexpr int KP = kBK * D / 8 / kThreads;        // K 16-byte loads per thread
-    static constexpr int VP = kBK * D / 8 / 2 / kThreads;    // V key-pair items per thread
-    static constexpr int DB = D / 32;         // 32-row blocks of head_dim in O^T
-    static constexpr int QS = D / 16;         // k-steps of the QK^T product
-    static_assert(KP >= 1 && VP >= 1, "tile shape");
+    static constexpr int WAVES = HPW * RB * NS;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int QROWS = 32 * RB;             // query rows per block
+    static constexpr int WKEYS = 32 * KB;             // keys per wave per super-tile
+    static constexpr int SKEYS = WKEYS * NS;          // keys per super-tile
+    static constexpr int PIECES = D / 8;              // 16-byte pieces per K/V row
+    static constexpr int ROW_BYTES = D * 2;
+    static constexpr int TILE_BYTES = SKEYS * ROW_BYTES;  // K (or V) bytes per super-tile
+    static constexpr int BLOCKS = TILE_BYTES / 1024;      // 1 KB direct-load blocks
+    static constexpr int LOADS = BLOCKS / WAVES;          // per wave, for K and again for V
+    static constexpr int DB = D / 32;                 // 32-row blocks of head_dim in O^T
+    static constexpr int QS = D / 16;                 // k-steps of the QK^T product
+    static_assert(BLOCKS % WAVES == 0 && LOADS >= 1, "tile shape");
+    static_assert(SKEYS <= 64 * WAVES, "one score per lane");
+    // merge scratch: one 4 KB slot (16 floats per lane) for every non-leading
+    // split wave, taken from the K buffer of the finished stage, then its V buffer
+    static constexpr int SLOTS = (NS - 1) * HPW * RB;
+    static constexpr int SLOTS_K = TILE_BYTES / 4096;
+    static_assert(SLOTS <= 2 * SLOTS_K, "merge scratch");
 };
 
-template <int D, int HPW, bool OUT_F32>
-__global__ __launch_bounds__(kThreads) void gated_attn(const uint16_t* __restrict__ q,
-                                                       const uint16_t* __restrict__ kk,
-                                                       const uint16_t* __restrict__ v,
-                                                       const float* __restrict__ key_score,
-                                                       const float* __restrict__ gains, float temp_coef,
-                                                       const int32_t* __restrict__ pos, int nk, int hq,
-                                                       int hkv, int n_qtiles, int per_xcd, int n_items,
-                                                       void* __restrict__ out) {
-    using C = AttnCfg<D, HPW>;
-    __shared__ __attribute__((aligned(16))) uint16_t sK[kBK * C::LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t sVt[D * C::LDV];
-    __shared__ __attribute__((aligned(16))) float sBias[HPW][kBK];
+// Permutation of the 16-byte pieces inside a K/V row: rotate the row index
+// left by one over log2(pieces) bits.
+template <int PIECES>
+__device__ __forceinline__ int swz(int r) {
+    if (PIECES == 16) return ((r << 1) | (r >> 3)) & 15;
+    return ((r << 1) | (r >> 2)) & 7;
+}
 
-    // ---- work item: (kv head, head group, query tile), XCD-aware
+template <int D, int HPW, int RB, int NS, int KB, bool OUT_F32>
+__global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16_t* __restrict__ q,
+                                                              const uint16_t* __restrict__ kk,
+                                                              const uint16_t* __restrict__ v,
+                                                              const float* __restrict__ key_score,
+                                                              const float* __restrict__ gains,
+                                                              float temp_coef, const int32_t* __restrict__ pos,
+                                                              int nk, int hq, int hkv, int npairs, int per_xcd,
+                                                              int n_items, void* __restrict__ out) {
+    using C = AttnCfg<D, HPW, RB, NS, KB>;
+    // one set of LDS objects per pipeline stage, so the compiler can see that
+    // reads of one stage never alias the loads in flight into the other
+    __shared__ __attribute__((aligned(1024))) uint8_t sK0[C::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t sV0[C::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t sK1[C::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t sV1[C::TILE_BYTES];
+    __shared__ __attribute__((aligned(256))) float sS0[C::SKEYS];
+    __shared__ __attribute__((aligned(256))) float sS1[C::SKEYS];
+    __shared__ float mbuf[HPW * RB][NS][32];
+    __shared__ float lbuf[HPW * RB][NS][32];
+
+    // ---- work item: (kv head, head group, query-block pair), XCD-aware
     const int lin = blockIdx.x;
     const int item = (lin % kXcds) * per_xcd + lin / kXcds;
     if (item >= n_items) return;
     const int G = hq / hkv;
     const int n_hg = G / HPW;
-    const int per_head = n_hg * n_qtiles;
+    const int per_head = n_hg * npairs;
     const int kvh = item / per_head;
     const int rem = item % per_head;
-    const int hg = rem / n_qtiles;
-    const int qt = n_qtiles - 1 - rem % n_qtiles;  // latest (longest) tiles first
+    const int hg = rem / npairs;
+    const int pr = rem % npairs;
+    const int nqb = (nk + C::QROWS - 1) / C::QROWS;
+    const int qbA = pr, qbB = nqb - 1 - pr;
+    const auto nst = [&](int qb) { return (min(nk, C::QROWS * qb + C::QROWS) - 1) / C::SKEYS + 1; };
+    const int nA = nst(qbA);
+    const int ntot = nA + (qbB != qbA ? nst(qbB) : 0);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, g = lane >> 5;
-    const int hl = wave % HPW, rb = wave / HPW;
+    const int hl = wave % HPW, rb = (wave / HPW) % RB, sp = wave / (HPW * RB);
+    const int hr = hl + HPW * rb;  // this wave's (head, row block) slot among the merge partners
     const int h = kvh * G + hg * HPW + hl;
-    const int q0 = qt * C::QROWS + rb * 32;  // this wave's first query row
-    const int t = q0 + l32;                   // this lane's query row
-    const int wg_last = min(nk, qt * C::QROWS + C::QROWS) - 1;
-    const int wave_last = min(nk - 1, q0 + 31);
+    const float sg = sqrtf((float)D) * gains[h];
+    const int quad = lane >> 4, jj = lane & 15;
+    const int tr_row = jj >> 2, tr_col = 4 * (jj & 3);
 
-    // ---- this lane's query row (B operand of S^T), temperature and scale
+    // ---- direct loads of one super-tile (keys j0 .. j0+SKEYS-1).  Rows past
+    // the last key repeat the last key (they are always causally masked).
+    auto issue = [&](int it, uint8_t* __restrict__ sK, uint8_t* __restrict__ sV, float* __restrict__ sS) {
+        const int st = it < nA ? it : it - nA;
+        const int j0 = st * C::SKEYS;
+        constexpr int rows_per_inst = 64 / C::PIECES;
+#pragma unroll
+        for (int r = 0; r < C::LOADS; ++r) {
+            const int blk = r * C::WAVES + wave;
+            const int row = blk * rows_per_inst + lane / C::PIECES;
+            const int piece = (lane % C::PIECES) ^ swz<C::PIECES>(row);
+            const int j = min(j0 + row, nk - 1);
+            const int64_t goff = ((int64_t)j * hkv + kvh) * D + piece * 8;
+            __builtin_amdgcn_global_load_lds(kk + goff, (TG_LDS void*)((TG_LDS uint8_t*)sK + blk * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(v + goff, (TG_LDS void*)((TG_LDS uint8_t*)sV + blk * 1024), 16, 0, 0);
+        }
+        if (wave * 64 < C::SKEYS) {  // scores: one per lane, first SKEYS/64 waves
+            const int j = min(j0 + wave * 64 + lane, nk - 1);
+            __builtin_amdgcn_global_load_lds(key_score + j, (TG_LDS void*)((TG_LDS uint8_t*)sS + wave * 256), 4, 0,
+                                             0);
+        }
+    };
+
+    // ---- per query-block state of this wave (head h, rows q0 .. q0+31)
     u32x4 qreg[C::QS];
-    {
+    f32x16 o[C::DB];
+    float m_run = -INFINITY, l_run = 0.0f, a_t = 0.0f;
+    bool all_pos = true;
+    int q0 = 0, t = 0, wave_last = 0;
+
+    auto begin_block = [&](int qb) {
+        q0 = C::QROWS * qb + 32 * rb;
+        t = q0 + l32;
+        wave_last = min(nk - 1, q0 + 31);
         const bool ok = t < nk;
         const uint16_t* qp = q + ((int64_t)t * hq + h) * D;
 #pragma unroll
         for (int s = 0; s < C::QS; ++s)
             qreg[s] = ok ? *reinterpret_cast<const u32x4*>(qp + s * 16 + g * 8) : u32x4{0, 0, 0, 0};
-    }
-    float lam = 1.0f;
-    if (t < nk) lam = 1.0f + temp_coef * logf((float)(t + 1) / ((float)pos[t] + 1.0f));
-    const float a_t = lam * kLog2e * (1.0f / sqrtf((float)D));
-    const float sqrt_d = sqrtf((float)D);
-
-    f32x16 o[C::DB];
+        float lam = 1.0f;
+        if (ok) lam = 1.0f + temp_coef * logf((float)(t + 1) / ((float)pos[t] + 1.0f));
+        a_t = lam * kLog2e * (1.0f / sqrtf((float)D));
+        all_pos = __builtin_amdgcn_ballot_w64(!(a_t > 0.0f)) == 0;  // wave-uniform
+        m_run = -INFINITY;
+        l_run = 0.0f;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) o[db] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.0f;
-
-    // ---- K/V tile staging (registers -> LDS)
-    u32x4 kreg[C::KP];
-    u32x4 vreg[C::VP][2];
-    auto load_tile = [&](int j0) {
-#pragma unroll
-        for (int r = 0; r < C::KP; ++r) {
-            const int p = tid + kThreads * r, row = p / (D / 8), col = (p % (D / 8)) * 8;
-            const int j = j0 + row;
-            kreg[r] = j < nk ? *reinterpret_cast<const u32x4*>(kk + ((int64_t)j * hkv + kvh) * D + col)
-                             : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int r = 0; r < C::VP; ++r) {
-            const int p = tid + kThreads * r, kp = p % (kBK / 2), dc = p / (kBK / 2);
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int j = j0 + 2 * kp + e;
-                vreg[r][e] = j < nk ? *reinterpret_cast<const u32x4*>(v + ((int64_t)j * hkv + kvh) * D + dc * 8)
-                                    : u32x4{0, 0, 0, 0};
-            }
-        }
-    };
-    auto store_tile = [&](int j0) {
-#pragma unroll
-        for (int r = 0; r < C::KP; ++r) {
-            const int p = tid + kThreads * r, row = p / (D / 8), col = (p % (D / 8)) * 8;
-            *reinterpret_cast<u32x4*>(&sK[row * C::LDK + col]) = kreg[r];
-        }
-#pragma unroll
-        for (int r = 0; r < C::VP; ++r) {
-            const int p = tid + kThreads * r, kp = p % (kBK / 2), dc = p / (kBK / 2);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t a = vreg[r][0][w], b = vreg[r][1][w];
-                // d = dc*8 + 2w (low halves) and dc*8 + 2w + 1 (high halves); keys 2kp, 2kp+1
-                *reinterpret_cast<uint32_t*>(&sVt[(dc * 8 + 2 * w) * C::LDV + 2 * kp]) =
-                    (a & 0xffffu) | (b << 16);
-                *reinterpret_cast<uint32_t*>(&sVt[(dc * 8 + 2 * w + 1) * C::LDV + 2 * kp]) =
-                    (a >> 16) | (b & 0xffff0000u);
-            }
-        }
-        if (tid < HPW * kBK) {
-            const int hh = tid / kBK, j = tid % kBK;
-            const int jj = j0 + j;
-            const float gh = gains[kvh * G + hg * HPW + hh];
-            sBias[hh][j] = jj < nk ? sqrt_d * gh * key_score[jj] : 0.0f;
-        }
+        for (int db = 0; db < C::DB; ++db) o[db] = f32x16{};
     };
 
-    load_tile(0);
-    for (int j0 = 0; j0 <= wg_last; j0 += kBK) {
-        __syncthreads();  // previous tile fully consumed
-        store_tile(j0);
+    // ---- merge the NS split waves of each head and write the block's rows.
+    // Every wave rescales its partial sums to the common max first, so the
+    // merge is a plain sum; the split-0 wave of each head adds the others
+    // (read through LDS, one head_dim block at a time) and writes the output.
+    auto finish_block = [&](uint8_t* scK, uint8_t* scV) {
+        const auto slot_ptr = [&](int slot) {
+            return reinterpret_cast<float*>(slot < C::SLOTS_K ? scK + slot * 4096 : scV + (slot - C::SLOTS_K) * 4096);
+        };
+        __syncthreads();  // every wave is done with this stage's K/V
+        if (g == 0) mbuf[hr][sp][l32] = m_run;
         __syncthreads();
-        if (j0 + kBK <= wg_last) load_tile(j0 + kBK);  // next tile's loads overlap this tile's math
-        if (j0 > wave_last) continue;                 // every key of this tile is in this wave's future
-
-        // S^T for 64 keys x 32 queries: two 32x32 blocks, started at the key bias.
-        f32x16 sacc[2];
+        float m_tot = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int s = 0; s < NS; ++s) m_tot = fmaxf(m_tot, mbuf[hr][s][l32]);
+        const float f = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_tot);
+        const float l_half = l_run + __shfl_xor(l_run, 32, 64);
+        if (g == 0) lbuf[hr][sp][l32] = l_half * f;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+            o[db] *= f;
+            if (NS > 1) {
+                if (sp != 0) {
+                    float* dst = slot_ptr(hr * (NS - 1) + sp - 1) + lane * 16;
+#pragma unroll
+                    for (int i4 = 0; i4 < 4; ++i4)
+                        *reinterpret_cast<float4*>(dst + 4 * i4) =
+                            float4{o[db][4 * i4], o[db][4 * i4 + 1], o[db][4 * i4 + 2], o[db][4 * i4 + 3]};
+                }
+                __syncthreads();
+                if (sp == 0) {
+#pragma unroll
+                    for (int s = 1; s < NS; ++s) {
+                        const float* src = slot_ptr(hr * (NS - 1) + s - 1) + lane * 16;
+#pragma unroll
+                        for (int i4 = 0; i4 < 4; ++i4) {
+                            const float4 x = *reinterpret_cast<const float4*>(src + 4 * i4);
+                            o[db][4 * i4] += x.x;
+                            o[db][4 * i4 + 1] += x.y;
+                            o[db][4 * i4 + 2] += x.z;
+                            o[db][4 * i4 + 3] += x.w;
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        if (sp != 0 || t >= nk) return;
+        float l_tot = 0.0f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) l_tot += lbuf[hr][s][l32];
+        const float inv = 1.0f / l_tot;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-                const float4 bv = *reinterpret_cast<const float4*>(&sBias[hl][kb * 32 + 8 * i4 + 4 * g]);
-                sacc[kb][4 * i4 + 0] = bv.x;
-                sacc[kb][4 * i4 + 1] = bv.y;
-                sacc[kb][4 * i4 + 2] = bv.z;
-                sacc[kb][4 * i4 + 3] = bv.w;
+                const int dd = db * 32 + 8 * i4 + 4 * g;
+                const int64_t off = ((int64_t)t * hq + h) * D + dd;
+                const float y0 = o[db][4 * i4] * inv, y1 = o[db][4 * i4 + 1] * inv;
+                const float y2 = o[db][4 * i4 + 2] * inv, y3 = o[db][4 * i4 + 3] * inv;
+                if (OUT_F32) {
+                    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + off) = float4{y0, y1, y2, y3};
+                } else {
+                    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + off) =
+                        u32x2{tgd::cvt_pk_bf16(y0, y1), tgd::cvt_pk_bf16(y2, y3)};
+                }
             }
+        }
+    };
+
+    // ---- one 32-key block of this wave's slice: S^T, online softmax, P.V.
+    auto key_block = [&](int k0, int rbase, const uint8_t* __restrict__ tK, const uint8_t* __restrict__ tV,
+                         const float* __restrict__ tS) {
+        // S^T for 32 keys x 32 queries, started at the key bias.
+        f32x16 sacc;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const float4 sv = *reinterpret_cast<const float4*>(&tS[rbase + 8 * i4 + 4 * g]);
+            sacc[4 * i4 + 0] = sg * sv.x;
+            sacc[4 * i4 + 1] = sg * sv.y;
+            sacc[4 * i4 + 2] = sg * sv.z;
+            sacc[4 * i4 + 3] = sg * sv.w;
         }
 #pragma unroll
         for (int s = 0; s < C::QS; ++s) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const u32x4 a = *reinterpret_cast<const u32x4*>(&sK[(kb * 32 + l32) * C::LDK + s * 16 + g * 8]);
-                sacc[kb] = tgd::mfma32(a, qreg[s], sacc[kb]);
-            }
+            const int row = rbase + l32;
+            const u32x4 a = *reinterpret_cast<const u32x4*>(tK + row * C::ROW_BYTES +
+                                                             16 * ((2 * s + g) ^ swz<C::PIECES>(row)));
+            sacc = tgd::mfma32(a, qreg[s], sacc);
         }
 
-        // logits in the exp2 domain, causal mask, tile max
-        const bool diag = j0 + kBK - 1 > q0;
-        float mt = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        // Logits in the exp2 domain are z = a_t * S.  When every row of the
+        // wave has a_t > 0 the block max is a_t * max(S) (rounding is
+        // monotonic), so p = 2^(a_t * S - m) is one FMA and one exp2.
+        // Otherwise (a temperature <= 0, possible when few early tokens were
+        // kept) z is formed explicitly first.
+        const bool diag = k0 + 31 > q0;
+        float mt = -INFINITY, a_eff;
+        if (__builtin_expect(all_pos, 1)) {
+            a_eff = a_t;
+            float smax = -INFINITY;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                float z = sacc[kb][i] * a_t;
-                if (diag) {
-                    const int j = j0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-                    if (j > t) z = -INFINITY;
-                }
-                sacc[kb][i] = z;
+                if (diag && k0 + 8 * (i >> 2) + 4 * g + (i & 3) > t) sacc[i] = -INFINITY;
+                smax = fmaxf(smax, sacc[i]);
+            }
+            mt = a_t * smax;
+        } else {
+            a_eff = 1.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float z = a_t * sacc[i];
+                if (diag && k0 + 8 * (i >> 2) + 4 * g + (i & 3) > t) z = -INFINITY;
+                sacc[i] = z;
                 mt = fmaxf(mt, z);
             }
         }
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
         const float m_new = fmaxf(m_run, mt);
-        const float alpha = exp2f(m_run - m_new);
+        // rows with no visible key yet in this split keep m = -inf
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        const bool moved = m_new != m_run;
         m_run = m_new;
         float ls = 0.0f;
-        u32x4 pb[2][2];  // P^T as bf16, [key block][k-step]
+        u32x4 pb[2];  // P^T as bf16, by k-step
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int i = 0; i < 16; i += 2) {
-                const float p0 = exp2f(sacc[kb][i] - m_new);
-                const float p1 = exp2f(sacc[kb][i + 1] - m_new);
-                ls += p0 + p1;
-                pb[kb][i >> 3][(i & 7) >> 1] = tgd::pack_bf16x2(p0, p1);
-            }
+        for (int i = 0; i < 16; i += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[i], a_eff, -m_use));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[i + 1], a_eff, -m_use));
+            ls += p0 + p1;
+            pb[i >> 3][(i & 7) >> 1] = tgd::cvt_pk_bf16(p0, p1);
         }
         l_run = l_run * alpha + ls;
+        if (__builtin_amdgcn_ballot_w64(moved)) {  // skip the rescale when no row max moved
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
+            for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
+        }
 
-        // O^T += V^T . P^T
+        // O^T += V^T . P^T.  The transposing read gives lane jj of each
+        // 16-lane group four consecutive keys of head_dim column dbase+jj when
+        // loading lane a+4e of the group addresses key row kbase+e, columns
+        // dbase+4a .. dbase+4a+3.
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int s = 0; s < 2; ++s) {
+            const int kbase = rbase + 16 * s + 4 * (quad >> 1);
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int key = kb * 32 + 16 * s + 4 * g;
+            for (int db = 0; db < C::DB; ++db) {
+                const int dcol = db * 32 + 16 * (quad & 1) + tr_col;
+                u32x4 a;
 #pragma unroll
-                for (int db = 0; db < C::DB; ++db) {
-                    const uint16_t* vr = &sVt[(db * 32 + l32) * C::LDV];
-                    const u32x2 lo = *reinterpret_cast<const u32x2*>(vr + key);
-                    const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + key + 8);
-                    const u32x4 a = u32x4{lo[0], lo[1], hi[0], hi[1]};
-                    o[db] = tgd::mfma32(a, pb[kb][s], o[db]);
+                for (int half = 0; half < 2; ++half) {
+                    const int row = kbase + 8 * half + tr_row;
+                    const int off = row * C::ROW_BYTES + 16 * ((dcol >> 3) ^ swz<C::PIECES>(row)) +
+                                    8 * ((dcol >> 2) & 1);
+                    const bf16x4_t x =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((TG_LDS bf16x4_t*)((TG_LDS uint8_t*)tV + off));
+                    const u32x2 w = __builtin_bit_cast(u32x2, x);
+                    a[2 * half] = w[0];
+                    a[2 * half + 1] = w[1];
                 }
+                o[db] = tgd::mfma32(a, pb[s], o[db]);
             }
         }
-    }
+    };
 
-    // ---- normalise and write this lane's query row
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    if (t >= nk) return;
-    const float inv = 1.0f / l_tot;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-            const int dd = db * 32 + 8 * i4 + 4 * g;
-            const int64_t off = ((int64_t)t * hq + h) * D + dd;
-            const float y0 = o[db][4 * i4] * inv, y1 = o[db][4 * i4 + 1] * inv;
-            const float y2 = o[db][4 * i4 + 2] * inv, y3 = o[db][4 * i4 + 3] * inv;
-            if (OUT_F32) {
-                *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + off) = float4{y0, y1, y2, y3};
-            } else {
-                *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + off) =
-                    u32x2{tgd::pack_bf16x2(y0, y1), tgd::pack_bf16x2(y2, y3)};
-            }
+    // ---- this wave's slice of one super-tile: keys j0 + WKEYS*sp .. +WKEYS-1,
+    // taken as KB blocks of 32 one after another.
+    auto compute = [&](int j0, const uint8_t* __restrict__ tK, const uint8_t* __restrict__ tV,
+                       const float* __restrict__ tS) {
+#pragma unroll 1
+        for (int kb = 0; kb < KB; ++kb) {  // one block at a time keeps the register footprint of one
+            const int k0 = j0 + C::WKEYS * sp + 32 * kb;
+            if (k0 > wave_last) break;  // the rest of the slice is in this wave's future
+            key_block(k0, C::WKEYS * sp + 32 * kb, tK, tV, tS);
         }
+    };
+
+    // One iteration: wait for its loads, start the next iteration's loads into
+    // the other stage (every wave finished reading it: barrier at the end of
+    // the previous iteration), multiply.  Current and next stage are distinct
+    // restrict pointers of one scope, so the reads of this stage never wait on
+    // the loads in flight into the other.
+    auto iterate = [&](int it, uint8_t* __restrict__ cK, uint8_t* __restrict__ cV, float* __restrict__ cS,
+                       uint8_t* __restrict__ nK, uint8_t* __restrict__ nV, float* __restrict__ nS) {
+        const bool inA = it < nA;
+        const int st = inA ? it : it - nA;
+        if (st == 0) begin_block(inA ? qbA : qbB);
+        TG_WAIT_VMCNT(0);
+        __builtin_amdgcn_s_barrier();
+        if (it + 1 < ntot) issue(it + 1, nK, nV, nS);
+        compute(st * C::SKEYS, cK, cV, cS);
+        const int last = inA ? nA - 1 : ntot - nA - 1;
+        if (st == last) finish_block(cK, cV);  // K and V of this stage serve as merge scratch
+        __builtin_amdgcn_s_barrier();      // this stage is free for the next issue
+    };
+
+    issue(0, sK0, sV0, sS0);
+    for (int it = 0; it < ntot; it += 2) {
+        iterate(it, sK0, sV0, sS0, sK1, sV1, sS1);
+        if (it + 1 < ntot) iterate(it + 1, sK1, sV1, sS1, sK0, sV0, sS0);
     }
 }
 
-template <int D, int HPW>
+template <int D, int HPW, int RB, int NS, int KB>
 int launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* ks, const float* gains,
                 float c, const int32_t* pos, int64_t nk, int hq, int hkv, void* out, int out_dtype,
                 hipStream_t s) {
-    using C = AttnCfg<D, HPW>;
-    const int n_qtiles = (int)((nk + C::QROWS - 1) / C::QROWS);
-    const int n_items = hkv * (hq / hkv / HPW) * n_qtiles;
+    using C = AttnCfg<D, HPW, RB, NS, KB>;
+    const int nqb = (int)((nk + C::QROWS - 1) / C::QROWS);
+    const int npairs = (nqb + 1) / 2;
+    const int n_items = hkv * (hq / hkv / HPW) * npairs;
     const int per_xcd = (n_items + kXcds - 1) / kXcds;
     const dim3 grid((unsigned)(per_xcd * kXcds));
     if (out_dtype == 1)
-        hipLaunchKernelGGL((gated_attn<D, HPW, true>), grid, dim3(kThreads), 0, s, q, k, v, ks, gains, c, pos,
-                           (int)nk, hq, hkv, n_qtiles, per_xcd, n_items, out);
+        hipLaunchKernelGGL((gated_attn<D, HPW, RB, NS, KB, true>), grid, dim3(C::THREADS), 0, s, q, k, v, ks, gains,
+                           c, pos, (int)nk, hq, hkv, npairs, per_xcd, n_items, out);
     else
-        hipLaunchKernelGGL((gated_attn<D, HPW, false>), grid, dim3(kThreads), 0, s, q, k, v, ks, gains, c, pos,
-                           (int)nk, hq, hkv, n_qtiles, per_xcd, n_items, out);
+        hipLaunchKernelGGL((gated_attn<D, HPW, RB, NS, KB, false>), grid, dim3(C::THREADS), 0, s, q, k, v, ks, gains,
+                           c, pos, (int)nk, hq, hkv, npairs, per_xcd, n_items, out);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_EDEVICE;
+}
+
+// Work items of a launch with query blocks of 32 * rb rows and hpw heads per workgroup.
+inline int64_t attn_items(int64_t nk, int hq, int hkv, int hpw, int rb) {
+    const int64_t nqb = (nk + 32 * rb - 1) / (32 * rb);
+    return (int64_t)hkv * (hq / hkv / hpw) * ((nqb + 1) / 2);
+}
+
+// Workgroups of eight waves (four when a kv head has a single q head):
+// heads sharing K/V x query row blocks x key splits.  Take the tallest query
+// blocks (most K/V reuse per byte read) that still give every CU a
+// workgroup; key splits make up the rest of the waves.  Super-tiles hold at
+// most 128 keys (64 KB of K and V per stage at head_dim 128).
+template <int D, int HPW>
+int launch_attn_h(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* ks, const float* gains,
+                  float c, const int32_t* pos, int64_t nk, int hq, int hkv, void* out, int out_dtype,
+                  hipStream_t s) {
+    constexpr int kCUs = 256;
+    constexpr int W = HPW == 1 ? 4 : 8 / HPW;  // row blocks x splits
+    if constexpr (W >= 4) {
+        if (attn_items(nk, hq, hkv, HPW, 4) >= kCUs)
+            return launch_attn<D, HPW, 4, W / 4, 2>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, s);
+    }
+    if constexpr (W >= 2) {
+        if (attn_items(nk, hq, hkv, HPW, 2) >= kCUs)
+            return launch_attn<D, HPW, 2, W / 2, 2>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, s);
+    }
+    return launch_attn<D, HPW, 1, W, (W >= 4 ? 1 : 2)>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, s);
 }
 
 template <int D>
@@ -291,9 +442,9 @@ int launch_attn_d(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
                   float c, const int32_t* pos, int64_t nk, int hq, int hkv, void* out, int out_dtype,
                   hipStream_t s) {
     const int G = hq / hkv;
-    if (G % 4 == 0) return launch_attn<D, 4>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, s);
-    if (G % 2 == 0) return launch_attn<D, 2>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, s);
-    return launch_attn<D, 1>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, s);
+    if (G % 4 == 0) return launch_attn_h<D, 4>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, s);
+    if (G % 2 == 0) return launch_attn_h<D, 2>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, s);
+    return launch_attn_h<D, 1>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, s);
 }
 
 }  // namespace

@@ -14,10 +14,13 @@
 // C^T = W1 . H^T: each lane then owns one token column and 16 hidden rows per
 // block, so GELU, the w2 dot product and the reduction over hidden units stay
 // in registers except for one exchange between the two half-waves and one
-// between waves.  Operand tiles of 64 d-columns are double-buffered in LDS;
-// the next tile's global loads are in flight while the current tile is
-// multiplied.  The row sums of squares come from the same LDS tiles.  Each
-// workgroup also writes the sum of its scores' squares (fixed order).
+// between waves.  Residual and W1 tiles of 64 d-columns go from memory
+// straight into a three-stage LDS ring with 16-byte direct loads (two tiles
+// in flight while the third is multiplied; W1 is re-read from L2 by every
+// workgroup, the residual once from HBM).  Rows are stored with their eight
+// 16-byte pieces XOR-permuted so the operand reads spread over the banks.
+// The row sums of squares come from the same operand reads.  Each workgroup
+// also writes the sum of its scores' squares (fixed order).
 //
 // Kernel 2 (gate_seqnorm): every workgroup reduces those per-block partial
 // sums in the same fixed order (fp64), forms rho = sqrt(mean s^2 + eps) and
@@ -36,7 +39,6 @@ using tgd::u32x4;
 constexpr int kThreads = 256;
 constexpr int kBT = tgi::kGateRowsPerBlock;  // 64 rows per workgroup
 constexpr int kKC = 64;                      // d-columns per LDS tile
-constexpr int kLd = kKC + 8;                 // padded LDS row (bf16 elements), 144 bytes
 
 template <int HD>
 struct Cfg {
@@ -46,14 +48,59 @@ struct Cfg {
     static constexpr int WT = kBT / WAVES_T;            // tokens per wave
     static constexpr int MB = WH / 32;                  // 32-row blocks of hidden units
     static constexpr int NB = WT / 32;                  // 32-column blocks of tokens
-    static constexpr int H_PIECES = kBT * kKC / 8 / kThreads;  // 16-byte loads per thread
-    static constexpr int W_PIECES = HD * kKC / 8 / kThreads;
     static_assert(MB >= 1 && NB >= 1, "tile shape");
 };
 
 __device__ __forceinline__ float gelu_erf(float a) {
     return 0.5f * a * (1.0f + erff(a * 0.70710678118654752440f));
 }
+
+// Permutation of the eight 16-byte pieces of a 128-byte LDS row: rotate the
+// row index left by one over three bits (spreads the operand reads of eight
+// consecutive rows over all banks).
+__device__ __forceinline__ int swz8(int r) { return ((r << 1) | (r >> 2)) & 7; }
+
+#define TG_LDS __attribute__((address_space(3)))
+
+// N 16-byte LDS reads issued together, waited for before the block ends.
+template <int N>
+__device__ __forceinline__ void lds_read_wait(u32x4 (&v)[N], const uint32_t (&a)[N]);
+template <>
+__device__ __forceinline__ void lds_read_wait<2>(u32x4 (&v)[2], const uint32_t (&a)[2]) {
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1])
+        : "v"(a[0]), "v"(a[1])
+        : "memory");
+}
+template <>
+__device__ __forceinline__ void lds_read_wait<3>(u32x4 (&v)[3], const uint32_t (&a)[3]) {
+    asm volatile(
+        "ds_read_b128 %0, %3\n\t"
+        "ds_read_b128 %1, %4\n\t"
+        "ds_read_b128 %2, %5\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2])
+        : "memory");
+}
+template <>
+__device__ __forceinline__ void lds_read_wait<4>(u32x4 (&v)[4], const uint32_t (&a)[4]) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+        : "memory");
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+#define TG_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
 template <int HD>
 __global__ __launch_bounds__(kThreads) void gate_mlp(const uint16_t* __restrict__ resid,
@@ -64,8 +111,16 @@ __global__ __launch_bounds__(kThreads) void gate_mlp(const uint16_t* __restrict_
                                                      float* __restrict__ s_out,
                                                      float* __restrict__ block_ss) {
     using C = Cfg<HD>;
-    __shared__ __attribute__((aligned(16))) uint16_t sH[2][kBT * kLd];
-    __shared__ __attribute__((aligned(16))) uint16_t sW[2][HD * kLd];
+    constexpr int H_BYTES = kBT * kKC * 2;            // residual tile: 64 rows x 128 bytes
+    constexpr int W_BYTES = HD * kKC * 2;             // W1 tile: HD rows x 128 bytes
+    constexpr int STAGE = H_BYTES + W_BYTES;
+    constexpr int H_LOADS = H_BYTES / 1024 / 4;       // 1 KB direct-load instructions per wave
+    constexpr int W_LOADS = W_BYTES / 1024 / 4;
+    constexpr int VM_PER_TILE = H_LOADS + W_LOADS;
+    // three pipeline stages, separate objects (see the tile loop)
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t st2[STAGE];
     __shared__ float sB1[HD], sW2[HD];
     __shared__ float sSq[C::WAVES_H][kBT];
     __shared__ float sPart[C::WAVES_H][kBT];
@@ -76,37 +131,32 @@ __global__ __launch_bounds__(kThreads) void gate_mlp(const uint16_t* __restrict_
     const int wh = wave % C::WAVES_H, wt = wave / C::WAVES_H;
     const int l32 = lane & 31, g = lane >> 5;
     const int64_t row0 = (int64_t)blockIdx.x * kBT;
+    const int nchunks = d / kKC;
 
     for (int j = tid; j < HD; j += kThreads) {
         sB1[j] = b1 ? tgd::bf16lo(b1[j]) : 0.0f;
         sW2[j] = tgd::bf16lo(w2[j]);
     }
 
-    u32x4 hreg[C::H_PIECES], wreg[C::W_PIECES];
-    auto load_tile = [&](int c) {
-        const int col0 = c * kKC;
+    // Direct HBM -> LDS loads of one 64-column tile: each wave instruction
+    // fills one 1 KB block = 8 rows of 128 bytes; lane l writes slot l%8 of
+    // row l/8 with the piece (l%8) ^ swz8(row).  Residual rows past n repeat
+    // row n-1 (their scores are never written).
+    auto issue = [&](int c, uint8_t* stg) {
+        const int slot = lane & 7;
 #pragma unroll
-        for (int r = 0; r < C::H_PIECES; ++r) {
-            int p = tid + kThreads * r, row = p >> 3, col = (p & 7) * 8;
-            int64_t gr = row0 + row;
-            hreg[r] = gr < n ? *reinterpret_cast<const u32x4*>(resid + gr * d + col0 + col) : u32x4{0, 0, 0, 0};
+        for (int r = 0; r < H_LOADS; ++r) {
+            const int blk = r * 4 + wave, row = blk * 8 + (lane >> 3);
+            const int64_t gr = min(row0 + row, n - 1);
+            const uint16_t* src = resid + gr * d + c * kKC + 8 * (slot ^ swz8(row));
+            __builtin_amdgcn_global_load_lds(src, (TG_LDS void*)((TG_LDS uint8_t*)stg + blk * 1024), 16, 0, 0);
         }
 #pragma unroll
-        for (int r = 0; r < C::W_PIECES; ++r) {
-            int p = tid + kThreads * r, row = p >> 3, col = (p & 7) * 8;
-            wreg[r] = *reinterpret_cast<const u32x4*>(w1 + (int64_t)row * d + col0 + col);
-        }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int r = 0; r < C::H_PIECES; ++r) {
-            int p = tid + kThreads * r, row = p >> 3, col = (p & 7) * 8;
-            *reinterpret_cast<u32x4*>(&sH[buf][row * kLd + col]) = hreg[r];
-        }
-#pragma unroll
-        for (int r = 0; r < C::W_PIECES; ++r) {
-            int p = tid + kThreads * r, row = p >> 3, col = (p & 7) * 8;
-            *reinterpret_cast<u32x4*>(&sW[buf][row * kLd + col]) = wreg[r];
+        for (int r = 0; r < W_LOADS; ++r) {
+            const int blk = r * 4 + wave, row = blk * 8 + (lane >> 3);
+            const uint16_t* src = w1 + (int64_t)row * d + c * kKC + 8 * (slot ^ swz8(row));
+            __builtin_amdgcn_global_load_lds(src, (TG_LDS void*)((TG_LDS uint8_t*)stg + H_BYTES + blk * 1024), 16,
+                                             0, 0);
         }
     };
 
@@ -119,44 +169,71 @@ __global__ __launch_bounds__(kThreads) void gate_mlp(const uint16_t* __restrict_
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) ssq[nb] = 0.0f;
 
-    const int nchunks = d / kKC;
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-    for (int c = 0; c < nchunks; ++c) {
-        const int buf = c & 1;
-        if (c + 1 < nchunks) load_tile(c + 1);
-        const uint16_t* tH = sH[buf];
-        const uint16_t* tW = sW[buf];
+    // Per-lane LDS byte offsets (within a stage) of the operand rows, without
+    // the piece: B (residual) rows first, then A (W1) rows.
+    uint32_t roff[C::NB + C::MB];
+    int rswz[C::NB + C::MB];
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) {
+        const int row = wt * C::WT + nb * 32 + l32;
+        roff[nb] = row * 128;
+        rswz[nb] = swz8(row);
+    }
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) {
+        const int row = wh * C::WH + mb * 32 + l32;
+        roff[C::NB + mb] = H_BYTES + row * 128;
+        rswz[C::NB + mb] = swz8(row);
+    }
+
+    // One tile: wait for its loads (the next tile's stay in flight), start the
+    // loads two tiles ahead into the stage every wave finished reading at the
+    // previous step, multiply.  k-step s of half-wave g reads piece 2s+g of a
+    // row.  The operand reads are issued from inline assembly that waits for
+    // them before it ends: the compiler cannot tell these LDS reads from the
+    // loads in flight into the other stages and would otherwise wait for all
+    // of them; the explicit vector-memory waits above order them instead.
+    auto step = [&](int c, const uint8_t* cur, uint8_t* ahead) {
+        if (c + 1 < nchunks) {
+            TG_WAIT_VMCNT(VM_PER_TILE);
+        } else {
+            TG_WAIT_VMCNT(0);
+        }
+        __builtin_amdgcn_s_barrier();
+        if (c + 2 < nchunks) issue(c + 2, ahead);
+        const uint32_t base = (uint32_t)(uintptr_t)(const TG_LDS uint8_t*)cur;
 #pragma unroll
         for (int s = 0; s < kKC / 16; ++s) {
-            const int kof = s * 16 + g * 8;
-            u32x4 a[C::MB], b[C::NB];
+            u32x4 op[C::NB + C::MB];
+            uint32_t addr[C::NB + C::MB];
 #pragma unroll
-            for (int mb = 0; mb < C::MB; ++mb)
-                a[mb] = *reinterpret_cast<const u32x4*>(&tW[(wh * C::WH + mb * 32 + l32) * kLd + kof]);
-#pragma unroll
-            for (int nb = 0; nb < C::NB; ++nb)
-                b[nb] = *reinterpret_cast<const u32x4*>(&tH[(wt * C::WT + nb * 32 + l32) * kLd + kof]);
+            for (int i = 0; i < C::NB + C::MB; ++i) addr[i] = base + roff[i] + 16 * ((2 * s + g) ^ rswz[i]);
+            lds_read_wait<C::NB + C::MB>(op, addr);
 #pragma unroll
             for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-                for (int nb = 0; nb < C::NB; ++nb) acc[mb][nb] = tgd::mfma32(a[mb], b[nb], acc[mb][nb]);
+                for (int nb = 0; nb < C::NB; ++nb)
+                    acc[mb][nb] = tgd::mfma32(op[C::NB + mb], op[nb], acc[mb][nb]);
             // row sums of squares: the waves sharing a token block split the k-steps
             if (s % C::WAVES_H == wh) {
 #pragma unroll
                 for (int nb = 0; nb < C::NB; ++nb) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        float lo = tgd::bf16lo(b[nb][q]), hi = tgd::bf16hi(b[nb][q]);
+                        const float lo = tgd::bf16lo(op[nb][q]), hi = tgd::bf16hi(op[nb][q]);
                         ssq[nb] = fmaf(lo, lo, ssq[nb]);
                         ssq[nb] = fmaf(hi, hi, ssq[nb]);
                     }
                 }
             }
         }
-        if (c + 1 < nchunks) store_tile(buf ^ 1);
-        __syncthreads();
+    };
+    issue(0, st0);
+    if (nchunks > 1) issue(1, st1);
+    for (int c = 0; c < nchunks; c += 3) {
+        step(c, st0, st2);
+        if (c + 1 < nchunks) step(c + 1, st1, st0);
+        if (c + 2 < nchunks) step(c + 2, st2, st1);
     }
 
     // Row norms: combine the two half-waves, then the waves of a token block.

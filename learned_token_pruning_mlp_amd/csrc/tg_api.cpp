@@ -59,7 +59,8 @@ int tg_select_topk(const float* score, const uint8_t* forced, int64_t n, int64_t
     if (n < 1 || n > kMaxRows || k < 1 || k > n || n_forced < 0 || n_forced > k) return TG_EINVAL;
     if (!forced && n_forced != 0) return TG_EINVAL;
     if (!score || !kept_idx) return TG_EINVAL;
-    if (!aligned(score, 4) || !aligned(kept_idx, 4) || (dev_status && !aligned(dev_status, 4)))
+    if (!aligned(score, 16) || (forced && !aligned(forced, 4)) || !aligned(kept_idx, 4) ||
+        (dev_status && !aligned(dev_status, 4)))
         return TG_EALIGN;
     if (!workspace || workspace_bytes < tgi::workspace_bytes(n)) return TG_EWORKSPACE;
     if (!aligned(workspace, 16)) return TG_EALIGN;

@@ -30,6 +30,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 pair with the hardware converter (v_cvt_pk_bf16_f32,
+// round to nearest even); lo lands in bits 0..15.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
 // 32x32x16 bf16 matrix-core product: C += A * B.
 // A: lane l holds row (l % 32), 8 k-values of k-group (l / 32).
 // B: lane l holds column (l % 32), the same 8 k-values of k-group (l / 32).

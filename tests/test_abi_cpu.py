@@ -91,7 +91,8 @@ def test_select_checks(lib):
     assert _sel(lib, forced=None) == E.TG_EINVAL  # forced count without a mask
     assert _sel(lib, score=None) == E.TG_EINVAL
     assert _sel(lib, kept=None) == E.TG_EINVAL
-    assert _sel(lib, score=A + 1) == E.TG_EALIGN
+    assert _sel(lib, score=A + 4) == E.TG_EALIGN
+    assert _sel(lib, forced=A + 2) == E.TG_EALIGN
     assert _sel(lib, ws=None) == E.TG_EWORKSPACE
     assert _sel(lib, ws_bytes=16) == E.TG_EWORKSPACE
 
