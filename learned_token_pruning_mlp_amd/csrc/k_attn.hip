@@ -34,9 +34,9 @@
 //  * K and V super-tiles go from memory straight into LDS with 16-byte
 //    direct loads, double-buffered (the next super-tile is in flight while
 //    this one is multiplied).  Rows are stored with their 16-byte pieces
-//    XOR-permuted by rotl(row), which keeps the K-operand reads and the
-//    transposing V reads (ds_read_b64_tr_b16, which hands each lane four keys
-//    of one head_dim column) free of bank conflicts.
+//    XOR-permuted by a function of the row that keeps the K-operand reads
+//    and the transposing V reads (ds_read_b64_tr_b16, which hands each lane
+//    four keys of one head_dim column) free of LDS bank conflicts.
 //  * Work items are laid out so all workgroups of one kv head run on the same
 //    XCD (workgroups go round-robin over the 8 XCDs), keeping that head's K/V
 //    in one L2.
@@ -83,12 +83,22 @@ struct AttnCfg {
     static_assert(SLOTS <= 2 * SLOTS_K, "merge scratch");
 };
 
-// Permutation of the 16-byte pieces inside a K/V row: rotate the row index
-// left by one over log2(pieces) bits.
+// Permutation of the 16-byte pieces inside a K/V row (XOR mask by row).
+// gfx950 LDS has 64 banks; a 16-byte read serves 16 consecutive lanes per
+// cycle and needs their (address/16) mod 16 distinct, the transposing 8-byte
+// read serves 32 lanes per cycle and needs (address/8) mod 32 distinct.
+// 256-byte rows: swap the two-bit halves of row mod 16 (a bijection over any
+// 16 consecutive rows for the K-operand reads; rows 4k..4k+3 differ in the
+// upper two bits for the transposing V reads).  128-byte rows (two rows per
+// bank sweep): rotate (row/2) mod 8 right by one bit.
 template <int PIECES>
 __device__ __forceinline__ int swz(int r) {
-    if (PIECES == 16) return ((r << 1) | (r >> 3)) & 15;
-    return ((r << 1) | (r >> 2)) & 7;
+    if (PIECES == 16) {
+        const int x = r & 15;
+        return ((x << 2) | (x >> 2)) & 15;
+    }
+    const int x = (r >> 1) & 7;
+    return ((x & 1) << 2) | (x >> 1);
 }
 
 template <int D, int HPW, int RB, int NS, int KB, bool OUT_F32>

@@ -55,10 +55,15 @@ __device__ __forceinline__ float gelu_erf(float a) {
     return 0.5f * a * (1.0f + erff(a * 0.70710678118654752440f));
 }
 
-// Permutation of the eight 16-byte pieces of a 128-byte LDS row: rotate the
-// row index left by one over three bits (spreads the operand reads of eight
-// consecutive rows over all banks).
-__device__ __forceinline__ int swz8(int r) { return ((r << 1) | (r >> 2)) & 7; }
+// Permutation of the eight 16-byte pieces of a 128-byte LDS row (XOR mask
+// by row).  gfx950 LDS has 64 banks and a 16-byte read serves 16 consecutive
+// lanes per cycle, which need distinct (address/16) mod 16: two 128-byte rows
+// span the banks once, so rotating (row/2) mod 8 right by one bit gives the
+// 16 rows read together 16 distinct bank groups.
+__device__ __forceinline__ int swz8(int r) {
+    const int x = (r >> 1) & 7;
+    return ((x & 1) << 2) | (x >> 1);
+}
 
 #define TG_LDS __attribute__((address_space(3)))
 

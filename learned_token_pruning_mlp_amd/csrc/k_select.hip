@@ -8,17 +8,22 @@
 //
 // Exact radix select on order-preserving 32-bit keys:
 //   key(x) grows with x; -0.0 maps like +0.0; NaN maps to 0 (below -inf).
-// Four 8-bit digit rounds find the key T of the (K-F)-th best prunable token
-// and the number m of tokens equal to T that are taken (the m lowest-index
-// ones).  The emit pass then writes the kept indices in ascending order:
-// token i goes to slot (#forced-or-above-T before i) + min(#ties before i, m).
-// Everything is integer arithmetic, so the result is bit-exact and
-// deterministic.
+// Three digit rounds (11, 11 and 10 bits) find the key T of the (K-F)-th best
+// prunable token and the number m of tokens equal to T that are taken (the m
+// lowest-index ones).  The emit pass then writes the kept indices in
+// ascending order: token i goes to slot (#forced-or-above-T before i) +
+// min(#ties before i, m).  Everything is integer arithmetic, so the result is
+// bit-exact and deterministic.
 //
 // One workgroup of 1024 threads does the whole selection (one launch, no
 // workspace traffic).  Up to 32768 tokens the keys stay in LDS (128 KB of the
-// CU's 160 KB) after one read of the scores; longer prompts re-read the
-// scores (L2-resident) in each round.
+// CU's 160 KB) after one read of the scores, and the first histogram is built
+// during that read.  The keys of the bucket chosen by the first round (for
+// real score distributions a small fraction) are then gathered into LDS so
+// the two later rounds only look at them; when the bucket is too large for
+// the gather buffer (e.g. all scores equal) those rounds sweep all keys with
+// a prefix filter instead.  Longer prompts re-read the scores (L2-resident)
+// in each sweep.
 #include <hip/hip_runtime.h>
 
 #include "tg_device.h"
@@ -68,26 +73,6 @@ __device__ __forceinline__ uint64_t block_excl_scan(uint64_t x, uint64_t* wsum, 
     return r;
 }
 
-// Adds one count per active lane to hist[bin].  Keys of real data often share
-// a few digit values (a Gaussian score has most of its mass in two or three
-// top-byte bins), and 64 lanes adding to one LDS word serialise.  So the
-// bins of the first two active lanes are counted with a ballot and added once
-// each; the remaining lanes, now mostly spread out, use plain LDS atomics.
-__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool act, int lane) {
-#pragma unroll
-    for (int peel = 0; peel < 2; ++peel) {
-        const uint64_t am = __builtin_amdgcn_ballot_w64(act);
-        if (am == 0) return;
-        const int leader = __builtin_ctzll(am);
-        const uint32_t lb = __builtin_amdgcn_readlane(bin, leader);
-        const bool same = act && bin == lb;
-        const uint64_t sm = __builtin_amdgcn_ballot_w64(same);
-        if (lane == leader) atomicAdd(&hist[lb], (uint32_t)__builtin_popcountll(sm));
-        act = act && !same;
-    }
-    if (act) atomicAdd(&hist[bin], 1u);
-}
-
 // Keys of tokens i .. i+3 (i a multiple of 4), straight from the scores.
 __device__ __forceinline__ uint4 keys4_global(const float* __restrict__ score, const uint8_t* __restrict__ forced,
                                               uint32_t i, uint32_t n) {
@@ -118,24 +103,65 @@ __global__ __launch_bounds__(kThreads) void select_topk_block(const float* __res
                                                               int64_t n64, int64_t n_forced, int64_t k64,
                                                               int32_t* __restrict__ kept,
                                                               int32_t* __restrict__ dev_status) {
+    constexpr int kBins = 2048;
+    constexpr int kCap = 4096;  // gathered candidates
     __shared__ __attribute__((aligned(16))) uint32_t keys[kKeysInLds ? kLdsKeys : 4];
-    __shared__ uint32_t whist[kWaves][256];
+    __shared__ uint32_t hist[kBins];
+    __shared__ __attribute__((aligned(16))) uint32_t cand[kCap];
     __shared__ uint64_t wsum[kWaves + 1];
     __shared__ uint32_t ctl[4];
-    __shared__ uint32_t wtot[4];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
     const uint32_t n = (uint32_t)n64, k = (uint32_t)k64;
     constexpr uint32_t kStep = kThreads * 16;  // tokens per sweep step: 4 groups of 4 per thread
 
     // Keys of 4 consecutive tokens starting at i (a multiple of 4; entries
-    // past n read as kForcedMark-free zeros and are skipped by the callers).
+    // past n are garbage and skipped by the callers).
     auto keys4 = [&](uint32_t i) -> uint4 {
         if (kKeysInLds) return *reinterpret_cast<const uint4*>(&keys[i]);
         return keys4_global(score, forced, i, n);
     };
+    // Sweep every token; f(i, key) for each i < n.
+    auto sweep = [&](auto&& f) {
+        for (uint32_t c0 = 0; c0 < n; c0 += kStep) {
+            uint4 kv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kv[e] = keys4(c0 + (e * kThreads + tid) * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t i = c0 + (e * kThreads + tid) * 4;
+                const uint32_t kk[4] = {kv[e].x, kv[e].y, kv[e].z, kv[e].w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (i + q < n) f(i + q, kk[q]);
+            }
+        }
+    };
+    // Find the bin holding the remaining-th largest key of the histogram
+    // (bins scanned from the top); sets ctl[0] = bin, ctl[1] = rank inside it.
+    auto pick_bin = [&](uint32_t remaining, int nbins) {
+        // thread t owns bins top-down: 2t and 2t+1 counted from the highest bin
+        const int b0 = nbins - 1 - 2 * tid, b1 = b0 - 1;
+        const uint32_t c0 = b0 >= 0 ? hist[b0] : 0, c1 = b1 >= 0 ? hist[b1] : 0;
+        uint64_t tot;
+        const uint32_t before = (uint32_t)block_excl_scan(c0 + c1, wsum, &tot);
+        if (b0 >= 0 && before < remaining && remaining <= before + c0) {
+            ctl[0] = b0;
+            ctl[1] = remaining - before;
+        }
+        if (b1 >= 0 && before + c0 < remaining && remaining <= before + c0 + c1) {
+            ctl[0] = b1;
+            ctl[1] = remaining - before - c0;
+        }
+        __syncthreads();
+    };
+    auto clear_hist = [&]() {
+        for (int b = tid; b < kBins; b += kThreads) hist[b] = 0;
+    };
 
-    // Round 0: count the forced tokens (and park the keys in LDS).
+    // Sweep 1: keys to LDS, forced count, histogram of the top 11 bits.
+    clear_hist();
+    __syncthreads();
     uint64_t fc = 0;
     for (uint32_t c0 = 0; c0 < n; c0 += kStep) {
         uint4 kv[4];
@@ -148,14 +174,16 @@ __global__ __launch_bounds__(kThreads) void select_topk_block(const float* __res
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 if (i + q < n) {
-                    fc += kk[q] == kForcedMark ? 1u : 0u;
+                    const bool f = kk[q] == kForcedMark;
+                    fc += f ? 1u : 0u;
+                    if (!f) atomicAdd(&hist[kk[q] >> 21], 1u);
                     if (kKeysInLds) keys[i + q] = kk[q];
                 }
             }
         }
     }
     uint64_t F;
-    block_excl_scan(fc, wsum, &F);  // its barriers also publish the LDS keys
+    block_excl_scan(fc, wsum, &F);  // its barriers also publish the keys and the histogram
     int64_t R = (int64_t)k - (int64_t)F;  // prunable tokens to choose
     if (tid == 0 && dev_status) {
         int32_t st = 0;
@@ -165,52 +193,45 @@ __global__ __launch_bounds__(kThreads) void select_topk_block(const float* __res
     }
     if (R < 0) R = 0;
 
-    // Rounds 1-4: radix select of the R-th largest prunable key.
-    uint32_t prefix = 0, pmask = 0, remaining = (uint32_t)R;
     uint32_t T = 0xffffffffu, m = 0;  // R == 0: no prunable token is taken
     if (R > 0) {
-        for (int round = 0; round < 4; ++round) {
-            const int shift = 24 - 8 * round;
-            for (int b = tid; b < kWaves * 256; b += kThreads) (&whist[0][0])[b] = 0;
+        // Round 1: top 11 bits.
+        pick_bin((uint32_t)R, kBins);
+        uint32_t prefix = ctl[0] << 21, pmask = 0x7ffu << 21, remaining = ctl[1];
+        const uint32_t bucket = hist[ctl[0]];
+        __syncthreads();
+
+        // Gather the bucket's keys when they fit; otherwise filter on the fly.
+        const bool gathered = bucket <= (uint32_t)kCap;
+        if (gathered) {
+            if (tid == 0) ctl[2] = 0;
             __syncthreads();
-            for (uint32_t c0 = 0; c0 < n; c0 += kStep) {
-                uint4 kv[4];
+            sweep([&](uint32_t, uint32_t key) {
+                if (key != kForcedMark && (key & pmask) == prefix) cand[atomicAdd(&ctl[2], 1u)] = key;
+            });
+            __syncthreads();
+        }
+        // Rounds 2 and 3: next 11 bits, then the last 10.
 #pragma unroll
-                for (int e = 0; e < 4; ++e) kv[e] = keys4(c0 + (e * kThreads + tid) * 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t i = c0 + (e * kThreads + tid) * 4;
-                    const uint32_t kk[4] = {kv[e].x, kv[e].y, kv[e].z, kv[e].w};
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const uint32_t key = kk[q];
-                        const bool act = i + q < n && key != kForcedMark && (key & pmask) == prefix;
-                        hist_add(&whist[wave][0], (key >> shift) & 255u, act, lane);
-                    }
+        for (int round = 0; round < 2; ++round) {
+            const int shift = round == 0 ? 10 : 0;
+            const uint32_t dmask = round == 0 ? 0x7ffu : 0x3ffu;
+            clear_hist();
+            __syncthreads();
+            if (gathered) {
+                for (uint32_t c = tid; c < bucket; c += kThreads) {
+                    const uint32_t key = cand[c];
+                    if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
                 }
+            } else {
+                sweep([&](uint32_t, uint32_t key) {
+                    if (key != kForcedMark && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+                });
             }
             __syncthreads();
-            uint32_t c = 0, incl = 0, b = 0;
-            if (tid < 256) {
-                // bins in descending order: thread t looks at digit 255 - t
-                b = 255u - tid;
-#pragma unroll
-                for (int w = 0; w < kWaves; ++w) c += whist[w][b];
-                incl = wave_incl_scan(c, lane);
-                if (lane == 63) wtot[wave] = incl;
-            }
-            __syncthreads();
-            if (tid < 256) {
-                for (int w = 0; w < wave; ++w) incl += wtot[w];
-                const uint32_t excl = incl - c;
-                if (excl < remaining && remaining <= incl) {
-                    ctl[0] = b;
-                    ctl[1] = remaining - excl;
-                }
-            }
-            __syncthreads();
+            pick_bin(remaining, (int)dmask + 1);
             prefix |= ctl[0] << shift;
-            pmask |= 255u << shift;
+            pmask |= dmask << shift;
             remaining = ctl[1];
             __syncthreads();
         }
@@ -258,6 +279,7 @@ __global__ __launch_bounds__(kThreads) void select_topk_block(const float* __res
         }
         carry += tot;
     }
+    (void)lane;
 }
 
 }  // namespace
