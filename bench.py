@@ -143,66 +143,82 @@ def main():
 
     stages = ["gate_score", "select_topk", "compact", "rope", "gated_attention"]
 
+    def mark(ev, j):
+        if ev is not None and ev[j] is not None:
+            ev[j].record(stream)
+
     def step(i, ev=None):
         r = resid[i % N_RESID_COPIES]
-        if ev is not None:
-            ev[0].record(stream)
+        mark(ev, 0)
         tg.tg_gate_score(r, w1, None, w2, 0.0, 1e-6, 1e-6, s_norm, None, ws)
-        if ev is not None:
-            ev[1].record(stream)
+        mark(ev, 1)
         tg.tg_select_topk(s_norm, forced, shp.n_forced, k, kept, None, ws)
-        if ev is not None:
-            ev[2].record(stream)
+        mark(ev, 2)
         tg.tg_compact(kept, n, r, resid_k, pos, pos_k, s_norm, score_k)
-        if ev is not None:
-            ev[3].record(stream)
+        mark(ev, 3)
         tg.tg_rope(q, pos_k, shp.rope_theta)
         tg.tg_rope(kk, pos_k, shp.rope_theta)
-        if ev is not None:
-            ev[4].record(stream)
+        mark(ev, 4)
         tg.tg_gated_attention(q, kk, vv, score_k, gains, shp.temp_coef, pos_k, out)
-        if ev is not None:
-            ev[5].record(stream)
+        mark(ev, 5)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly `steps` steps, synchronised on both sides
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
+    # ---- per-stage breakdown (outside the timed region): events between all launches
+    n_diag = max(1, min(20, args.steps))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_diag)]
+    for i in range(n_diag):
         step(i, evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-
     per_stage = {s: 0.0 for s in stages}
     for e in evs:
         for j, s in enumerate(stages):
             per_stage[s] += e[j].elapsed_time(e[j + 1])
-    per_stage = {s: v / args.steps for s, v in per_stage.items()}  # ms per launch (rope: both calls)
-    event_ms = sum(per_stage.values())
-
-    # ---- roofline of the dominant kernel
+    per_stage = {s: v / n_diag for s, v in per_stage.items()}  # ms per step (rope: both calls)
     dom = max(per_stage, key=per_stage.get)
+    dom_j = stages.index(dom)
+
+    # ---- timed region: exactly `steps` steps, synchronised on both sides.  Only
+    # the dominant stage is bracketed by events (on the stream its kernel runs on).
+    dom_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+
+    def timed_step(i):
+        marks = [None] * 6
+        marks[dom_j], marks[dom_j + 1] = dom_ev[i]
+        step(i, marks)
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        timed_step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    dom_ms = sum(a.elapsed_time(b) for a, b in dom_ev) / args.steps
+
+    # ---- roofline of the dominant kernel, timed inside the timed region
     if dom == "gated_attention":
-        achieved = attn_flops(shp) / (per_stage[dom] * 1e-3) / 1e12
+        achieved = attn_flops(shp) / (dom_ms * 1e-3) / 1e12
         roof = {"kernel": "gated_attn", "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                 "traffic": traffic_for("k_attn.hip", args.workload)}
     elif dom == "gate_score":
-        achieved = gate_bytes(shp) / (per_stage[dom] * 1e-3) / 1e9
+        achieved = gate_bytes(shp) / (dom_ms * 1e-3) / 1e9
         roof = {"kernel": "gate_mlp+gate_seqnorm", "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                 "traffic": traffic_for("k_gate.hip", args.workload)}
     else:
-        achieved = compact_bytes(shp) / (per_stage[dom] * 1e-3) / 1e9
+        achieved = compact_bytes(shp) / (dom_ms * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS, "traffic": None}
+    roof["launch_us"] = dom_ms * 1e3
+    per_stage[dom] = dom_ms
     attn_tflops = attn_flops(shp) / (per_stage["gated_attention"] * 1e-3) / 1e12
     gate_gbs = gate_bytes(shp) / (per_stage["gate_score"] * 1e-3) / 1e9
+    event_ms = sum(per_stage.values())
 
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev).fill_(1)

@@ -79,7 +79,9 @@ size_t tg_workspace_bytes(int64_t n);
  * [P1 gate][P2 method][P3 how][P5 Fig 1(a)(b)].
  *   r_i  = 1 / sqrt(mean_k resid_ik^2 + eps_row)
  *   a_ij = r_i * sum_k resid_ik w1_jk + b1_j
- *   s_i  = sum_j w2_j GELU(a_ij) + b2              (GELU: exact erf form)
+ *   s_i  = sum_j w2_j GELU(a_ij) + b2
+ *   GELU is the erf form a/2 (1 + erf(a/sqrt 2)); erf is evaluated to an
+ *   absolute error of at most 1.5e-7 (not correctly rounded).
  *   score_norm_i = s_i / sqrt(mean_i s_i^2 + eps_seq)
  * resid      [n, d] bf16: post-attention residual of layer L (row stride d).
  * w1         [hd, d] bf16: first scorer layer, with the elementwise weight of

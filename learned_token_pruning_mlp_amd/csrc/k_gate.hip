@@ -51,8 +51,24 @@ struct Cfg {
     static_assert(MB >= 1 && NB >= 1, "tile shape");
 };
 
+// GELU(a) = a * Phi(a) = a/2 * (1 + erf(a / sqrt 2)).  erf by the rational
+// approximation of Abramowitz & Stegun, Handbook of Mathematical Functions,
+// formula 7.1.26 (|error| <= 1.5e-7 for x >= 0; odd extension):
+//   erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
+//   t = 1 / (1 + p x).
+// Over the 256 hidden units of a score this moves the normalised score by
+// about 1e-5 at most.
 __device__ __forceinline__ float gelu_erf(float a) {
-    return 0.5f * a * (1.0f + erff(a * 0.70710678118654752440f));
+    constexpr float p = 0.3275911f;
+    constexpr float a1 = 0.254829592f, a2 = -0.284496736f, a3 = 1.421413741f, a4 = -1.453152027f,
+                    a5 = 1.061405429f;
+    const float x = fabsf(a) * 0.70710678118654752440f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(p, x, 1.0f));
+    const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, a5, a4), a3), a2), a1);
+    const float e = __builtin_amdgcn_exp2f(-x * x * 1.44269504088896340736f);
+    const float erf_abs = fmaf(-poly, e, 1.0f);
+    const float erf_v = a < 0.0f ? -erf_abs : erf_abs;
+    return 0.5f * a * (1.0f + erf_v);
 }
 
 // Permutation of the eight 16-byte pieces of a 128-byte LDS row (XOR mask
@@ -67,30 +83,11 @@ __device__ __forceinline__ int swz8(int r) {
 
 #define TG_LDS __attribute__((address_space(3)))
 
-// N 16-byte LDS reads issued together, waited for before the block ends.
+// N 16-byte LDS reads issued together and waited for before the block ends
+// (the registers an inline-assembly load writes must be complete when the
+// block ends).
 template <int N>
 __device__ __forceinline__ void lds_read_wait(u32x4 (&v)[N], const uint32_t (&a)[N]);
-template <>
-__device__ __forceinline__ void lds_read_wait<2>(u32x4 (&v)[2], const uint32_t (&a)[2]) {
-    asm volatile(
-        "ds_read_b128 %0, %2\n\t"
-        "ds_read_b128 %1, %3\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(v[0]), "=&v"(v[1])
-        : "v"(a[0]), "v"(a[1])
-        : "memory");
-}
-template <>
-__device__ __forceinline__ void lds_read_wait<3>(u32x4 (&v)[3], const uint32_t (&a)[3]) {
-    asm volatile(
-        "ds_read_b128 %0, %3\n\t"
-        "ds_read_b128 %1, %4\n\t"
-        "ds_read_b128 %2, %5\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2])
-        : "memory");
-}
 template <>
 __device__ __forceinline__ void lds_read_wait<4>(u32x4 (&v)[4], const uint32_t (&a)[4]) {
     asm volatile(
@@ -101,6 +98,37 @@ __device__ __forceinline__ void lds_read_wait<4>(u32x4 (&v)[4], const uint32_t (
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
         : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+        : "memory");
+}
+template <>
+__device__ __forceinline__ void lds_read_wait<6>(u32x4 (&v)[6], const uint32_t (&a)[6]) {
+    asm volatile(
+        "ds_read_b128 %0, %6\n\t"
+        "ds_read_b128 %1, %7\n\t"
+        "ds_read_b128 %2, %8\n\t"
+        "ds_read_b128 %3, %9\n\t"
+        "ds_read_b128 %4, %10\n\t"
+        "ds_read_b128 %5, %11\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5])
+        : "memory");
+}
+template <>
+__device__ __forceinline__ void lds_read_wait<8>(u32x4 (&v)[8], const uint32_t (&a)[8]) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %9\n\t"
+        "ds_read_b128 %2, %10\n\t"
+        "ds_read_b128 %3, %11\n\t"
+        "ds_read_b128 %4, %12\n\t"
+        "ds_read_b128 %5, %13\n\t"
+        "ds_read_b128 %6, %14\n\t"
+        "ds_read_b128 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]),
+          "=&v"(v[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
         : "memory");
 }
 
@@ -147,23 +175,27 @@ __global__ __launch_bounds__(kThreads) void gate_mlp(const uint16_t* __restrict_
     // fills one 1 KB block = 8 rows of 128 bytes; lane l writes slot l%8 of
     // row l/8 with the piece (l%8) ^ swz8(row).  Residual rows past n repeat
     // row n-1 (their scores are never written).
-    auto issue = [&](int c, uint8_t* stg) {
+    // Instructions [i0, i1) of the VM_PER_TILE direct loads of a tile: the
+    // residual blocks first, then the W1 blocks.
+    auto issue_part = [&](int c, uint8_t* stg, int i0, int i1) {
         const int slot = lane & 7;
 #pragma unroll
-        for (int r = 0; r < H_LOADS; ++r) {
-            const int blk = r * 4 + wave, row = blk * 8 + (lane >> 3);
-            const int64_t gr = min(row0 + row, n - 1);
-            const uint16_t* src = resid + gr * d + c * kKC + 8 * (slot ^ swz8(row));
-            __builtin_amdgcn_global_load_lds(src, (TG_LDS void*)((TG_LDS uint8_t*)stg + blk * 1024), 16, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < W_LOADS; ++r) {
-            const int blk = r * 4 + wave, row = blk * 8 + (lane >> 3);
-            const uint16_t* src = w1 + (int64_t)row * d + c * kKC + 8 * (slot ^ swz8(row));
-            __builtin_amdgcn_global_load_lds(src, (TG_LDS void*)((TG_LDS uint8_t*)stg + H_BYTES + blk * 1024), 16,
-                                             0, 0);
+        for (int r = 0; r < VM_PER_TILE; ++r) {
+            if (r < i0 || r >= i1) continue;
+            if (r < H_LOADS) {
+                const int blk = r * 4 + wave, row = blk * 8 + (lane >> 3);
+                const int64_t gr = min(row0 + row, n - 1);
+                const uint16_t* src = resid + gr * d + c * kKC + 8 * (slot ^ swz8(row));
+                __builtin_amdgcn_global_load_lds(src, (TG_LDS void*)((TG_LDS uint8_t*)stg + blk * 1024), 16, 0, 0);
+            } else {
+                const int blk = (r - H_LOADS) * 4 + wave, row = blk * 8 + (lane >> 3);
+                const uint16_t* src = w1 + (int64_t)row * d + c * kKC + 8 * (slot ^ swz8(row));
+                __builtin_amdgcn_global_load_lds(src, (TG_LDS void*)((TG_LDS uint8_t*)stg + H_BYTES + blk * 1024),
+                                                 16, 0, 0);
+            }
         }
     };
+    auto issue = [&](int c, uint8_t* stg) { issue_part(c, stg, 0, VM_PER_TILE); };
 
     f32x16 acc[C::MB][C::NB];
 #pragma unroll
@@ -205,29 +237,46 @@ __global__ __launch_bounds__(kThreads) void gate_mlp(const uint16_t* __restrict_
             TG_WAIT_VMCNT(0);
         }
         __builtin_amdgcn_s_barrier();
-        if (c + 2 < nchunks) issue(c + 2, ahead);
+        const bool more = c + 2 < nchunks;
         const uint32_t base = (uint32_t)(uintptr_t)(const TG_LDS uint8_t*)cur;
+        constexpr int NOP = C::NB + C::MB;  // operand reads per k-step
+        constexpr int NPAIR = kKC / 32;     // k-step pairs per tile
 #pragma unroll
-        for (int s = 0; s < kKC / 16; ++s) {
-            u32x4 op[C::NB + C::MB];
-            uint32_t addr[C::NB + C::MB];
+        for (int s2 = 0; s2 < kKC / 16; s2 += 2) {
+            // the loads two tiles ahead go out in slices between the pairs, so
+            // the load path is not swamped before any multiply starts
+            if (more) {
+                constexpr int per = (VM_PER_TILE + NPAIR - 1) / NPAIR;
+                issue_part(c + 2, ahead, (s2 / 2) * per, (s2 / 2 + 1) * per);
+            }
+            // both k-steps' operands in one block: the reads of this pair are in
+            // flight while the matrix cores still work on the previous pair
+            u32x4 op[2 * NOP];
+            uint32_t addr[2 * NOP];
 #pragma unroll
-            for (int i = 0; i < C::NB + C::MB; ++i) addr[i] = base + roff[i] + 16 * ((2 * s + g) ^ rswz[i]);
-            lds_read_wait<C::NB + C::MB>(op, addr);
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int mb = 0; mb < C::MB; ++mb)
+                for (int i = 0; i < NOP; ++i)
+                    addr[u * NOP + i] = base + roff[i] + 16 * ((2 * (s2 + u) + g) ^ rswz[i]);
+            lds_read_wait<2 * NOP>(op, addr);
 #pragma unroll
-                for (int nb = 0; nb < C::NB; ++nb)
-                    acc[mb][nb] = tgd::mfma32(op[C::NB + mb], op[nb], acc[mb][nb]);
-            // row sums of squares: the waves sharing a token block split the k-steps
-            if (s % C::WAVES_H == wh) {
+            for (int u = 0; u < 2; ++u) {
+                const int s = s2 + u;
 #pragma unroll
-                for (int nb = 0; nb < C::NB; ++nb) {
+                for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float lo = tgd::bf16lo(op[nb][q]), hi = tgd::bf16hi(op[nb][q]);
-                        ssq[nb] = fmaf(lo, lo, ssq[nb]);
-                        ssq[nb] = fmaf(hi, hi, ssq[nb]);
+                    for (int nb = 0; nb < C::NB; ++nb)
+                        acc[mb][nb] = tgd::mfma32(op[u * NOP + C::NB + mb], op[u * NOP + nb], acc[mb][nb]);
+                // row sums of squares: the waves sharing a token block split the k-steps
+                if (s % C::WAVES_H == wh) {
+#pragma unroll
+                    for (int nb = 0; nb < C::NB; ++nb) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const float lo = tgd::bf16lo(op[u * NOP + nb][q]), hi = tgd::bf16hi(op[u * NOP + nb][q]);
+                            ssq[nb] = fmaf(lo, lo, ssq[nb]);
+                            ssq[nb] = fmaf(hi, hi, ssq[nb]);
+                        }
                     }
                 }
             }
