@@ -39,6 +39,7 @@ def parse():
     p.add_argument("--workload", default="n16k",
                    choices=["n16k", "n32k-k1024", "n32k-k4096", "n32k-k8192", "n128k", "full16k", "tiny"])
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    p.add_argument("--no-attn-sweep", action="store_true", help="skip the attention-only K sweep")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="also run one plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -221,10 +222,15 @@ def main():
     event_ms = sum(per_stage.values())
 
     if args.copy_probe_mib:
-        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        # counter calibration: one elementwise kernel that reads and writes exactly
+        # copy_probe_mib MiB (float32 multiply into a separate buffer)
+        src = torch.ones((args.copy_probe_mib << 20) // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        torch.mul(src, 2.0, out=dst)
         torch.cuda.synchronize()
+        del src, dst
+
+    sweep = None if args.no_attn_sweep else attn_sweep(tg, torch, dev, shp)
 
     result = {
         "metric": METRIC,
@@ -248,12 +254,50 @@ def main():
         "attn_tflops": attn_tflops,
         "gate_hbm_gbs": gate_gbs,
         "roofline": roof,
+        "attn_sweep": sweep,
         "cpu_baseline": None,
     }
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(shp, seed, inp, a)
     print(json.dumps(result), flush=True)
+
+
+def attn_sweep(tg, torch, dev, shp, ks=(4096, 8192, 16384), reps=10):
+    """Gated attention alone at longer kept lists (same heads and head_dim):
+    TFLOP/s of algorithmic causal work and the fraction of the bf16 peak.
+    Timing-only inputs: N(0,1) q/k/v and scores, positions 4t."""
+    res = {}
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    for k in ks:
+        q = torch.randn((k, shp.hq, shp.head_dim), generator=g, device=dev).to(torch.bfloat16)
+        kk = torch.randn((k, shp.hkv, shp.head_dim), generator=g, device=dev).to(torch.bfloat16)
+        vv = torch.randn((k, shp.hkv, shp.head_dim), generator=g, device=dev).to(torch.bfloat16)
+        ks_ = torch.randn(k, generator=g, device=dev)
+        gains = torch.rand(shp.hq, generator=g, device=dev) * 1.5 + 0.5
+        pos = torch.arange(k, dtype=torch.int32, device=dev) * 4
+        out = torch.empty_like(q)
+        stream = torch.cuda.current_stream()
+
+        def run():
+            tg.tg_gated_attention(q, kk, vv, ks_, gains, shp.temp_coef, pos, out)
+
+        for _ in range(2):
+            run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        flops = 4.0 * shp.hq * shp.head_dim * k * (k + 1) / 2.0
+        tf = flops / (us * 1e-6) / 1e12
+        res[str(k)] = {"us": round(us, 2), "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del q, kk, vv, out
+    return res
 
 
 def cpu_baseline(shp, seed, inp, a):

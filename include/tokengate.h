@@ -162,7 +162,9 @@ int tg_rope(tg_bf16* x, const int32_t* pos, int64_t rows, int32_t heads, int32_t
  * key_score [n_kept] fp32 (normalised score of each kept token); gains [hq] fp32;
  * pos [n_kept] int32 original positions (>= 0, increasing).
  * out [n_kept, hq, head_dim]: bf16 if out_dtype == 0, fp32 if out_dtype == 1.
- * Supported: head_dim in {64, 128}, hq % hkv == 0.  n_kept == 0 is a no-op.
+ * Supported: head_dim in {64, 128}, hq % hkv == 0, and K and V each under
+ * 2 GiB (n_kept * hkv * head_dim * 2 < 2^31; else TG_EUNSUPPORTED).
+ * n_kept == 0 is a no-op.
  * bf16 matrix-core products with fp32 accumulation; softmax in fp32.
  */
 int tg_gated_attention(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v,

@@ -42,6 +42,8 @@
 //    in one L2.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "tg_device.h"
 #include "tg_internal.h"
 
@@ -55,6 +57,10 @@ using tgd::u32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 
 constexpr int kXcds = 8;
+// Fourth word of a raw buffer resource on gfx9-family parts: 32-bit data
+// format, no swizzle; with a zero stride, offsets at or past num_records read
+// as zero.
+constexpr int kBufferWord3 = 0x00020000;
 constexpr float kLog2e = 1.44269504088896340736f;
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
@@ -82,6 +88,21 @@ struct AttnCfg {
     static constexpr int SLOTS_K = TILE_BYTES / 4096;
     static_assert(SLOTS <= 2 * SLOTS_K, "merge scratch");
 };
+
+// Direct load of `size` bytes per lane from base + voff + soff into LDS at
+// lds + size * lane, through a raw buffer resource covering `bytes` bytes:
+// offsets at or past the end read as zero.
+template <int SIZE>
+__device__ __forceinline__ void buffer_to_lds(const void* base, int bytes, TG_LDS uint8_t* lds, uint32_t voff,
+                                              uint32_t soff) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferWord3);
+    static_assert(SIZE == 16 || SIZE == 4, "direct-load size");
+    if constexpr (SIZE == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (TG_LDS void*)lds, 16, voff, soff, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (TG_LDS void*)lds, 4, voff, soff, 0, 0);
+}
 
 // Permutation of the 16-byte pieces inside a K/V row (XOR mask by row).
 // gfx950 LDS has 64 banks; a 16-byte read serves 16 consecutive lanes per
@@ -139,7 +160,8 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
     const int nA = nst(qbA);
     const int ntot = nA + (qbB != qbA ? nst(qbB) : 0);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in a scalar register
     const int l32 = lane & 31, g = lane >> 5;
     const int hl = wave % HPW, rb = (wave / HPW) % RB, sp = wave / (HPW * RB);
     const int hr = hl + HPW * rb;  // this wave's (head, row block) slot among the merge partners
@@ -148,27 +170,34 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
     const int quad = lane >> 4, jj = lane & 15;
     const int tr_row = jj >> 2, tr_col = 4 * (jj & 3);
 
-    // ---- direct loads of one super-tile (keys j0 .. j0+SKEYS-1).  Rows past
-    // the last key repeat the last key (they are always causally masked).
+    // ---- direct loads of one super-tile (keys j0 .. j0+SKEYS-1), through
+    // buffer resources: each lane's 32-bit offset within a tile is fixed for
+    // the kernel and the tile start is a scalar offset.  Rows past the last
+    // key fall outside the resource and read as zeros (they are always
+    // causally masked).
+    const int row_bytes_g = hkv * D * 2;  // bytes between consecutive keys of K and V
+    const int kv_bytes = nk * row_bytes_g;
+    uint32_t goff[C::LOADS];
+#pragma unroll
+    for (int r = 0; r < C::LOADS; ++r) {
+        constexpr int rows_per_inst = 64 / C::PIECES;
+        const int blk = r * C::WAVES + wave;
+        const int row = blk * rows_per_inst + lane / C::PIECES;
+        const int piece = (lane % C::PIECES) ^ swz<C::PIECES>(row);
+        goff[r] = row * row_bytes_g + kvh * D * 2 + piece * 16;
+    }
     auto issue = [&](int it, uint8_t* __restrict__ sK, uint8_t* __restrict__ sV, float* __restrict__ sS) {
         const int st = it < nA ? it : it - nA;
         const int j0 = st * C::SKEYS;
-        constexpr int rows_per_inst = 64 / C::PIECES;
+        const int tile_off = j0 * row_bytes_g;
 #pragma unroll
         for (int r = 0; r < C::LOADS; ++r) {
             const int blk = r * C::WAVES + wave;
-            const int row = blk * rows_per_inst + lane / C::PIECES;
-            const int piece = (lane % C::PIECES) ^ swz<C::PIECES>(row);
-            const int j = min(j0 + row, nk - 1);
-            const int64_t goff = ((int64_t)j * hkv + kvh) * D + piece * 8;
-            __builtin_amdgcn_global_load_lds(kk + goff, (TG_LDS void*)((TG_LDS uint8_t*)sK + blk * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(v + goff, (TG_LDS void*)((TG_LDS uint8_t*)sV + blk * 1024), 16, 0, 0);
+            buffer_to_lds<16>(kk, kv_bytes, (TG_LDS uint8_t*)sK + blk * 1024, goff[r], tile_off);
+            buffer_to_lds<16>(v, kv_bytes, (TG_LDS uint8_t*)sV + blk * 1024, goff[r], tile_off);
         }
-        if (wave * 64 < C::SKEYS) {  // scores: one per lane, first SKEYS/64 waves
-            const int j = min(j0 + wave * 64 + lane, nk - 1);
-            __builtin_amdgcn_global_load_lds(key_score + j, (TG_LDS void*)((TG_LDS uint8_t*)sS + wave * 256), 4, 0,
-                                             0);
-        }
+        if (wave * 64 < C::SKEYS)  // scores: one per lane, first SKEYS/64 waves
+            buffer_to_lds<4>(key_score, nk * 4, (TG_LDS uint8_t*)sS + wave * 256, (wave * 64 + lane) * 4, j0 * 4);
     };
 
     // ---- per query-block state of this wave (head h, rows q0 .. q0+31)
@@ -200,7 +229,8 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
     // ---- merge the NS split waves of each head and write the block's rows.
     // Every wave rescales its partial sums to the common max first, so the
     // merge is a plain sum; the split-0 wave of each head adds the others
-    // (read through LDS, one head_dim block at a time) and writes the output.
+    // (read through LDS, one head_dim block at a time, 16 consecutive bytes
+    // per lane) and writes the output.
     auto finish_block = [&](uint8_t* scK, uint8_t* scV) {
         const auto slot_ptr = [&](int slot) {
             return reinterpret_cast<float*>(slot < C::SLOTS_K ? scK + slot * 4096 : scV + (slot - C::SLOTS_K) * 4096);
@@ -212,27 +242,27 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
 #pragma unroll
         for (int s = 0; s < NS; ++s) m_tot = fmaxf(m_tot, mbuf[hr][s][l32]);
         const float f = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_tot);
-        const float l_half = l_run + __shfl_xor(l_run, 32, 64);
+        const float l_half = tgd::half_sum(l_run);
         if (g == 0) lbuf[hr][sp][l32] = l_half * f;
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
             o[db] *= f;
             if (NS > 1) {
                 if (sp != 0) {
-                    float* dst = slot_ptr(hr * (NS - 1) + sp - 1) + lane * 16;
+                    float* dst = slot_ptr(hr * (NS - 1) + sp - 1);
 #pragma unroll
                     for (int i4 = 0; i4 < 4; ++i4)
-                        *reinterpret_cast<float4*>(dst + 4 * i4) =
+                        *reinterpret_cast<float4*>(dst + 4 * (i4 * 64 + lane)) =
                             float4{o[db][4 * i4], o[db][4 * i4 + 1], o[db][4 * i4 + 2], o[db][4 * i4 + 3]};
                 }
                 __syncthreads();
                 if (sp == 0) {
 #pragma unroll
                     for (int s = 1; s < NS; ++s) {
-                        const float* src = slot_ptr(hr * (NS - 1) + s - 1) + lane * 16;
+                        const float* src = slot_ptr(hr * (NS - 1) + s - 1);
 #pragma unroll
                         for (int i4 = 0; i4 < 4; ++i4) {
-                            const float4 x = *reinterpret_cast<const float4*>(src + 4 * i4);
+                            const float4 x = *reinterpret_cast<const float4*>(src + 4 * (i4 * 64 + lane));
                             o[db][4 * i4] += x.x;
                             o[db][4 * i4 + 1] += x.y;
                             o[db][4 * i4 + 2] += x.z;
@@ -266,60 +296,92 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
         }
     };
 
+    // ---- LDS byte offsets of this wave's operand reads, fixed for the whole
+    // kernel.  The swizzle depends on the row modulo 16 only, so the offsets
+    // of key block kb and of the second 16-key half of a block are these plus
+    // constants.
+    //  K (A operand of S^T): key row rb0 + l32, piece 2s + g.
+    //  V (A operand of O^T, transposing read): lane a+4e of a 16-lane group
+    //  addresses key row kbase + e and head_dim columns dbase + 4a .. + 3.
+    const int rb0 = C::WKEYS * sp;
+    uint32_t koff[C::QS];
+#pragma unroll
+    for (int s = 0; s < C::QS; ++s) {
+        const int row = rb0 + l32;
+        koff[s] = row * C::ROW_BYTES + 16 * ((2 * s + g) ^ swz<C::PIECES>(row));
+    }
+    uint32_t voff[C::DB][2];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int row = rb0 + 4 * (quad >> 1) + 8 * half + tr_row;
+            const int dcol = db * 32 + 16 * (quad & 1) + tr_col;
+            voff[db][half] = row * C::ROW_BYTES + 16 * ((dcol >> 3) ^ swz<C::PIECES>(row)) + 8 * ((dcol >> 2) & 1);
+        }
+    }
+    const uint32_t soff = 4 * (rb0 + 4 * g);
+
+    // Running maxima are only raised when a row's block max exceeds them by
+    // more than 2^kTau in the exp2 domain; in between, probabilities up to
+    // 2^kTau are accumulated (exact in fp32, bf16 keeps its relative
+    // precision).  This skips nearly every rescale of the accumulators.
+    constexpr float kTau = 8.0f;
+
     // ---- one 32-key block of this wave's slice: S^T, online softmax, P.V.
-    auto key_block = [&](int k0, int rbase, const uint8_t* __restrict__ tK, const uint8_t* __restrict__ tV,
-                         const float* __restrict__ tS) {
+    // POS: every row of the wave has a_t > 0 (the usual case).  Logits in the
+    // exp2 domain are z = a_t * S; the block max is then a_t * max(S)
+    // (rounding is monotonic), so p = 2^(a_t * S - m) is one FMA and one
+    // exp2.  Otherwise (a temperature <= 0, possible when few early tokens
+    // were kept) z is formed explicitly first.
+    auto key_block = [&](auto pos_tag, int k0, int kb, const uint8_t* __restrict__ tK,
+                         const uint8_t* __restrict__ tV, const float* __restrict__ tS) __attribute__((always_inline)) {
+        constexpr bool POS = decltype(pos_tag)::value;
+        const uint8_t* bK = tK + kb * 32 * C::ROW_BYTES;
+        const uint8_t* bV = tV + kb * 32 * C::ROW_BYTES;
+        const float* bS = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(tS) + soff) + 32 * kb;
         // S^T for 32 keys x 32 queries, started at the key bias.
         f32x16 sacc;
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
-            const float4 sv = *reinterpret_cast<const float4*>(&tS[rbase + 8 * i4 + 4 * g]);
+            const float4 sv = *reinterpret_cast<const float4*>(bS + 8 * i4);
             sacc[4 * i4 + 0] = sg * sv.x;
             sacc[4 * i4 + 1] = sg * sv.y;
             sacc[4 * i4 + 2] = sg * sv.z;
             sacc[4 * i4 + 3] = sg * sv.w;
         }
+        u32x4 ka[C::QS];
 #pragma unroll
-        for (int s = 0; s < C::QS; ++s) {
-            const int row = rbase + l32;
-            const u32x4 a = *reinterpret_cast<const u32x4*>(tK + row * C::ROW_BYTES +
-                                                             16 * ((2 * s + g) ^ swz<C::PIECES>(row)));
-            sacc = tgd::mfma32(a, qreg[s], sacc);
+        for (int s = 0; s < C::QS; ++s) ka[s] = *reinterpret_cast<const u32x4*>(bK + koff[s]);
+#pragma unroll
+        for (int s = 0; s < C::QS; ++s) sacc = tgd::mfma32(ka[s], qreg[s], sacc);
+        if (k0 + 31 > q0) {  // diagonal block (wave-uniform): hide keys after the query
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (k0 + 8 * (i >> 2) + 4 * g + (i & 3) > t) sacc[i] = -INFINITY;
         }
-
-        // Logits in the exp2 domain are z = a_t * S.  When every row of the
-        // wave has a_t > 0 the block max is a_t * max(S) (rounding is
-        // monotonic), so p = 2^(a_t * S - m) is one FMA and one exp2.
-        // Otherwise (a temperature <= 0, possible when few early tokens were
-        // kept) z is formed explicitly first.
-        const bool diag = k0 + 31 > q0;
-        float mt = -INFINITY, a_eff;
-        if (__builtin_expect(all_pos, 1)) {
-            a_eff = a_t;
+        float mt = -INFINITY;
+        if constexpr (POS) {
             float smax = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                if (diag && k0 + 8 * (i >> 2) + 4 * g + (i & 3) > t) sacc[i] = -INFINITY;
-                smax = fmaxf(smax, sacc[i]);
-            }
+            for (int i = 0; i < 16; ++i) smax = fmaxf(smax, sacc[i]);
             mt = a_t * smax;
         } else {
-            a_eff = 1.0f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                float z = a_t * sacc[i];
-                if (diag && k0 + 8 * (i >> 2) + 4 * g + (i & 3) > t) z = -INFINITY;
-                sacc[i] = z;
-                mt = fmaxf(mt, z);
+                sacc[i] = sacc[i] == -INFINITY ? -INFINITY : a_t * sacc[i];  // masked stay masked
+                mt = fmaxf(mt, sacc[i]);
             }
         }
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        const float m_new = fmaxf(m_run, mt);
-        // rows with no visible key yet in this split keep m = -inf
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        const bool moved = m_new != m_run;
-        m_run = m_new;
+        mt = tgd::half_max(mt);
+        // Raise the running max only past the slack.  A row with no visible key
+        // yet keeps m = -inf (and exponent offset 0: all its p are 0).
+        const bool bump = mt > m_run + kTau;
+        const bool had = m_run != -INFINITY;
+        const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
+        if (bump) m_run = mt;
+        const float m_use = m_run == -INFINITY ? 0.0f : m_run;
+        const float a_eff = POS ? a_t : 1.0f;
         float ls = 0.0f;
         u32x4 pb[2];  // P^T as bf16, by k-step
 #pragma unroll
@@ -330,29 +392,22 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
             pb[i >> 3][(i & 7) >> 1] = tgd::cvt_pk_bf16(p0, p1);
         }
         l_run = l_run * alpha + ls;
-        if (__builtin_amdgcn_ballot_w64(moved)) {  // skip the rescale when no row max moved
+        if (__builtin_amdgcn_ballot_w64(bump && had)) {
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
         }
 
-        // O^T += V^T . P^T.  The transposing read gives lane jj of each
-        // 16-lane group four consecutive keys of head_dim column dbase+jj when
-        // loading lane a+4e of the group addresses key row kbase+e, columns
-        // dbase+4a .. dbase+4a+3.
+        // O^T += V^T . P^T; the transposing read hands lane jj of each 16-lane
+        // group four consecutive keys of one head_dim column.
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const int kbase = rbase + 16 * s + 4 * (quad >> 1);
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) {
-                const int dcol = db * 32 + 16 * (quad & 1) + tr_col;
                 u32x4 a;
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
-                    const int row = kbase + 8 * half + tr_row;
-                    const int off = row * C::ROW_BYTES + 16 * ((dcol >> 3) ^ swz<C::PIECES>(row)) +
-                                    8 * ((dcol >> 2) & 1);
-                    const bf16x4_t x =
-                        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((TG_LDS bf16x4_t*)((TG_LDS uint8_t*)tV + off));
+                    const bf16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (TG_LDS bf16x4_t*)((TG_LDS uint8_t*)bV + voff[db][half] + 16 * s * C::ROW_BYTES));
                     const u32x2 w = __builtin_bit_cast(u32x2, x);
                     a[2 * half] = w[0];
                     a[2 * half + 1] = w[1];
@@ -368,9 +423,12 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
                        const float* __restrict__ tS) {
 #pragma unroll 1
         for (int kb = 0; kb < KB; ++kb) {  // one block at a time keeps the register footprint of one
-            const int k0 = j0 + C::WKEYS * sp + 32 * kb;
+            const int k0 = j0 + rb0 + 32 * kb;
             if (k0 > wave_last) break;  // the rest of the slice is in this wave's future
-            key_block(k0, C::WKEYS * sp + 32 * kb, tK, tV, tS);
+            if (__builtin_expect(all_pos, 1))
+                key_block(std::true_type{}, k0, kb, tK, tV, tS);
+            else
+                key_block(std::false_type{}, k0, kb, tK, tV, tS);
         }
     };
 

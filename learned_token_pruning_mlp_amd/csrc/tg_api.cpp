@@ -114,6 +114,8 @@ int tg_gated_attention(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, con
     if (out_dtype != 0 && out_dtype != 1) return TG_EINVAL;
     if (!(temp_coef == temp_coef) || temp_coef > 3.4e38f || temp_coef < -3.4e38f) return TG_EINVAL;
     if (head_dim != 64 && head_dim != 128) return TG_EUNSUPPORTED;
+    // K and V are read through 32-bit buffer offsets: each must stay under 2 GiB
+    if (n_kept * (int64_t)hkv * head_dim * 2 >= (int64_t(1) << 31)) return TG_EUNSUPPORTED;
     if (n_kept == 0) return TG_OK;
     if (!q || !k || !v || !key_score || !gains || !pos || !out) return TG_EINVAL;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(key_score, 4) ||

@@ -152,6 +152,8 @@ def test_attention_checks(lib):
     assert _att(lib, hq=6, hkv=4) == E.TG_EINVAL
     assert _att(lib, hkv=0) == E.TG_EINVAL
     assert _att(lib, D=96) == E.TG_EUNSUPPORTED
+    assert _att(lib, nk=1 << 20, hq=16, hkv=8, D=128) == E.TG_EUNSUPPORTED  # K, V of 2 GiB
+    assert _att(lib, nk=(1 << 20) - 1, hq=16, hkv=8, D=128, q=None) == E.TG_EINVAL  # just under: size accepted
     assert _att(lib, od=2) == E.TG_EINVAL
     assert _att(lib, c=float("nan")) == E.TG_EINVAL
     assert _att(lib, q=None) == E.TG_EINVAL

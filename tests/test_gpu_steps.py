@@ -169,7 +169,7 @@ def test_compact(n, k, d):
 
 # ------------------------------------------------------------- RoPE
 
-@pytest.mark.parametrize("rows,heads,D", [(300, 4, 64), (2048, 24, 128), (5, 1, 2)])
+@pytest.mark.parametrize("rows,heads,D", [(300, 4, 64), (2048, 24, 128), (5, 1, 2), (3, 2, 48), (131, 8, 256)])
 def test_rope(rows, heads, D):
     gu.say(f"rope rows={rows} heads={heads} D={D}")
     g = np.random.default_rng(rows)
@@ -184,6 +184,26 @@ def test_rope(rows, heads, D):
     diff = np.abs(got.astype(np.int32) - want.astype(np.int32))
     assert diff.max() <= 1
     assert np.mean(diff != 0) < 1e-3
+
+
+def test_rope_unaligned_buffer():
+    """A tensor that starts 2 bytes past a 16-byte boundary takes the
+    per-element path; results are the same as for an aligned copy."""
+    gu.say("rope unaligned rows=77 heads=3 D=128")
+    rows, heads, D = 77, 3, 128
+    g = np.random.default_rng(5)
+    x = synth.normal_bf16(9, 1, (rows, heads, D))
+    pos = np.sort(g.choice(50000, size=rows, replace=False)).astype(np.int32)
+    flat = torch.empty(rows * heads * D + 8, dtype=torch.bfloat16, device=gu.dev())
+    t = flat[1:1 + rows * heads * D].view(rows, heads, D)
+    t.copy_(gu.bf16(x))
+    assert t.data_ptr() % 16 == 2
+    tg.tg_rope(t, gu.i32(pos), 1.0e6)
+    a = gu.bf16(x)
+    tg.tg_rope(a, gu.i32(pos), 1.0e6)
+    assert np.array_equal(gu.bits(t), gu.bits(a))
+    diff = np.abs(gu.bits(t).astype(np.int32) - oracle.rope(x, pos, 1.0e6).astype(np.int32))
+    assert diff.max() <= 1
 
 
 # ------------------------------------------------------------- attention
