@@ -22,7 +22,18 @@
 //    p = 2^(a_t * S - m) with a_t = lambda_t * log2(e) / sqrt(D).
 //  * The S^T accumulator layout is the B-operand layout of O^T = V^T . P^T
 //    (keys along k), so P goes from registers to the matrix core with one
-//    hardware bf16 conversion per pair.
+//    hardware bf16 conversion per pair; the row sums are taken from the same
+//    bf16 pairs (v_dot2_f32_bf16, two keys per instruction), so numerator
+//    and denominator use one P.
+//  * A row whose temperature lambda_t is negative (possible when few early
+//    tokens were kept) is computed as |lambda_t| * (-S): its query and its
+//    key-bias scale change sign, which is exact, so every row has a positive
+//    exp2 scale and one code path serves all rows.
+//  * Per 32-key block a wave issues all its K-operand and score reads, the
+//    eight S^T products, then the transposing V reads before the softmax, so
+//    LDS latency overlaps the matrix cores; it raises its issue priority
+//    while it feeds the matrix cores, which staggers the two waves of a SIMD
+//    into alternating matrix and vector phases.
 //  * Work split: a workgroup owns one GQA kv head, HPW of its q heads and a
 //    pair of 32-row query blocks (b, last - b), so every workgroup carries the
 //    same causal work.  The keys of a query block are streamed as super-tiles
@@ -122,6 +133,14 @@ __device__ __forceinline__ int swz(int r) {
     return ((x & 1) << 2) | (x >> 1);
 }
 
+// acc + lo + hi of a packed bf16 pair, in fp32.
+__device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    constexpr uint32_t kOnes = 0x3f803f80u;  // (1.0, 1.0) in bf16
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pair), __builtin_bit_cast(bf16x2_t, kOnes),
+                                           acc, false);
+}
+
 template <int D, int HPW, int RB, int NS, int KB, bool OUT_F32>
 __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ kk,
@@ -203,8 +222,7 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
     // ---- per query-block state of this wave (head h, rows q0 .. q0+31)
     u32x4 qreg[C::QS];
     f32x16 o[C::DB];
-    float m_run = -INFINITY, l_run = 0.0f, a_t = 0.0f;
-    bool all_pos = true;
+    float m_run = -INFINITY, l_run = 0.0f, a_t = 0.0f, sgl = 0.0f;
     int q0 = 0, t = 0, wave_last = 0;
 
     auto begin_block = [&](int qb) {
@@ -218,8 +236,16 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
             qreg[s] = ok ? *reinterpret_cast<const u32x4*>(qp + s * 16 + g * 8) : u32x4{0, 0, 0, 0};
         float lam = 1.0f;
         if (ok) lam = 1.0f + temp_coef * logf((float)(t + 1) / ((float)pos[t] + 1.0f));
-        a_t = lam * kLog2e * (1.0f / sqrtf((float)D));
-        all_pos = __builtin_amdgcn_ballot_w64(!(a_t > 0.0f)) == 0;  // wave-uniform
+        // A row with lambda < 0 takes z = |lambda| * (-S): its query and its
+        // key-bias scale change sign (exact), so every row has a positive exp2
+        // scale; lambda = 0 (all logits 0) takes a tiny positive one.
+        const bool neg = lam < 0.0f;
+        a_t = fmaxf(fabsf(lam) * kLog2e * (1.0f / sqrtf((float)D)), 1e-30f);
+        sgl = neg ? -sg : sg;
+        if (neg) {
+#pragma unroll
+            for (int s = 0; s < C::QS; ++s) qreg[s] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+        }
         m_run = -INFINITY;
         l_run = 0.0f;
 #pragma unroll
@@ -329,51 +355,61 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
     constexpr float kTau = 8.0f;
 
     // ---- one 32-key block of this wave's slice: S^T, online softmax, P.V.
-    // POS: every row of the wave has a_t > 0 (the usual case).  Logits in the
-    // exp2 domain are z = a_t * S; the block max is then a_t * max(S)
-    // (rounding is monotonic), so p = 2^(a_t * S - m) is one FMA and one
-    // exp2.  Otherwise (a temperature <= 0, possible when few early tokens
-    // were kept) z is formed explicitly first.
-    auto key_block = [&](auto pos_tag, int k0, int kb, const uint8_t* __restrict__ tK,
-                         const uint8_t* __restrict__ tV, const float* __restrict__ tS) __attribute__((always_inline)) {
-        constexpr bool POS = decltype(pos_tag)::value;
+    // Every row has a_t > 0, so the logits in the exp2 domain are a_t * S,
+    // the block max is a_t * max(S) (rounding is monotonic) and
+    // p = 2^(a_t * S - m) is one FMA and one exp2.
+    auto key_block = [&](int k0, int kb, const uint8_t* __restrict__ tK, const uint8_t* __restrict__ tV,
+                         const float* __restrict__ tS) __attribute__((always_inline)) {
         const uint8_t* bK = tK + kb * 32 * C::ROW_BYTES;
         const uint8_t* bV = tV + kb * 32 * C::ROW_BYTES;
         const float* bS = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(tS) + soff) + 32 * kb;
+        // all K-operand and score reads of the block go out together
+        u32x4 ka[C::QS];
+#pragma unroll
+        for (int s = 0; s < C::QS; ++s) ka[s] = *reinterpret_cast<const u32x4*>(bK + koff[s]);
+        float4 sv[4];
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) sv[i4] = *reinterpret_cast<const float4*>(bS + 8 * i4);
         // S^T for 32 keys x 32 queries, started at the key bias.
         f32x16 sacc;
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
-            const float4 sv = *reinterpret_cast<const float4*>(bS + 8 * i4);
-            sacc[4 * i4 + 0] = sg * sv.x;
-            sacc[4 * i4 + 1] = sg * sv.y;
-            sacc[4 * i4 + 2] = sg * sv.z;
-            sacc[4 * i4 + 3] = sg * sv.w;
+            sacc[4 * i4 + 0] = sgl * sv[i4].x;
+            sacc[4 * i4 + 1] = sgl * sv[i4].y;
+            sacc[4 * i4 + 2] = sgl * sv[i4].z;
+            sacc[4 * i4 + 3] = sgl * sv[i4].w;
         }
-        u32x4 ka[C::QS];
-#pragma unroll
-        for (int s = 0; s < C::QS; ++s) ka[s] = *reinterpret_cast<const u32x4*>(bK + koff[s]);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int s = 0; s < C::QS; ++s) sacc = tgd::mfma32(ka[s], qreg[s], sacc);
+        __builtin_amdgcn_s_setprio(0);
+        // V operands: the transposing read hands lane jj of each 16-lane group
+        // four consecutive keys of one head_dim column; issued before the
+        // softmax so they land while it runs.
+        u32x4 va[2][C::DB];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const bf16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (TG_LDS bf16x4_t*)((TG_LDS uint8_t*)bV + voff[db][half] + 16 * s * C::ROW_BYTES));
+                    const u32x2 w = __builtin_bit_cast(u32x2, x);
+                    va[s][db][2 * half] = w[0];
+                    va[s][db][2 * half + 1] = w[1];
+                }
+            }
+        }
         if (k0 + 31 > q0) {  // diagonal block (wave-uniform): hide keys after the query
 #pragma unroll
             for (int i = 0; i < 16; ++i)
                 if (k0 + 8 * (i >> 2) + 4 * g + (i & 3) > t) sacc[i] = -INFINITY;
         }
-        float mt = -INFINITY;
-        if constexpr (POS) {
-            float smax = -INFINITY;
+        float smax = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) smax = fmaxf(smax, sacc[i]);
-            mt = a_t * smax;
-        } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                sacc[i] = sacc[i] == -INFINITY ? -INFINITY : a_t * sacc[i];  // masked stay masked
-                mt = fmaxf(mt, sacc[i]);
-            }
-        }
-        mt = tgd::half_max(mt);
+        for (int i = 0; i < 16; ++i) smax = fmaxf(smax, sacc[i]);
+        const float mt = tgd::half_max(a_t * smax);
         // Raise the running max only past the slack.  A row with no visible key
         // yet keeps m = -inf (and exponent offset 0: all its p are 0).
         const bool bump = mt > m_run + kTau;
@@ -381,40 +417,28 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
         const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
         if (bump) m_run = mt;
         const float m_use = m_run == -INFINITY ? 0.0f : m_run;
-        const float a_eff = POS ? a_t : 1.0f;
         float ls = 0.0f;
         u32x4 pb[2];  // P^T as bf16, by k-step
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[i], a_eff, -m_use));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[i + 1], a_eff, -m_use));
-            ls += p0 + p1;
-            pb[i >> 3][(i & 7) >> 1] = tgd::cvt_pk_bf16(p0, p1);
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[i], a_t, -m_use));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[i + 1], a_t, -m_use));
+            const uint32_t pk = tgd::cvt_pk_bf16(p0, p1);
+            pb[i >> 3][(i & 7) >> 1] = pk;
+            ls = add_pair(pk, ls);  // the row sum uses the same bf16 P as P.V
         }
         l_run = l_run * alpha + ls;
         if (__builtin_amdgcn_ballot_w64(bump && had)) {
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
         }
-
-        // O^T += V^T . P^T; the transposing read hands lane jj of each 16-lane
-        // group four consecutive keys of one head_dim column.
+        // O^T += V^T . P^T
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
-            for (int db = 0; db < C::DB; ++db) {
-                u32x4 a;
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const bf16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                        (TG_LDS bf16x4_t*)((TG_LDS uint8_t*)bV + voff[db][half] + 16 * s * C::ROW_BYTES));
-                    const u32x2 w = __builtin_bit_cast(u32x2, x);
-                    a[2 * half] = w[0];
-                    a[2 * half + 1] = w[1];
-                }
-                o[db] = tgd::mfma32(a, pb[s], o[db]);
-            }
-        }
+            for (int db = 0; db < C::DB; ++db) o[db] = tgd::mfma32(va[s][db], pb[s], o[db]);
+        __builtin_amdgcn_s_setprio(0);
     };
 
     // ---- this wave's slice of one super-tile: keys j0 + WKEYS*sp .. +WKEYS-1,
@@ -425,10 +449,7 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
         for (int kb = 0; kb < KB; ++kb) {  // one block at a time keeps the register footprint of one
             const int k0 = j0 + rb0 + 32 * kb;
             if (k0 > wave_last) break;  // the rest of the slice is in this wave's future
-            if (__builtin_expect(all_pos, 1))
-                key_block(std::true_type{}, k0, kb, tK, tV, tS);
-            else
-                key_block(std::false_type{}, k0, kb, tK, tV, tS);
+            key_block(k0, kb, tK, tV, tS);
         }
     };
 
