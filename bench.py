@@ -1,7 +1,7 @@
 """Throughput of the TokenGate gated-prefill hot path on one MI355X.
 
 One step = one pass of the whole path over one prompt (batch 1):
-    tg_gate_score -> tg_select_topk -> tg_compact -> tg_rope (q, k) -> tg_gated_attention
+    tg_gate_score -> tg_select_topk -> tg_compact -> tg_rope_qk -> tg_gated_attention
 at the Qwen3-1.7B-shaped gate layer: d_model 2048, scorer 2048->256->1,
 N = 16384 tokens (last 64 forced-keep), K = 2048 kept, 16 q / 8 kv heads,
 head_dim 128, one upper layer of token-gated attention.  Inputs are seeded
@@ -157,8 +157,7 @@ def main():
         mark(ev, 2)
         tg.tg_compact(kept, n, r, resid_k, pos, pos_k, s_norm, score_k)
         mark(ev, 3)
-        tg.tg_rope(q, pos_k, shp.rope_theta)
-        tg.tg_rope(kk, pos_k, shp.rope_theta)
+        tg.tg_rope_qk(q, kk, pos_k, shp.rope_theta)
         mark(ev, 4)
         tg.tg_gated_attention(q, kk, vv, score_k, gains, shp.temp_coef, pos_k, out)
         mark(ev, 5)
@@ -177,7 +176,7 @@ def main():
     for e in evs:
         for j, s in enumerate(stages):
             per_stage[s] += e[j].elapsed_time(e[j + 1])
-    per_stage = {s: v / n_diag for s, v in per_stage.items()}  # ms per step (rope: both calls)
+    per_stage = {s: v / n_diag for s, v in per_stage.items()}  # ms per step
     dom = max(per_stage, key=per_stage.get)
     dom_j = stages.index(dom)
 

@@ -7,7 +7,7 @@
  *   tg_select_topk     -> forced-keep top-K picks the tokens that continue;
  *   tg_compact         -> the kept rows, their original positions, their scores
  *                         and any extra per-token streams (KV rows) are gathered;
- *   tg_rope            -> (auxiliary) rotary embedding at the original positions;
+ *   tg_rope, tg_rope_qk -> (auxiliary) rotary embedding at the original positions;
  *   tg_gated_attention -> causal attention over the kept tokens only, with a
  *                         per-key importance bias and a per-query temperature.
  *
@@ -150,6 +150,17 @@ int tg_compact(const int32_t* kept_idx, int64_t k, int64_t n, const tg_bf16* res
  */
 int tg_rope(tg_bf16* x, const int32_t* pos, int64_t rows, int32_t heads, int32_t head_dim,
             double theta, void* stream);
+
+/*
+ * tg_rope_qk -- tg_rope on the query and key rows of one upper layer in one
+ * launch (auxiliary; [P5 Fig 1(a)(b)]): q [rows, hq, head_dim] and
+ * k [rows, hk, head_dim] bf16, both rotated in place at the same original
+ * positions pos [rows] int32 >= 0.  Same convention, precision and limits as
+ * tg_rope (hq, hk >= 1); the results equal two tg_rope calls bit for bit.
+ * q and k must not overlap.
+ */
+int tg_rope_qk(tg_bf16* q, tg_bf16* k, const int32_t* pos, int64_t rows, int32_t hq, int32_t hk,
+               int32_t head_dim, double theta, void* stream);
 
 /*
  * tg_gated_attention -- token-gated causal attention over the kept list, one

@@ -27,7 +27,7 @@ TG_STATUS_FORCED_OVER_K = 2
 TG_MAX_GATHER = 16
 
 EXPORTS = ("tg_status_string", "tg_abi_version", "tg_workspace_bytes", "tg_gate_score",
-           "tg_select_topk", "tg_compact", "tg_rope", "tg_gated_attention")
+           "tg_select_topk", "tg_compact", "tg_rope", "tg_rope_qk", "tg_gated_attention")
 
 
 class TgGather(ctypes.Structure):
@@ -67,6 +67,8 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
     L.tg_compact.restype = ctypes.c_int
     L.tg_rope.argtypes = [P, P, I64, I32, I32, ctypes.c_double, P]
     L.tg_rope.restype = ctypes.c_int
+    L.tg_rope_qk.argtypes = [P, P, P, I64, I32, I32, I32, ctypes.c_double, P]
+    L.tg_rope_qk.restype = ctypes.c_int
     L.tg_gated_attention.argtypes = [P, P, P, P, P, F, P, I64, I32, I32, I32, P, I32, P]
     L.tg_gated_attention.restype = ctypes.c_int
     _lib = L
@@ -192,6 +194,15 @@ def tg_rope(x: torch.Tensor, pos: torch.Tensor, theta: float, stream=None) -> No
     _need(x, "x", torch.bfloat16)
     _need(pos, "pos", torch.int32, (rows,))
     _check("tg_rope", load().tg_rope(_ptr(x), _ptr(pos), rows, heads, hd, float(theta), _stream(stream)))
+
+
+def tg_rope_qk(q: torch.Tensor, k: torch.Tensor, pos: torch.Tensor, theta: float, stream=None) -> None:
+    rows, hq, hd = q.shape
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, (rows, k.shape[1], hd))
+    _need(pos, "pos", torch.int32, (rows,))
+    _check("tg_rope_qk", load().tg_rope_qk(_ptr(q), _ptr(k), _ptr(pos), rows, hq, k.shape[1], hd, float(theta),
+                                           _stream(stream)))
 
 
 def tg_gated_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_score: torch.Tensor,

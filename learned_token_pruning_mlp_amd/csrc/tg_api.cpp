@@ -107,6 +107,17 @@ int tg_rope(tg_bf16* x, const int32_t* pos, int64_t rows, int32_t heads, int32_t
     return tgi::launch_rope(x, pos, rows, heads, head_dim, theta, stream);
 }
 
+int tg_rope_qk(tg_bf16* q, tg_bf16* k, const int32_t* pos, int64_t rows, int32_t hq, int32_t hk,
+               int32_t head_dim, double theta, void* stream) {
+    if (rows < 0 || rows > kMaxRows || hq < 1 || hk < 1 || head_dim < 2 || head_dim > 256 || head_dim % 2 != 0)
+        return TG_EINVAL;
+    if (!(theta > 0.0) || theta > 1e300) return TG_EINVAL;
+    if (rows == 0) return TG_OK;
+    if (!q || !k || !pos) return TG_EINVAL;
+    if (!aligned(q, 2) || !aligned(k, 2) || !aligned(pos, 4)) return TG_EALIGN;
+    return tgi::launch_rope_qk(q, k, pos, rows, hq, hk, head_dim, theta, stream);
+}
+
 int tg_gated_attention(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, const float* key_score,
                        const float* gains, float temp_coef, const int32_t* pos, int64_t n_kept, int32_t hq,
                        int32_t hkv, int32_t head_dim, void* out, int32_t out_dtype, void* stream) {

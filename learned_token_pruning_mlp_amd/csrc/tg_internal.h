@@ -46,6 +46,9 @@ int launch_compact(const int32_t* kept_idx, int64_t k, int64_t n, const uint16_t
 int launch_rope(uint16_t* x, const int32_t* pos, int64_t rows, int heads, int head_dim,
                 double theta, void* stream);
 
+int launch_rope_qk(uint16_t* q, uint16_t* k, const int32_t* pos, int64_t rows, int hq, int hk, int head_dim,
+                   double theta, void* stream);
+
 int launch_gated_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                            const float* key_score, const float* gains, float temp_coef,
                            const int32_t* pos, int64_t n_kept, int hq, int hkv, int head_dim,

@@ -138,6 +138,21 @@ def test_rope_checks(lib):
     assert lib.tg_rope(A + 1, A, 10, 8, 128, 1e6, None) == E.TG_EALIGN
 
 
+def test_rope_qk_checks(lib):
+    E = binding
+    assert lib.tg_rope_qk(A, A, A, 0, 16, 8, 128, 1e6, None) == E.TG_OK
+    assert lib.tg_rope_qk(A, A, A, 10, 16, 0, 128, 1e6, None) == E.TG_EINVAL
+    assert lib.tg_rope_qk(A, A, A, 10, 0, 8, 128, 1e6, None) == E.TG_EINVAL
+    assert lib.tg_rope_qk(A, A, A, 10, 16, 8, 127, 1e6, None) == E.TG_EINVAL
+    assert lib.tg_rope_qk(A, A, A, 10, 16, 8, 258, 1e6, None) == E.TG_EINVAL
+    assert lib.tg_rope_qk(A, A, A, -1, 16, 8, 128, 1e6, None) == E.TG_EINVAL
+    assert lib.tg_rope_qk(A, A, A, 10, 16, 8, 128, -1.0, None) == E.TG_EINVAL
+    assert lib.tg_rope_qk(A, None, A, 10, 16, 8, 128, 1e6, None) == E.TG_EINVAL
+    assert lib.tg_rope_qk(A, A, None, 10, 16, 8, 128, 1e6, None) == E.TG_EINVAL
+    assert lib.tg_rope_qk(A, A + 1, A, 10, 16, 8, 128, 1e6, None) == E.TG_EALIGN
+    assert lib.tg_rope_qk(A, A, A + 2, 10, 16, 8, 128, 1e6, None) == E.TG_EALIGN
+
+
 def _att(lib, **kw):
     a = dict(q=A, k=A, v=A, ks=A, g=A, c=0.1, pos=A, nk=128, hq=4, hkv=2, D=64, out=A, od=0, stream=None)
     a.update(kw)

@@ -206,6 +206,47 @@ def test_rope_unaligned_buffer():
     assert diff.max() <= 1
 
 
+@pytest.mark.parametrize("rows,hq,hk,D", [(2048, 16, 8, 128), (301, 4, 2, 64), (7, 3, 5, 48), (1, 1, 1, 128),
+                                          (999, 6, 2, 256)])
+def test_rope_qk(rows, hq, hk, D):
+    """q and k rotated in one launch equal the per-tensor results bit for bit."""
+    gu.say(f"rope_qk rows={rows} hq={hq} hk={hk} D={D}")
+    g = np.random.default_rng(rows + hq)
+    xq = synth.normal_bf16(rows + 1, 1, (rows, hq, D))
+    xk = synth.normal_bf16(rows + 2, 1, (rows, hk, D))
+    pos = np.sort(g.choice(131072, size=rows, replace=False)).astype(np.int32)
+    tq, tk = gu.bf16(xq), gu.bf16(xk)
+    tg.tg_rope_qk(tq, tk, gu.i32(pos), 1.0e6)
+    rq, rk = gu.bf16(xq), gu.bf16(xk)
+    tg.tg_rope(rq, gu.i32(pos), 1.0e6)
+    tg.tg_rope(rk, gu.i32(pos), 1.0e6)
+    assert np.array_equal(gu.bits(tq), gu.bits(rq))
+    assert np.array_equal(gu.bits(tk), gu.bits(rk))
+    for got, x in ((gu.bits(tq), xq), (gu.bits(tk), xk)):
+        diff = np.abs(got.astype(np.int32) - oracle.rope(x, pos, 1.0e6).astype(np.int32))
+        assert diff.max() <= 1
+        assert np.mean(diff != 0) < 1e-3
+
+
+def test_rope_qk_unaligned_k():
+    """A key buffer 2 bytes past a 16-byte boundary sends both tensors down
+    the per-element path; results equal the aligned ones."""
+    gu.say("rope_qk unaligned k rows=64 hq=4 hk=2 D=128")
+    rows, hq, hk, D = 64, 4, 2, 128
+    xq = synth.normal_bf16(21, 1, (rows, hq, D))
+    xk = synth.normal_bf16(22, 1, (rows, hk, D))
+    pos = (np.arange(rows) * 37).astype(np.int32)
+    flat = torch.empty(rows * hk * D + 8, dtype=torch.bfloat16, device=gu.dev())
+    tk = flat[1:1 + rows * hk * D].view(rows, hk, D)
+    tk.copy_(gu.bf16(xk))
+    tq = gu.bf16(xq)
+    tg.tg_rope_qk(tq, tk, gu.i32(pos), 1.0e6)
+    aq, ak = gu.bf16(xq), gu.bf16(xk)
+    tg.tg_rope_qk(aq, ak, gu.i32(pos), 1.0e6)
+    assert np.array_equal(gu.bits(tq), gu.bits(aq))
+    assert np.array_equal(gu.bits(tk), gu.bits(ak))
+
+
 # ------------------------------------------------------------- attention
 
 def _run_attn(a, out_dtype=torch.float32):

@@ -69,8 +69,7 @@ def test_headline_path_n16k():
     a = synth.attn_inputs(shp.k, shp.hq, shp.hkv, shp.head_dim, seed=2, pos=ref_kept,
                           key_score=got_norm[ref_kept])
     q, kk = gu.bf16(a.q), gu.bf16(a.k)
-    tg.tg_rope(q, pos_k, shp.rope_theta)
-    tg.tg_rope(kk, pos_k, shp.rope_theta)
+    tg.tg_rope_qk(q, kk, pos_k, shp.rope_theta)
     q_bits, k_bits = gu.bits(q), gu.bits(kk)
     out = torch.empty((shp.k, shp.hq, shp.head_dim), dtype=torch.float32, device=gu.dev())
     tg.tg_gated_attention(q, kk, gu.bf16(a.v), score_k, gu.f32(a.gains), shp.temp_coef, pos_k, out)
