@@ -16,7 +16,10 @@
 // bit-exact and deterministic.
 //
 // One workgroup of 1024 threads does the whole selection (one launch, no
-// workspace traffic).  Up to 32768 tokens the keys stay in LDS (128 KB of the
+// workspace traffic).  The bin searches run in one wave (two wave scans), the
+// candidate gather reserves LDS room with one atomic per wave and step, and
+// the emit pass gives each thread sixteen consecutive tokens, so the
+// workgroup meets at few barriers.  Up to 32768 tokens the keys stay in LDS (128 KB of the
 // CU's 160 KB) after one read of the scores, and the first histogram is built
 // during that read.  The keys of the bucket chosen by the first round (for
 // real score distributions a small fraction) are then gathered into LDS so
@@ -52,6 +55,10 @@ __device__ __forceinline__ T wave_incl_scan(T x, int lane) {
         if (lane >= o) x += y;
     }
     return x;
+}
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
 // Exclusive scan over the whole workgroup; returns the block total in *total.
@@ -106,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void select_topk_block(const float* __res
     constexpr int kBins = 2048;
     constexpr int kCap = 4096;  // gathered candidates
     __shared__ __attribute__((aligned(16))) uint32_t keys[kKeysInLds ? kLdsKeys : 4];
-    __shared__ uint32_t hist[kBins];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
     __shared__ __attribute__((aligned(16))) uint32_t cand[kCap];
     __shared__ uint64_t wsum[kWaves + 1];
     __shared__ uint32_t ctl[4];
@@ -139,19 +146,30 @@ __global__ __launch_bounds__(kThreads) void select_topk_block(const float* __res
     };
     // Find the bin holding the remaining-th largest key of the histogram
     // (bins scanned from the top); sets ctl[0] = bin, ctl[1] = rank inside it.
+    // One wave does it with two wave scans (no workgroup barrier inside):
+    // lane l sums the l-th chunk of nbins/64 bins counted from the top; the
+    // lane whose running count reaches `remaining` owns the bin, which its
+    // chunk's bins then locate with a second scan.
     auto pick_bin = [&](uint32_t remaining, int nbins) {
-        // thread t owns bins top-down: 2t and 2t+1 counted from the highest bin
-        const int b0 = nbins - 1 - 2 * tid, b1 = b0 - 1;
-        const uint32_t c0 = b0 >= 0 ? hist[b0] : 0, c1 = b1 >= 0 ? hist[b1] : 0;
-        uint64_t tot;
-        const uint32_t before = (uint32_t)block_excl_scan(c0 + c1, wsum, &tot);
-        if (b0 >= 0 && before < remaining && remaining <= before + c0) {
-            ctl[0] = b0;
-            ctl[1] = remaining - before;
-        }
-        if (b1 >= 0 && before + c0 < remaining && remaining <= before + c0 + c1) {
-            ctl[0] = b1;
-            ctl[1] = remaining - before - c0;
+        if (threadIdx.x < 64) {
+            const int per = nbins / 64;
+            const int hi = nbins - lane * per;
+            uint32_t sum = 0;
+            for (int i = 0; i < per; i += 4) {
+                const uint4 h4 = *reinterpret_cast<const uint4*>(&hist[hi - per + i]);
+                sum += h4.x + h4.y + h4.z + h4.w;
+            }
+            const uint32_t incl = wave_incl_scan(sum, lane);
+            const int L = __builtin_ctzll(__builtin_amdgcn_ballot_w64(incl >= remaining));
+            const uint32_t before = __shfl(incl - sum, L, 64);
+            const int hiL = nbins - L * per;
+            const uint32_t c = lane < per ? hist[hiL - 1 - lane] : 0u;
+            const uint32_t ci = wave_incl_scan(c, lane) + before;
+            const int b = __builtin_ctzll(__builtin_amdgcn_ballot_w64(lane < per && ci >= remaining));
+            if (lane == b) {
+                ctl[0] = hiL - 1 - b;
+                ctl[1] = remaining - (ci - c);
+            }
         }
         __syncthreads();
     };
@@ -182,8 +200,15 @@ __global__ __launch_bounds__(kThreads) void select_topk_block(const float* __res
             }
         }
     }
-    uint64_t F;
-    block_excl_scan(fc, wsum, &F);  // its barriers also publish the keys and the histogram
+    // forced count: a wave sum, then every thread adds the per-wave sums
+    // after the barrier that also publishes the keys and the histogram
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) fc += __shfl_xor(fc, o, 64);
+    if (lane == 0) wsum[threadIdx.x >> 6] = fc;
+    __syncthreads();
+    uint64_t F = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) F += wsum[w];
     int64_t R = (int64_t)k - (int64_t)F;  // prunable tokens to choose
     if (tid == 0 && dev_status) {
         int32_t st = 0;
@@ -204,11 +229,30 @@ __global__ __launch_bounds__(kThreads) void select_topk_block(const float* __res
         // Gather the bucket's keys when they fit; otherwise filter on the fly.
         const bool gathered = bucket <= (uint32_t)kCap;
         if (gathered) {
+            // each wave reserves room for its matches with one LDS atomic per
+            // four keys a lane, then the lanes write them
             if (tid == 0) ctl[2] = 0;
             __syncthreads();
-            sweep([&](uint32_t, uint32_t key) {
-                if (key != kForcedMark && (key & pmask) == prefix) cand[atomicAdd(&ctl[2], 1u)] = key;
-            });
+            for (uint32_t c0 = 0; c0 < n; c0 += kStep) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t i = c0 + (e * kThreads + tid) * 4;
+                    const uint4 kv = keys4(i);
+                    const uint32_t kq[4] = {kv.x, kv.y, kv.z, kv.w};
+                    uint32_t hit = 0;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (i + q < n && kq[q] != kForcedMark && (kq[q] & pmask) == prefix) hit |= 1u << q;
+                    const uint32_t cnt = __builtin_popcount(hit);
+                    const uint32_t incl = wave_incl_scan(cnt, lane);
+                    uint32_t base = 0;
+                    if (lane == 63 && incl) base = atomicAdd(&ctl[2], incl);
+                    base = __shfl(base, 63, 64) + incl - cnt;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (hit & (1u << q)) cand[base++] = kq[q];
+                }
+            }
             __syncthreads();
         }
         // Rounds 2 and 3: next 11 bits, then the last 10.
@@ -240,36 +284,37 @@ __global__ __launch_bounds__(kThreads) void select_topk_block(const float* __res
     }
 
     // Emit, in index order: slot = (#kind1 before) + min(#ties before, m).
+    // Sixteen consecutive tokens per thread, so up to 16384 tokens take one
+    // pass (one workgroup scan).
     uint64_t carry = 0;
-    for (uint32_t c0 = 0; c0 < n; c0 += kThreads * 8) {
-        const uint32_t base = c0 + (uint32_t)tid * 8;
-        const uint4 k0 = keys4(base), k1 = keys4(base + 4);
-        const uint32_t kk[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-        uint8_t kind[8];  // 0 = dropped, 1 = forced or above T, 2 = equal to T
-        uint32_t ca = 0, cb = 0;
+    for (uint32_t c0 = 0; c0 < n; c0 += kThreads * 16) {
+        const uint32_t base = c0 + (uint32_t)tid * 16;
+        uint32_t ka = 0, kb = 0;  // bit e: token base+e is forced or above T / equal to T
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            uint8_t kd = 0;
-            if (base + e < n) {
-                const uint32_t key = kk[e];
-                if (key == kForcedMark) kd = 1;
-                else if (key > T) kd = 1;
-                else if (key == T) kd = 2;
+        for (int v4 = 0; v4 < 4; ++v4) {
+            const uint4 kv = keys4(base + 4 * v4);
+            const uint32_t kq[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int e = 4 * v4 + q;
+                if (base + e < n) {
+                    const uint32_t key = kq[q];
+                    if (key == kForcedMark || key > T) ka |= 1u << e;
+                    else if (key == T) kb |= 1u << e;
+                }
             }
-            kind[e] = kd;
-            ca += kd == 1;
-            cb += kd == 2;
         }
+        const uint32_t ca = __builtin_popcount(ka), cb = __builtin_popcount(kb);
         uint64_t tot;
         const uint64_t ex = block_excl_scan(((uint64_t)ca << 32) | cb, wsum, &tot) + carry;
         uint32_t A = (uint32_t)(ex >> 32), B = (uint32_t)ex;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            if (kind[e] == 1) {
+        for (int e = 0; e < 16; ++e) {
+            if (ka & (1u << e)) {
                 const uint32_t slot = A + (B < m ? B : m);
                 if (slot < k) kept[slot] = (int32_t)(base + e);
                 ++A;
-            } else if (kind[e] == 2) {
+            } else if (kb & (1u << e)) {
                 if (B < m) {
                     const uint32_t slot = A + B;
                     if (slot < k) kept[slot] = (int32_t)(base + e);

@@ -77,6 +77,60 @@ def test_headline_path_n16k():
     gu.check_attention(gu.host(out), ref, "headline attention")
 
 
+def test_path_graph_replays_match_eager():
+    """The whole headline step captured as one HIP graph (the launch sequence
+    is fixed once K is known): every replay, with eager work and
+    synchronisations between the replays, reproduces the eager outputs bit
+    for bit."""
+    shp = synth.QWEN3_1P7B_N16K
+    gu.say("graph replays of the headline step")
+    n, k = shp.n, shp.k
+    inp = synth.gate_inputs(shp, seed=2)
+    a = synth.attn_inputs(k, shp.hq, shp.hkv, shp.head_dim, seed=2)
+    resid, w1, w2 = gu.bf16(inp.resid), gu.bf16(inp.w1), gu.bf16(inp.w2)
+    forced, pos = gu.u8(inp.forced), gu.i32(inp.pos)
+    q0, k0, v, gains = gu.bf16(a.q), gu.bf16(a.k), gu.bf16(a.v), gu.f32(a.gains)
+    q, kk = q0.clone(), k0.clone()
+    dev = gu.dev()
+    s_norm = torch.empty(n, dtype=torch.float32, device=dev)
+    ws = tg.workspace(n)
+    kept = torch.empty(k, dtype=torch.int32, device=dev)
+    resid_k = torch.empty((k, shp.d), dtype=torch.bfloat16, device=dev)
+    pos_k = torch.empty(k, dtype=torch.int32, device=dev)
+    score_k = torch.empty(k, dtype=torch.float32, device=dev)
+    out = torch.empty((k, shp.hq, shp.head_dim), dtype=torch.float32, device=dev)
+
+    def step():
+        tg.tg_gate_score(resid, w1, None, w2, 0.0, 1e-6, 1e-6, s_norm, None, ws)
+        tg.tg_select_topk(s_norm, forced, shp.n_forced, k, kept, None, ws)
+        tg.tg_compact(kept, n, resid, resid_k, pos, pos_k, s_norm, score_k)
+        tg.tg_rope_qk(q, kk, pos_k, shp.rope_theta)
+        tg.tg_gated_attention(q, kk, v, score_k, gains, shp.temp_coef, pos_k, out)
+
+    def snapshot():
+        ts = (s_norm, kept, resid_k.view(torch.int16), pos_k, score_k, out, q.view(torch.int16), kk.view(torch.int16))
+        return [gu.host(t).view(np.uint8).copy() for t in ts]
+
+    step()
+    want = snapshot()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for r in range(3):
+        q.copy_(q0)  # RoPE works in place: every replay starts from the same q and k
+        kk.copy_(k0)
+        for t in (s_norm, score_k, out):
+            t.fill_(float("nan"))
+        kept.fill_(-1)
+        pos_k.fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = snapshot()
+        for x, y in zip(got, want):
+            assert np.array_equal(x, y), f"replay {r}"
+
+
 @pytest.mark.parametrize("k", synth.N32K_BUDGETS)
 def test_budget_sweep_n32k(k):
     """N=32768, Student-t (df=3) scores fed straight to select; budgets
