@@ -63,6 +63,8 @@ namespace {
 using tgd::f32x16;
 using tgd::u32x2;
 using tgd::u32x4;
+template <int N>
+using IC = std::integral_constant<int, N>;
 
 #define TG_LDS __attribute__((address_space(3)))
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
@@ -93,11 +95,13 @@ struct AttnCfg {
     static constexpr int QS = D / 16;                 // k-steps of the QK^T product
     static_assert(BLOCKS % WAVES == 0 && LOADS >= 1, "tile shape");
     static_assert(SKEYS <= 64 * WAVES, "one score per lane");
-    // merge scratch: one 4 KB slot (16 floats per lane) for every non-leading
-    // split wave, taken from the K buffer of the finished stage, then its V buffer
-    static constexpr int SLOTS = (NS - 1) * HPW * RB;
-    static constexpr int SLOTS_K = TILE_BYTES / 4096;
-    static_assert(SLOTS <= 2 * SLOTS_K, "merge scratch");
+    // merge scratch: one slot per wave holding half of its O^T accumulators
+    // (8 floats per lane per 32 head_dim rows), taken from the K buffer of the
+    // finished stage, then its V buffer; a slot never straddles the two
+    static constexpr int SLOT_BYTES = DB * 2048;
+    static_assert(NS == 1 || (WAVES * SLOT_BYTES <= 2 * TILE_BYTES && TILE_BYTES % SLOT_BYTES == 0),
+                  "merge scratch");
+    static_assert(NS == 1 || NS == 2 || NS == 4, "merge rounds");
 };
 
 // Direct load of `size` bytes per lane from base + voff + soff into LDS at
@@ -139,6 +143,30 @@ __device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
     constexpr uint32_t kOnes = 0x3f803f80u;  // (1.0, 1.0) in bf16
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pair), __builtin_bit_cast(bf16x2_t, kOnes),
                                            acc, false);
+}
+
+// Normalise and write units LO .. LO+N-1 of a lane's O^T accumulators (unit
+// u = 4 values: head_dim rows 32 (u/4) + 8 (u%4) + 4 g .. +3 of query row t).
+// Compile-time unit indices keep the accumulators in fixed registers.
+template <int D, int LO, int N, bool OUT_F32>
+__device__ __forceinline__ void store_units(const f32x16 (&o)[D / 32], float l, int t, int nk, int hq, int h, int g,
+                                            void* __restrict__ out) {
+    if (t >= nk) return;
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int u = LO; u < LO + N; ++u) {
+        const int i = 4 * (u % 4);
+        const int dd = (u / 4) * 32 + 8 * (u % 4) + 4 * g;
+        const int64_t off = ((int64_t)t * hq + h) * D + dd;
+        const float y0 = o[u / 4][i] * inv, y1 = o[u / 4][i + 1] * inv;
+        const float y2 = o[u / 4][i + 2] * inv, y3 = o[u / 4][i + 3] * inv;
+        if (OUT_F32) {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + off) = float4{y0, y1, y2, y3};
+        } else {
+            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + off) =
+                u32x2{tgd::cvt_pk_bf16(y0, y1), tgd::cvt_pk_bf16(y2, y3)};
+        }
+    }
 }
 
 template <int D, int HPW, int RB, int NS, int KB, bool OUT_F32>
@@ -253,72 +281,77 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
     };
 
     // ---- merge the NS split waves of each head and write the block's rows.
-    // Every wave rescales its partial sums to the common max first, so the
-    // merge is a plain sum; the split-0 wave of each head adds the others
-    // (read through LDS, one head_dim block at a time, 16 consecutive bytes
-    // per lane) and writes the output.
-    auto finish_block = [&](uint8_t* scK, uint8_t* scV) {
-        const auto slot_ptr = [&](int slot) {
-            return reinterpret_cast<float*>(slot < C::SLOTS_K ? scK + slot * 4096 : scV + (slot - C::SLOTS_K) * 4096);
-        };
-        __syncthreads();  // every wave is done with this stage's K/V
-        if (g == 0) mbuf[hr][sp][l32] = m_run;
-        __syncthreads();
-        float m_tot = -INFINITY;
+    // Recursive halving over the splits: in each round a wave and its partner
+    // (split indices differing in one bit) swap halves of the head_dim units
+    // they still hold; each keeps one half and adds the partner's copy of it,
+    // both rescaled to the pair's common max.  After log2(NS) rounds a wave
+    // holds the merged sums of 1/NS of head_dim and writes those output
+    // columns.  A wave writes each round's outgoing half into the LDS slot it
+    // read in the round before (whose only reader was itself), so one barrier
+    // per round suffices.  A unit is 4 accumulator values per lane (16 bytes,
+    // 1 KB per wave).
+    auto finish_block = [&](uint8_t* scK, uint8_t* scV) __attribute__((always_inline)) {
+        constexpr int U = 4 * C::DB;
+        float l = tgd::half_sum(l_run);  // per query (the half-waves held different keys)
+        if constexpr (NS == 1) {
+            store_units<D, 0, U, OUT_F32>(o, l, t, nk, hq, h, g, out);
+        } else {
+            const auto slot_ptr = [&](int slot) {
+                const int off = (hr * NS + slot) * C::SLOT_BYTES;
+                return reinterpret_cast<float*>(off < C::TILE_BYTES ? scK + off : scV + (off - C::TILE_BYTES));
+            };
+            __syncthreads();  // every wave is done with this stage's K/V
+            // One round with split stride S while holding units LO .. LO+2*half-1;
+            // x = XOR of the strides of the earlier rounds.  The branch on this
+            // wave's split bit is wave-uniform; every wave meets one barrier.
+            const auto round = [&](auto self, auto LO, auto S, int x) __attribute__((always_inline)) -> void {
+                constexpr int lo = decltype(LO)::value, s = decltype(S)::value;
+                constexpr int half = U * s / NS;
+                const int ws = sp ^ x, rs = sp ^ s ^ x;
+                const auto step = [&](auto KEEP) __attribute__((always_inline)) {
+                    constexpr int keep = decltype(KEEP)::value;
+                    constexpr int give = keep == lo ? lo + half : lo;
+                    float* dst = slot_ptr(ws);
 #pragma unroll
-        for (int s = 0; s < NS; ++s) m_tot = fmaxf(m_tot, mbuf[hr][s][l32]);
-        const float f = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_tot);
-        const float l_half = tgd::half_sum(l_run);
-        if (g == 0) lbuf[hr][sp][l32] = l_half * f;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-            o[db] *= f;
-            if (NS > 1) {
-                if (sp != 0) {
-                    float* dst = slot_ptr(hr * (NS - 1) + sp - 1);
-#pragma unroll
-                    for (int i4 = 0; i4 < 4; ++i4)
-                        *reinterpret_cast<float4*>(dst + 4 * (i4 * 64 + lane)) =
-                            float4{o[db][4 * i4], o[db][4 * i4 + 1], o[db][4 * i4 + 2], o[db][4 * i4 + 3]};
-                }
-                __syncthreads();
-                if (sp == 0) {
-#pragma unroll
-                    for (int s = 1; s < NS; ++s) {
-                        const float* src = slot_ptr(hr * (NS - 1) + s - 1);
-#pragma unroll
-                        for (int i4 = 0; i4 < 4; ++i4) {
-                            const float4 x = *reinterpret_cast<const float4*>(src + 4 * (i4 * 64 + lane));
-                            o[db][4 * i4] += x.x;
-                            o[db][4 * i4 + 1] += x.y;
-                            o[db][4 * i4 + 2] += x.z;
-                            o[db][4 * i4 + 3] += x.w;
-                        }
+                    for (int u = give; u < give + half; ++u) {
+                        const f32x16& a = o[u / 4];
+                        const int i = 4 * (u % 4);
+                        *reinterpret_cast<float4*>(dst + 4 * ((u - give) * 64 + lane)) =
+                            float4{a[i], a[i + 1], a[i + 2], a[i + 3]};
                     }
-                }
-                __syncthreads();
-            }
-        }
-        if (sp != 0 || t >= nk) return;
-        float l_tot = 0.0f;
+                    if (g == 0) {
+                        mbuf[hr][ws][l32] = m_run;
+                        lbuf[hr][ws][l32] = l;
+                    }
+                    __syncthreads();
+                    const float mp = mbuf[hr][rs][l32], lp = lbuf[hr][rs][l32];
+                    const float mn = fmaxf(m_run, mp);
+                    const float fs = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - mn);
+                    const float fp = mp == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mp - mn);
+                    const float* src = slot_ptr(rs);
 #pragma unroll
-        for (int s = 0; s < NS; ++s) l_tot += lbuf[hr][s][l32];
-        const float inv = 1.0f / l_tot;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const int dd = db * 32 + 8 * i4 + 4 * g;
-                const int64_t off = ((int64_t)t * hq + h) * D + dd;
-                const float y0 = o[db][4 * i4] * inv, y1 = o[db][4 * i4 + 1] * inv;
-                const float y2 = o[db][4 * i4 + 2] * inv, y3 = o[db][4 * i4 + 3] * inv;
-                if (OUT_F32) {
-                    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + off) = float4{y0, y1, y2, y3};
-                } else {
-                    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + off) =
-                        u32x2{tgd::cvt_pk_bf16(y0, y1), tgd::cvt_pk_bf16(y2, y3)};
-                }
-            }
+                    for (int u = keep; u < keep + half; ++u) {
+                        const float4 y = *reinterpret_cast<const float4*>(src + 4 * ((u - keep) * 64 + lane));
+                        f32x16& a = o[u / 4];
+                        const int i = 4 * (u % 4);
+                        a[i] = fmaf(a[i], fs, y.x * fp);
+                        a[i + 1] = fmaf(a[i + 1], fs, y.y * fp);
+                        a[i + 2] = fmaf(a[i + 2], fs, y.z * fp);
+                        a[i + 3] = fmaf(a[i + 3], fs, y.w * fp);
+                    }
+                    l = fmaf(l, fs, lp * fp);
+                    m_run = mn;
+                    if constexpr (s > 1)
+                        self(self, KEEP, IC<s / 2>{}, x ^ s);
+                    else
+                        store_units<D, keep, half, OUT_F32>(o, l, t, nk, hq, h, g, out);
+                };
+                if (sp & s)
+                    step(IC<lo + half>{});
+                else
+                    step(IC<lo>{});
+            };
+            round(round, IC<0>{}, IC<NS / 2>{}, 0);
         }
     };
 
@@ -453,11 +486,11 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
         }
     };
 
-    // One iteration: wait for its loads, start the next iteration's loads into
-    // the other stage (every wave finished reading it: barrier at the end of
-    // the previous iteration), multiply.  Current and next stage are distinct
-    // restrict pointers of one scope, so the reads of this stage never wait on
-    // the loads in flight into the other.
+    // One iteration: wait for its loads; the barrier then also means every
+    // wave has finished the previous iteration, which read (and merged in)
+    // the other stage, so the next iteration's loads can go there; multiply.
+    // Current and next stage are distinct restrict pointers of one scope, so
+    // the reads of this stage never wait on the loads in flight into the other.
     auto iterate = [&](int it, uint8_t* __restrict__ cK, uint8_t* __restrict__ cV, float* __restrict__ cS,
                        uint8_t* __restrict__ nK, uint8_t* __restrict__ nV, float* __restrict__ nS) {
         const bool inA = it < nA;
@@ -469,7 +502,6 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
         compute(st * C::SKEYS, cK, cV, cS);
         const int last = inA ? nA - 1 : ntot - nA - 1;
         if (st == last) finish_block(cK, cV);  // K and V of this stage serve as merge scratch
-        __builtin_amdgcn_s_barrier();      // this stage is free for the next issue
     };
 
     issue(0, sK0, sV0, sS0);

@@ -27,7 +27,6 @@ namespace {
 using tgd::u32x4;
 
 constexpr int kThreads = 128;
-constexpr int kUnits = 4;  // 16-byte pieces per thread and pass
 
 // Frequencies theta^(-2j/D), j < D/2, evaluated once on the host in fp64.
 struct Freqs {
