@@ -56,19 +56,20 @@ struct Cfg {
 // formula 7.1.26 (|error| <= 1.5e-7 for x >= 0; odd extension):
 //   erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
 //   t = 1 / (1 + p x).
-// Over the 256 hidden units of a score this moves the normalised score by
-// about 1e-5 at most.
-__device__ __forceinline__ float gelu_erf(float a) {
+// With E = erf(|a| / sqrt 2) and erf odd, 2 GELU(a) = a + |a| E, which is
+// what this returns (the caller folds in the 1/2); exp(-x^2) with
+// x^2 = a^2 / 2 is exp2(a * (a * -log2(e)/2)).  Over the 256 hidden units of a
+// score this moves the normalised score by about 1e-5 at most.
+__device__ __forceinline__ float gelu2_erf(float a) {
     constexpr float p = 0.3275911f;
     constexpr float a1 = 0.254829592f, a2 = -0.284496736f, a3 = 1.421413741f, a4 = -1.453152027f,
                     a5 = 1.061405429f;
-    const float x = fabsf(a) * 0.70710678118654752440f;
-    const float t = __builtin_amdgcn_rcpf(fmaf(p, x, 1.0f));
+    constexpr float kHalfLog2e = 0.72134752044448170368f;  // log2(e) / 2
+    const float ax = fabsf(a);
+    const float t = __builtin_amdgcn_rcpf(fmaf(p * 0.70710678118654752440f, ax, 1.0f));
     const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, a5, a4), a3), a2), a1);
-    const float e = __builtin_amdgcn_exp2f(-x * x * 1.44269504088896340736f);
-    const float erf_abs = fmaf(-poly, e, 1.0f);
-    const float erf_v = a < 0.0f ? -erf_abs : erf_abs;
-    return 0.5f * a * (1.0f + erf_v);
+    const float e = __builtin_amdgcn_exp2f(a * (a * -kHalfLog2e));
+    return fmaf(ax, fmaf(-poly, e, 1.0f), a);
 }
 
 // Permutation of the eight 16-byte pieces of a 128-byte LDS row (XOR mask
@@ -83,54 +84,39 @@ __device__ __forceinline__ int swz8(int r) {
 
 #define TG_LDS __attribute__((address_space(3)))
 
-// N 16-byte LDS reads issued together and waited for before the block ends
-// (the registers an inline-assembly load writes must be complete when the
-// block ends).
-template <int N>
-__device__ __forceinline__ void lds_read_wait(u32x4 (&v)[N], const uint32_t (&a)[N]);
-template <>
-__device__ __forceinline__ void lds_read_wait<4>(u32x4 (&v)[4], const uint32_t (&a)[4]) {
-    asm volatile(
-        "ds_read_b128 %0, %4\n\t"
-        "ds_read_b128 %1, %5\n\t"
-        "ds_read_b128 %2, %6\n\t"
-        "ds_read_b128 %3, %7\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
-        : "memory");
+// Fourth word of a raw buffer resource on gfx9-family parts: 32-bit data
+// format, no swizzle; with a zero stride, offsets at or past num_records read
+// as zero.
+constexpr int kBufferWord3 = 0x00020000;
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over `bytes` bytes from base (zero stride).
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, int bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return i32x4{(int32_t)(uint32_t)a, (int32_t)((uint32_t)(a >> 32) & 0xffffu), bytes, kBufferWord3};
 }
-template <>
-__device__ __forceinline__ void lds_read_wait<6>(u32x4 (&v)[6], const uint32_t (&a)[6]) {
+
+// Direct load of 16 bytes per lane from the resource at voff + soff into LDS
+// at lds + 16 * lane.  Issued from inline assembly so the compiler does not
+// track these LDS writes: it would otherwise make the operand reads of one
+// stage wait for the loads in flight into the others.  The instruction writes
+// no register; the tile loop orders it with explicit vector-memory waits and
+// the workgroup barrier.
+// (m0 is set right before each use of it, so clobbering it here is safe.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void buffer_to_lds16(i32x4 rs, const TG_LDS uint8_t* lds, uint32_t voff, uint32_t soff) {
+    const uint32_t m = (uint32_t)(uintptr_t)lds;
     asm volatile(
-        "ds_read_b128 %0, %6\n\t"
-        "ds_read_b128 %1, %7\n\t"
-        "ds_read_b128 %2, %8\n\t"
-        "ds_read_b128 %3, %9\n\t"
-        "ds_read_b128 %4, %10\n\t"
-        "ds_read_b128 %5, %11\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5])
-        : "memory");
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds"
+        :
+        : "s"(m), "v"(voff), "s"(rs), "s"(soff)
+        : "memory", "m0");
 }
-template <>
-__device__ __forceinline__ void lds_read_wait<8>(u32x4 (&v)[8], const uint32_t (&a)[8]) {
-    asm volatile(
-        "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %9\n\t"
-        "ds_read_b128 %2, %10\n\t"
-        "ds_read_b128 %3, %11\n\t"
-        "ds_read_b128 %4, %12\n\t"
-        "ds_read_b128 %5, %13\n\t"
-        "ds_read_b128 %6, %14\n\t"
-        "ds_read_b128 %7, %15\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]),
-          "=&v"(v[7])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
-        : "memory");
-}
+#pragma clang diagnostic pop
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
 #define TG_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
@@ -160,7 +146,8 @@ __global__ __launch_bounds__(kThreads) void gate_mlp(const uint16_t* __restrict_
     __shared__ float sR[kBT];
     __shared__ float sS[kBT];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in a scalar register
     const int wh = wave % C::WAVES_H, wt = wave / C::WAVES_H;
     const int l32 = lane & 31, g = lane >> 5;
     const int64_t row0 = (int64_t)blockIdx.x * kBT;
@@ -168,34 +155,41 @@ __global__ __launch_bounds__(kThreads) void gate_mlp(const uint16_t* __restrict_
 
     for (int j = tid; j < HD; j += kThreads) {
         sB1[j] = b1 ? tgd::bf16lo(b1[j]) : 0.0f;
-        sW2[j] = tgd::bf16lo(w2[j]);
+        sW2[j] = 0.5f * tgd::bf16lo(w2[j]);
     }
 
-    // Direct HBM -> LDS loads of one 64-column tile: each wave instruction
-    // fills one 1 KB block = 8 rows of 128 bytes; lane l writes slot l%8 of
-    // row l/8 with the piece (l%8) ^ swz8(row).  Residual rows past n repeat
-    // row n-1 (their scores are never written).
-    // Instructions [i0, i1) of the VM_PER_TILE direct loads of a tile: the
-    // residual blocks first, then the W1 blocks.
-    auto issue_part = [&](int c, uint8_t* stg, int i0, int i1) {
+    // Direct loads of one 64-column tile into LDS, through buffer resources:
+    // each wave instruction fills one 1 KB block = 8 rows of 128 bytes; lane l
+    // writes slot l%8 of row l/8 with the piece (l%8) ^ swz8(row).  A lane's
+    // byte offset within the rows is fixed for the kernel and the tile start is
+    // a scalar offset.  Residual rows past n repeat row n-1 (their scores are
+    // never written).  The residual blocks of a tile come first, then W1's.
+    const int rows_ok = (int)min((int64_t)kBT, n - row0);
+    const uint16_t* rbase = resid + row0 * d;
+    const i32x4 r_rs = buffer_rsrc(rbase, rows_ok * d * 2);
+    const i32x4 w_rs = buffer_rsrc(w1, HD * d * 2);
+    uint32_t voff[VM_PER_TILE];
+#pragma unroll
+    for (int r = 0; r < VM_PER_TILE; ++r) {
         const int slot = lane & 7;
+        const int blk = (r < H_LOADS ? r : r - H_LOADS) * 4 + wave, row = blk * 8 + (lane >> 3);
+        const int src_row = r < H_LOADS ? min(row, rows_ok - 1) : row;
+        voff[r] = (uint32_t)(src_row * d + 8 * (slot ^ swz8(row))) * 2u;
+    }
+    // instructions [i0, i1) of the tile's direct loads
+    auto issue_part = [&](int c, uint8_t* __restrict__ stg, int i0, int i1) {
+        const int soff = c * kKC * 2;
 #pragma unroll
         for (int r = 0; r < VM_PER_TILE; ++r) {
             if (r < i0 || r >= i1) continue;
-            if (r < H_LOADS) {
-                const int blk = r * 4 + wave, row = blk * 8 + (lane >> 3);
-                const int64_t gr = min(row0 + row, n - 1);
-                const uint16_t* src = resid + gr * d + c * kKC + 8 * (slot ^ swz8(row));
-                __builtin_amdgcn_global_load_lds(src, (TG_LDS void*)((TG_LDS uint8_t*)stg + blk * 1024), 16, 0, 0);
-            } else {
-                const int blk = (r - H_LOADS) * 4 + wave, row = blk * 8 + (lane >> 3);
-                const uint16_t* src = w1 + (int64_t)row * d + c * kKC + 8 * (slot ^ swz8(row));
-                __builtin_amdgcn_global_load_lds(src, (TG_LDS void*)((TG_LDS uint8_t*)stg + H_BYTES + blk * 1024),
-                                                 16, 0, 0);
-            }
+            if (r < H_LOADS)
+                buffer_to_lds16(r_rs, (TG_LDS uint8_t*)stg + (r * 4 + wave) * 1024, voff[r], soff);
+            else
+                buffer_to_lds16(w_rs, (TG_LDS uint8_t*)stg + H_BYTES + ((r - H_LOADS) * 4 + wave) * 1024, voff[r],
+                                soff);
         }
     };
-    auto issue = [&](int c, uint8_t* stg) { issue_part(c, stg, 0, VM_PER_TILE); };
+    auto issue = [&](int c, uint8_t* __restrict__ stg) { issue_part(c, stg, 0, VM_PER_TILE); };
 
     f32x16 acc[C::MB][C::NB];
 #pragma unroll
@@ -208,8 +202,9 @@ __global__ __launch_bounds__(kThreads) void gate_mlp(const uint16_t* __restrict_
 
     // Per-lane LDS byte offsets (within a stage) of the operand rows, without
     // the piece: B (residual) rows first, then A (W1) rows.
-    uint32_t roff[C::NB + C::MB];
-    int rswz[C::NB + C::MB];
+    constexpr int NOP = C::NB + C::MB;  // operand reads per k-step
+    uint32_t roff[NOP];
+    int rswz[NOP];
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) {
         const int row = wt * C::WT + nb * 32 + l32;
@@ -223,60 +218,50 @@ __global__ __launch_bounds__(kThreads) void gate_mlp(const uint16_t* __restrict_
         rswz[C::NB + mb] = swz8(row);
     }
 
-    // One tile: wait for its loads (the next tile's stay in flight), start the
-    // loads two tiles ahead into the stage every wave finished reading at the
-    // previous step, multiply.  k-step s of half-wave g reads piece 2s+g of a
-    // row.  The operand reads are issued from inline assembly that waits for
-    // them before it ends: the compiler cannot tell these LDS reads from the
-    // loads in flight into the other stages and would otherwise wait for all
-    // of them; the explicit vector-memory waits above order them instead.
-    auto step = [&](int c, const uint8_t* cur, uint8_t* ahead) {
+    // One tile: wait for its loads (the next tile's stay in flight); the
+    // barrier also means every wave finished the previous step, so the loads
+    // two tiles ahead can go into the stage it read; then all operand reads of
+    // the tile, and its products with those loads in between.  k-step s of half-wave g reads piece 2s+g of
+    // a row.  The current and the ahead stage are distinct restrict pointers
+    // of one scope.
+    auto step = [&](int c, const uint8_t* __restrict__ cur, uint8_t* __restrict__ ahead) {
         if (c + 1 < nchunks) {
             TG_WAIT_VMCNT(VM_PER_TILE);
         } else {
             TG_WAIT_VMCNT(0);
         }
-        __builtin_amdgcn_s_barrier();
+        // barrier that the compiler also treats as a memory fence for its own
+        // scheduling (no LDS read moves above it)
+        asm volatile("s_barrier" ::: "memory");
         const bool more = c + 2 < nchunks;
-        const uint32_t base = (uint32_t)(uintptr_t)(const TG_LDS uint8_t*)cur;
-        constexpr int NOP = C::NB + C::MB;  // operand reads per k-step
-        constexpr int NPAIR = kKC / 32;     // k-step pairs per tile
+        u32x4 op[kKC / 16][NOP];
 #pragma unroll
-        for (int s2 = 0; s2 < kKC / 16; s2 += 2) {
-            // the loads two tiles ahead go out in slices between the pairs, so
-            // the load path is not swamped before any multiply starts
+        for (int s = 0; s < kKC / 16; ++s)
+#pragma unroll
+            for (int i = 0; i < NOP; ++i)
+                op[s][i] = *reinterpret_cast<const u32x4*>(cur + roff[i] + 16 * ((2 * s + g) ^ rswz[i]));
+        constexpr int KS = kKC / 16;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+#pragma unroll
+            for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < C::NB; ++nb) acc[mb][nb] = tgd::mfma32(op[s][C::NB + mb], op[s][nb], acc[mb][nb]);
+            // the loads two tiles ahead go out in slices between the k-steps,
+            // so the address unit works while the matrix cores do
             if (more) {
-                constexpr int per = (VM_PER_TILE + NPAIR - 1) / NPAIR;
-                issue_part(c + 2, ahead, (s2 / 2) * per, (s2 / 2 + 1) * per);
+                constexpr int per = (VM_PER_TILE + KS - 1) / KS;
+                issue_part(c + 2, ahead, s * per, (s + 1) * per);
             }
-            // both k-steps' operands in one block: the reads of this pair are in
-            // flight while the matrix cores still work on the previous pair
-            u32x4 op[2 * NOP];
-            uint32_t addr[2 * NOP];
+            // row sums of squares: the waves sharing a token block split the k-steps
+            if (s % C::WAVES_H == wh) {
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
+                for (int nb = 0; nb < C::NB; ++nb) {
 #pragma unroll
-                for (int i = 0; i < NOP; ++i)
-                    addr[u * NOP + i] = base + roff[i] + 16 * ((2 * (s2 + u) + g) ^ rswz[i]);
-            lds_read_wait<2 * NOP>(op, addr);
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int s = s2 + u;
-#pragma unroll
-                for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-                    for (int nb = 0; nb < C::NB; ++nb)
-                        acc[mb][nb] = tgd::mfma32(op[u * NOP + C::NB + mb], op[u * NOP + nb], acc[mb][nb]);
-                // row sums of squares: the waves sharing a token block split the k-steps
-                if (s % C::WAVES_H == wh) {
-#pragma unroll
-                    for (int nb = 0; nb < C::NB; ++nb) {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const float lo = tgd::bf16lo(op[u * NOP + nb][q]), hi = tgd::bf16hi(op[u * NOP + nb][q]);
-                            ssq[nb] = fmaf(lo, lo, ssq[nb]);
-                            ssq[nb] = fmaf(hi, hi, ssq[nb]);
-                        }
+                    for (int q = 0; q < 4; ++q) {
+                        const float lo = tgd::bf16lo(op[s][nb][q]), hi = tgd::bf16hi(op[s][nb][q]);
+                        ssq[nb] = fmaf(lo, lo, ssq[nb]);
+                        ssq[nb] = fmaf(hi, hi, ssq[nb]);
                     }
                 }
             }
@@ -305,8 +290,19 @@ __global__ __launch_bounds__(kThreads) void gate_mlp(const uint16_t* __restrict_
     }
     __syncthreads();
 
-    // GELU and the w2 dot product over this wave's hidden units.
+    // GELU and the w2 dot product over this wave's hidden units (sW2 holds
+    // w2 / 2, the factor that gelu2_erf leaves out).
     float part[C::NB];
+    float b1r[C::MB][16], w2r[C::MB][16];
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int j = wh * C::WH + mb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+            b1r[mb][i] = sB1[j];
+            w2r[mb][i] = sW2[j];
+        }
+    }
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) {
         const float r = sR[wt * C::WT + nb * 32 + l32];
@@ -314,11 +310,7 @@ __global__ __launch_bounds__(kThreads) void gate_mlp(const uint16_t* __restrict_
 #pragma unroll
         for (int mb = 0; mb < C::MB; ++mb) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int j = wh * C::WH + mb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-                const float a = fmaf(r, acc[mb][nb][i], sB1[j]);
-                p = fmaf(sW2[j], gelu_erf(a), p);
-            }
+            for (int i = 0; i < 16; ++i) p = fmaf(w2r[mb][i], gelu2_erf(fmaf(r, acc[mb][nb][i], b1r[mb][i])), p);
         }
         p += __shfl_xor(p, 32, 64);
         part[nb] = p;
@@ -349,12 +341,20 @@ __global__ __launch_bounds__(kThreads) void gate_mlp(const uint16_t* __restrict_
 constexpr int kNormThreads = 256;
 constexpr int kNormPerThread = 4;
 
-__global__ __launch_bounds__(kNormThreads) void gate_seqnorm(const float* __restrict__ s_raw,
+__global__ __launch_bounds__(kNormThreads) void gate_seqnorm(const float* s_raw,
                                                              const float* __restrict__ block_ss,
                                                              int64_t nblocks, int64_t n, float eps_seq,
-                                                             float* __restrict__ s_norm) {
+                                                             float* s_norm) {
     __shared__ double red[kNormThreads / 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // this thread's raw scores first: their loads overlap the reduction
+    const int64_t base = (int64_t)blockIdx.x * kNormThreads * kNormPerThread;
+    float x[kNormPerThread];
+#pragma unroll
+    for (int e = 0; e < kNormPerThread; ++e) {
+        const int64_t i = base + (int64_t)e * kNormThreads + tid;
+        x[e] = i < n ? s_raw[i] : 0.0f;
+    }
     double acc = 0.0;
     for (int64_t b = tid; b < nblocks; b += kNormThreads) acc += (double)block_ss[b];
 #pragma unroll
@@ -365,11 +365,10 @@ __global__ __launch_bounds__(kNormThreads) void gate_seqnorm(const float* __rest
 #pragma unroll
     for (int w = 0; w < kNormThreads / 64; ++w) tot += red[w];
     const float rho = (float)sqrt(tot / (double)n + (double)eps_seq);
-    const int64_t base = (int64_t)blockIdx.x * kNormThreads * kNormPerThread;
 #pragma unroll
     for (int e = 0; e < kNormPerThread; ++e) {
-        int64_t i = base + (int64_t)e * kNormThreads + tid;
-        if (i < n) s_norm[i] = s_raw[i] / rho;
+        const int64_t i = base + (int64_t)e * kNormThreads + tid;
+        if (i < n) s_norm[i] = x[e] / rho;
     }
 }
 
