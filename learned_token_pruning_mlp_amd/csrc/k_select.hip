@@ -46,14 +46,18 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Inclusive scan over the 64 lanes of a wave.
-template <typename T>
-__device__ __forceinline__ T wave_incl_scan(T x, int lane) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        T y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
+// Inclusive scan over the 64 lanes of a wave with DPP lane moves (no LDS
+// round trips): shifts by 1, 2, 4 and 8 inside each row of 16 lanes (lanes
+// with no source add 0), then the last lane of row 0 is added to row 1 and of
+// row 2 to row 3 (row_bcast:15), then the last lane of row 1 to rows 2 and 3
+// (row_bcast:31).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);  // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);  // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);  // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);  // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
     return x;
 }
 
@@ -61,23 +65,29 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// Exclusive scan over the whole workgroup; returns the block total in *total.
-__device__ __forceinline__ uint64_t block_excl_scan(uint64_t x, uint64_t* wsum, uint64_t* total) {
+// Exclusive scan over the whole workgroup with one barrier: wave scans, wave
+// totals through LDS (wsum: kWaves slots, alternated by the caller between
+// consecutive scans so a slow reader of the last one is never overwritten),
+// and every thread adds the totals of the waves below its own.  Returns the
+// exclusive prefix; *total gets the workgroup sum.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* wsum, uint32_t* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint64_t incl = wave_incl_scan(x, lane);
+    const uint32_t incl = wave_incl_scan(x);
     if (lane == 63) wsum[wave] = incl;
     __syncthreads();
-    if (wave == 0) {
-        uint64_t w = lane < kWaves ? wsum[lane] : 0;
-        uint64_t wi = wave_incl_scan(w, lane);
-        if (lane < kWaves) wsum[lane] = wi - w;  // exclusive offsets
-        if (lane == kWaves - 1) wsum[kWaves] = wi;
+    uint32_t below = 0, all = 0;
+#pragma unroll
+    for (int w4 = 0; w4 < kWaves; w4 += 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(&wsum[w4]);
+        const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            all += vv[q];
+            if (w4 + q < wave) below += vv[q];
+        }
     }
-    __syncthreads();
-    uint64_t r = incl - x + wsum[wave];
-    *total = wsum[kWaves];
-    __syncthreads();
-    return r;
+    *total = all;
+    return below + incl - x;
 }
 
 // Keys of tokens i .. i+3 (i a multiple of 4), straight from the scores.
@@ -113,9 +123,16 @@ __global__ __launch_bounds__(kThreads) void select_topk_block(const float* __res
     constexpr int kBins = 2048;
     constexpr int kCap = 4096;  // gathered candidates
     __shared__ __attribute__((aligned(16))) uint32_t keys[kKeysInLds ? kLdsKeys : 4];
-    __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
-    __shared__ __attribute__((aligned(16))) uint32_t cand[kCap];
-    __shared__ uint64_t wsum[kWaves + 1];
+    // first-round histogram in three copies (lane % 3 picks one), so lanes of
+    // a wave that hit the same bin mostly update different words; copy 0 then
+    // holds the sum and serves the later rounds, and the gathered candidates
+    // take the place of copies 1 and 2
+    constexpr int kCopies = 3;
+    static_assert((kCopies - 1) * kBins >= kCap, "candidate room");
+    __shared__ __attribute__((aligned(16))) uint32_t hist4[kCopies][kBins];
+    uint32_t* hist = hist4[0];
+    uint32_t* cand = hist4[1];
+    __shared__ __attribute__((aligned(16))) uint32_t wsum[2][kWaves];
     __shared__ uint32_t ctl[4];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -159,12 +176,12 @@ __global__ __launch_bounds__(kThreads) void select_topk_block(const float* __res
                 const uint4 h4 = *reinterpret_cast<const uint4*>(&hist[hi - per + i]);
                 sum += h4.x + h4.y + h4.z + h4.w;
             }
-            const uint32_t incl = wave_incl_scan(sum, lane);
+            const uint32_t incl = wave_incl_scan(sum);
             const int L = __builtin_ctzll(__builtin_amdgcn_ballot_w64(incl >= remaining));
-            const uint32_t before = __shfl(incl - sum, L, 64);
+            const uint32_t before = __builtin_amdgcn_readlane(incl - sum, L);
             const int hiL = nbins - L * per;
             const uint32_t c = lane < per ? hist[hiL - 1 - lane] : 0u;
-            const uint32_t ci = wave_incl_scan(c, lane) + before;
+            const uint32_t ci = wave_incl_scan(c) + before;
             const int b = __builtin_ctzll(__builtin_amdgcn_ballot_w64(lane < per && ci >= remaining));
             if (lane == b) {
                 ctl[0] = hiL - 1 - b;
@@ -178,9 +195,11 @@ __global__ __launch_bounds__(kThreads) void select_topk_block(const float* __res
     };
 
     // Sweep 1: keys to LDS, forced count, histogram of the top 11 bits.
-    clear_hist();
+    for (int b = tid * 4; b < kCopies * kBins; b += kThreads * 4)
+        *reinterpret_cast<uint4*>(&hist4[0][0] + b) = uint4{0u, 0u, 0u, 0u};
     __syncthreads();
-    uint64_t fc = 0;
+    uint32_t fcw = 0;  // forced tokens seen by this wave (wave-uniform)
+    uint32_t* myhist = hist4[lane % kCopies];
     for (uint32_t c0 = 0; c0 < n; c0 += kStep) {
         uint4 kv[4];
 #pragma unroll
@@ -188,27 +207,34 @@ __global__ __launch_bounds__(kThreads) void select_topk_block(const float* __res
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const uint32_t i = c0 + (e * kThreads + tid) * 4;
+            if (kKeysInLds && i + 4 <= n) *reinterpret_cast<uint4*>(&keys[i]) = kv[e];
             const uint32_t kk[4] = {kv[e].x, kv[e].y, kv[e].z, kv[e].w};
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                if (i + q < n) {
-                    const bool f = kk[q] == kForcedMark;
-                    fc += f ? 1u : 0u;
-                    if (!f) atomicAdd(&hist[kk[q] >> 21], 1u);
-                    if (kKeysInLds) keys[i + q] = kk[q];
-                }
+                const bool ok = i + q < n;
+                const bool f = ok && kk[q] == kForcedMark;
+                fcw += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(f));
+                if (ok && !f) atomicAdd(&myhist[kk[q] >> 21], 1u);
+                if (kKeysInLds && ok && i + 4 > n) keys[i + q] = kk[q];
             }
         }
     }
-    // forced count: a wave sum, then every thread adds the per-wave sums
-    // after the barrier that also publishes the keys and the histogram
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) fc += __shfl_xor(fc, o, 64);
-    if (lane == 0) wsum[threadIdx.x >> 6] = fc;
+    if (lane == 0) wsum[0][threadIdx.x >> 6] = fcw;
     __syncthreads();
     uint64_t F = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) F += wsum[w];
+    for (int w = 0; w < kWaves; ++w) F += wsum[0][w];
+    // merge the histogram copies into copy 0
+    for (int b = tid * 4; b < kBins; b += kThreads * 4) {
+        uint4 h = *reinterpret_cast<const uint4*>(&hist4[0][b]);
+#pragma unroll
+        for (int c = 1; c < kCopies; ++c) {
+            const uint4 x = *reinterpret_cast<const uint4*>(&hist4[c][b]);
+            h.x += x.x, h.y += x.y, h.z += x.z, h.w += x.w;
+        }
+        *reinterpret_cast<uint4*>(&hist4[0][b]) = h;
+    }
+    __syncthreads();
     int64_t R = (int64_t)k - (int64_t)F;  // prunable tokens to choose
     if (tid == 0 && dev_status) {
         int32_t st = 0;
@@ -226,11 +252,15 @@ __global__ __launch_bounds__(kThreads) void select_topk_block(const float* __res
         const uint32_t bucket = hist[ctl[0]];
         __syncthreads();
 
-        // Gather the bucket's keys when they fit; otherwise filter on the fly.
-        const bool gathered = bucket <= (uint32_t)kCap;
+        // Long prompts (keys re-read from memory in every sweep) gather the
+        // bucket's keys when they fit; with the keys in LDS, and for buckets
+        // too large to gather, the later rounds sweep all keys with a prefix
+        // filter.
+        const bool gathered = !kKeysInLds && bucket <= (uint32_t)kCap;
         if (gathered) {
             // each wave reserves room for its matches with one LDS atomic per
-            // four keys a lane, then the lanes write them
+            // four keys a lane; a lane's slots follow from ballots of the
+            // matches (all lanes below it, then its own lower keys)
             if (tid == 0) ctl[2] = 0;
             __syncthreads();
             for (uint32_t c0 = 0; c0 < n; c0 += kStep) {
@@ -239,18 +269,23 @@ __global__ __launch_bounds__(kThreads) void select_topk_block(const float* __res
                     const uint32_t i = c0 + (e * kThreads + tid) * 4;
                     const uint4 kv = keys4(i);
                     const uint32_t kq[4] = {kv.x, kv.y, kv.z, kv.w};
-                    uint32_t hit = 0;
+                    bool hit[4];
+                    uint64_t bq[4];
+                    uint32_t wtot = 0, pre = 0;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (i + q < n && kq[q] != kForcedMark && (kq[q] & pmask) == prefix) hit |= 1u << q;
-                    const uint32_t cnt = __builtin_popcount(hit);
-                    const uint32_t incl = wave_incl_scan(cnt, lane);
+                    for (int q = 0; q < 4; ++q) {
+                        hit[q] = i + q < n && kq[q] != kForcedMark && (kq[q] & pmask) == prefix;
+                        bq[q] = __builtin_amdgcn_ballot_w64(hit[q]);
+                        wtot += (uint32_t)__builtin_popcountll(bq[q]);
+                        pre += lanes_below(bq[q]);
+                    }
+                    if (wtot == 0) continue;  // wave-uniform
                     uint32_t base = 0;
-                    if (lane == 63 && incl) base = atomicAdd(&ctl[2], incl);
-                    base = __shfl(base, 63, 64) + incl - cnt;
+                    if (lane == 0) base = atomicAdd(&ctl[2], wtot);
+                    base = __builtin_amdgcn_readlane(base, 0) + pre;
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        if (hit & (1u << q)) cand[base++] = kq[q];
+                        if (hit[q]) cand[base++] = kq[q];
                 }
             }
             __syncthreads();
@@ -286,8 +321,9 @@ __global__ __launch_bounds__(kThreads) void select_topk_block(const float* __res
     // Emit, in index order: slot = (#kind1 before) + min(#ties before, m).
     // Sixteen consecutive tokens per thread, so up to 16384 tokens take one
     // pass (one workgroup scan).
-    uint64_t carry = 0;
-    for (uint32_t c0 = 0; c0 < n; c0 += kThreads * 16) {
+    uint64_t carryA = 0, carryB = 0;
+    int pass = 0;
+    for (uint32_t c0 = 0; c0 < n; c0 += kThreads * 16, ++pass) {
         const uint32_t base = c0 + (uint32_t)tid * 16;
         uint32_t ka = 0, kb = 0;  // bit e: token base+e is forced or above T / equal to T
 #pragma unroll
@@ -304,27 +340,38 @@ __global__ __launch_bounds__(kThreads) void select_topk_block(const float* __res
                 }
             }
         }
+        // both counts in one word: each is at most 16 per thread and 16384
+        // per pass
         const uint32_t ca = __builtin_popcount(ka), cb = __builtin_popcount(kb);
-        uint64_t tot;
-        const uint64_t ex = block_excl_scan(((uint64_t)ca << 32) | cb, wsum, &tot) + carry;
-        uint32_t A = (uint32_t)(ex >> 32), B = (uint32_t)ex;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            if (ka & (1u << e)) {
-                const uint32_t slot = A + (B < m ? B : m);
-                if (slot < k) kept[slot] = (int32_t)(base + e);
-                ++A;
-            } else if (kb & (1u << e)) {
-                if (B < m) {
-                    const uint32_t slot = A + B;
-                    if (slot < k) kept[slot] = (int32_t)(base + e);
-                }
-                ++B;
+        uint32_t tot;
+        const uint32_t ex = block_excl_scan((ca << 16) | cb, wsum[pass & 1], &tot);
+        const uint64_t A = carryA + (ex >> 16), B = carryB + (ex & 0xffffu);
+        // Only kept tokens are visited: those of kind 1 and the first m - B
+        // ties of this thread (ties before it took B of the m).  Token e's
+        // slot is (#kind 1 before it) + min(#ties before it, m).
+        uint32_t keep = ka;
+        if (B < m) {
+            uint32_t ties = kb;
+            if (m - B < (uint64_t)cb) {
+                // only the first m - B of them fit: clear the rest
+                uint32_t rest = kb;
+                for (uint32_t r = 0; r < (uint32_t)(m - B); ++r) rest &= rest - 1;
+                ties &= ~rest;
             }
+            keep |= ties;
         }
-        carry += tot;
+        while (keep) {
+            const int e = __builtin_ctz(keep);
+            keep &= keep - 1;
+            const uint32_t below = (1u << e) - 1u;
+            const uint64_t a_before = A + __builtin_popcount(ka & below);
+            const uint64_t b_before = B + __builtin_popcount(kb & below);
+            const uint64_t slot = a_before + (b_before < m ? b_before : m);
+            if (slot < k) kept[slot] = (int32_t)(base + e);
+        }
+        carryA += tot >> 16;
+        carryB += tot & 0xffffu;
     }
-    (void)lane;
 }
 
 }  // namespace
