@@ -6,7 +6,9 @@
 // gate sits; slinene.github.io digest, method key points; aiwillknow.com,
 // Figure 1(a)(b)).
 //
-// Kernel 1 (gate_mlp): one workgroup takes 64 residual rows.  The residual
+// Kernel 1 (gate_mlp): one workgroup takes 64 residual rows (eight waves for
+// 256 hidden units, two per SIMD, so one wave's load latency hides behind the
+// other's products; four below).  The residual
 // row norm is applied after the product, as a per-row scale (the product is
 // linear in the row), so the matrix cores see the exact bf16 residual:
 //     a_ij = r_i * (h_i . w1_j) + b1_j,  r_i = 1/sqrt(mean_k h_ik^2 + eps)
@@ -36,14 +38,17 @@ namespace {
 using tgd::f32x16;
 using tgd::u32x4;
 
-constexpr int kThreads = 256;
 constexpr int kBT = tgi::kGateRowsPerBlock;  // 64 rows per workgroup
 constexpr int kKC = 64;                      // d-columns per LDS tile
 
 template <int HD>
 struct Cfg {
+    // 256 hidden units: eight waves (two per SIMD, so one wave's LDS and
+    // direct-load latency hides behind the other's products); fewer: four
+    static constexpr int WAVES = HD >= 256 ? 8 : 4;
+    static constexpr int THREADS = 64 * WAVES;
     static constexpr int WAVES_H = HD >= 128 ? 4 : 2;  // waves along hidden units
-    static constexpr int WAVES_T = 4 / WAVES_H;         // waves along tokens
+    static constexpr int WAVES_T = WAVES / WAVES_H;     // waves along tokens
     static constexpr int WH = HD / WAVES_H;             // hidden units per wave
     static constexpr int WT = kBT / WAVES_T;            // tokens per wave
     static constexpr int MB = WH / 32;                  // 32-row blocks of hidden units
@@ -122,7 +127,7 @@ __device__ __forceinline__ void buffer_to_lds16(i32x4 rs, const TG_LDS uint8_t* 
 #define TG_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
 template <int HD>
-__global__ __launch_bounds__(kThreads) void gate_mlp(const uint16_t* __restrict__ resid,
+__global__ __launch_bounds__(Cfg<HD>::THREADS) void gate_mlp(const uint16_t* __restrict__ resid,
                                                      const uint16_t* __restrict__ w1,
                                                      const uint16_t* __restrict__ b1,
                                                      const uint16_t* __restrict__ w2, float b2,
@@ -133,8 +138,9 @@ __global__ __launch_bounds__(kThreads) void gate_mlp(const uint16_t* __restrict_
     constexpr int H_BYTES = kBT * kKC * 2;            // residual tile: 64 rows x 128 bytes
     constexpr int W_BYTES = HD * kKC * 2;             // W1 tile: HD rows x 128 bytes
     constexpr int STAGE = H_BYTES + W_BYTES;
-    constexpr int H_LOADS = H_BYTES / 1024 / 4;       // 1 KB direct-load instructions per wave
-    constexpr int W_LOADS = W_BYTES / 1024 / 4;
+    constexpr int H_LOADS = H_BYTES / 1024 / C::WAVES;  // 1 KB direct-load instructions per wave
+    constexpr int W_LOADS = W_BYTES / 1024 / C::WAVES;
+    static_assert(H_LOADS >= 1 && H_BYTES % (1024 * C::WAVES) == 0 && W_BYTES % (1024 * C::WAVES) == 0, "loads");
     constexpr int VM_PER_TILE = H_LOADS + W_LOADS;
     // three pipeline stages, separate objects (see the tile loop)
     __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
@@ -153,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void gate_mlp(const uint16_t* __restrict_
     const int64_t row0 = (int64_t)blockIdx.x * kBT;
     const int nchunks = d / kKC;
 
-    for (int j = tid; j < HD; j += kThreads) {
+    for (int j = tid; j < HD; j += C::THREADS) {
         sB1[j] = b1 ? tgd::bf16lo(b1[j]) : 0.0f;
         sW2[j] = 0.5f * tgd::bf16lo(w2[j]);
     }
@@ -172,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void gate_mlp(const uint16_t* __restrict_
 #pragma unroll
     for (int r = 0; r < VM_PER_TILE; ++r) {
         const int slot = lane & 7;
-        const int blk = (r < H_LOADS ? r : r - H_LOADS) * 4 + wave, row = blk * 8 + (lane >> 3);
+        const int blk = (r < H_LOADS ? r : r - H_LOADS) * C::WAVES + wave, row = blk * 8 + (lane >> 3);
         const int src_row = r < H_LOADS ? min(row, rows_ok - 1) : row;
         voff[r] = (uint32_t)(src_row * d + 8 * (slot ^ swz8(row))) * 2u;
     }
@@ -183,9 +189,9 @@ __global__ __launch_bounds__(kThreads) void gate_mlp(const uint16_t* __restrict_
         for (int r = 0; r < VM_PER_TILE; ++r) {
             if (r < i0 || r >= i1) continue;
             if (r < H_LOADS)
-                buffer_to_lds16(r_rs, (TG_LDS uint8_t*)stg + (r * 4 + wave) * 1024, voff[r], soff);
+                buffer_to_lds16(r_rs, (TG_LDS uint8_t*)stg + (r * C::WAVES + wave) * 1024, voff[r], soff);
             else
-                buffer_to_lds16(w_rs, (TG_LDS uint8_t*)stg + H_BYTES + ((r - H_LOADS) * 4 + wave) * 1024, voff[r],
+                buffer_to_lds16(w_rs, (TG_LDS uint8_t*)stg + H_BYTES + ((r - H_LOADS) * C::WAVES + wave) * 1024, voff[r],
                                 soff);
         }
     };
@@ -377,7 +383,7 @@ int launch_gate_hd(const uint16_t* resid, const uint16_t* w1, const uint16_t* b1
                    float b2, int64_t n, int d, float eps_row, float* s_out, float* block_ss,
                    hipStream_t s) {
     const int64_t nb = tgi::gate_blocks(n);
-    hipLaunchKernelGGL(gate_mlp<HD>, dim3((unsigned)nb), dim3(kThreads), 0, s, resid, w1, b1, w2, b2, n,
+    hipLaunchKernelGGL(gate_mlp<HD>, dim3((unsigned)nb), dim3(Cfg<HD>::THREADS), 0, s, resid, w1, b1, w2, b2, n,
                        d, eps_row, s_out, block_ss);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_EDEVICE;
 }
