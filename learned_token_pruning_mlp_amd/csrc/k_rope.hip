@@ -87,7 +87,7 @@ __device__ __forceinline__ void rotate8(u32x4 a, u32x4 b, const double* c8, cons
 // row, then the angles (waiting only for their inputs while the data loads
 // fly), then rotate and store.
 constexpr int kThreadsV8 = 256;
-constexpr int kUnitsV8 = 4;  // 16-byte pieces per thread in the first pass
+constexpr int kUnitsV8 = 4;  // 16-byte pieces per thread in the first pass (at most)
 
 template <int D>
 __global__ __launch_bounds__(kThreadsV8) void rope_row_v8(uint16_t* __restrict__ x0, int h0,
@@ -99,6 +99,7 @@ __global__ __launch_bounds__(kThreadsV8) void rope_row_v8(uint16_t* __restrict__
     const int64_t row = blockIdx.x;
     const int tid = threadIdx.x;
     const int units = (h0 + h1) * GROUPS;
+    const int passes = min(kUnitsV8, (units + kThreadsV8 - 1) / kThreadsV8);  // workgroup-uniform
     // unit e: head hh = e / GROUPS (the first h0 in x0, the rest in x1),
     // pairs 8 * (e % GROUPS) .. +7
     auto unit_ptr = [&](int e) -> uint16_t* {
@@ -113,8 +114,9 @@ __global__ __launch_bounds__(kThreadsV8) void rope_row_v8(uint16_t* __restrict__
     u32x4 a[kUnitsV8], b[kUnitsV8];
 #pragma unroll
     for (int u = 0; u < kUnitsV8; ++u) {
-        // units past the end re-read unit 0 (always present) and are not stored:
-        // no branch around the loads, so they all stay in flight together
+        if (u >= passes) break;
+        // threads past the last unit re-read unit 0 (always present) and do
+        // not store: no branch around the loads, so they stay in flight together
         const int e = u * kThreadsV8 + tid;
         const uint16_t* xp = unit_ptr(e < units ? e : 0);
         a[u] = *reinterpret_cast<const u32x4*>(xp);
@@ -125,6 +127,7 @@ __global__ __launch_bounds__(kThreadsV8) void rope_row_v8(uint16_t* __restrict__
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < kUnitsV8; ++u) {
+        if (u >= passes) break;
         const int e = u * kThreadsV8 + tid;
         if (e < units) {
             uint16_t* xp = unit_ptr(e);
