@@ -16,17 +16,16 @@
 // bit-exact and deterministic.
 //
 // One workgroup of 1024 threads does the whole selection (one launch, no
-// workspace traffic).  The bin searches run in one wave (two wave scans), the
-// candidate gather reserves LDS room with one atomic per wave and step, and
-// the emit pass gives each thread sixteen consecutive tokens, so the
-// workgroup meets at few barriers.  Up to 32768 tokens the keys stay in LDS (128 KB of the
-// CU's 160 KB) after one read of the scores, and the first histogram is built
-// during that read.  The keys of the bucket chosen by the first round (for
-// real score distributions a small fraction) are then gathered into LDS so
-// the two later rounds only look at them; when the bucket is too large for
-// the gather buffer (e.g. all scores equal) those rounds sweep all keys with
-// a prefix filter instead.  Longer prompts re-read the scores (L2-resident)
-// in each sweep.
+// workspace traffic).  Up to 32768 tokens each thread keeps the keys of 16
+// (or 32) consecutive tokens in registers after one read of the scores, so
+// every later phase works on registers; the first histogram is built during
+// that read, in eight LDS copies chosen by lane (float keys crowd into a few
+// dozen top-11-bit bins, so lanes of one wave would otherwise collide on the
+// same words), and the later rounds filter the keys by the prefix chosen so
+// far.  Bin searches run in one wave with DPP scans; the emit pass takes one
+// block scan of packed counts and visits only the kept tokens.  Longer
+// prompts re-read the scores (L2-resident) in each sweep and gather the
+// first round's bucket into LDS when it fits.
 #include <hip/hip_runtime.h>
 
 #include "tg_device.h"
@@ -36,7 +35,6 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kLdsKeys = 32768;
 constexpr uint32_t kForcedMark = 0xffffffffu;  // no score maps here (max key is +inf's)
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -114,7 +112,170 @@ __device__ __forceinline__ uint4 keys4_global(const float* __restrict__ score, c
     return k;
 }
 
-template <bool kKeysInLds>
+// Prompts of up to kThreads * KPT tokens: thread t holds the keys of tokens
+// t*KPT .. t*KPT+KPT-1 in registers for the whole selection (one read of the
+// scores), so no phase touches LDS for keys.  Same rounds and emit as the
+// long-prompt kernel below.
+template <int KPT>
+__global__ __launch_bounds__(kThreads) void select_topk_regs(const float* __restrict__ score,
+                                                             const uint8_t* __restrict__ forced,
+                                                             int64_t n64, int64_t n_forced, int64_t k64,
+                                                             int32_t* __restrict__ kept,
+                                                             int32_t* __restrict__ dev_status) {
+    static_assert(KPT % 4 == 0 && KPT <= 32, "keys per thread");
+    constexpr int kBins = 2048;
+    // first-round histogram in eight copies (lane % 8 picks one), so lanes of
+    // a wave that hit the same bin mostly update different words (float keys
+    // crowd into a few dozen top-11-bit bins); copy 0 then holds the sum and
+    // serves the later rounds
+    constexpr int kCopies = 8;
+    __shared__ __attribute__((aligned(16))) uint32_t histc[kCopies][kBins];
+    uint32_t* hist = histc[0];
+    __shared__ __attribute__((aligned(16))) uint32_t wsum[2][kWaves];
+    __shared__ uint32_t ctl[4];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const uint32_t n = (uint32_t)n64, k = (uint32_t)k64;
+    const uint32_t base = (uint32_t)tid * KPT;
+    const int nvalid = base >= n ? 0 : (int)min((uint32_t)KPT, n - base);  // this thread's tokens
+
+    uint32_t key[KPT];
+#pragma unroll
+    for (int v = 0; v < KPT / 4; ++v) {
+        const uint4 k4 = base + 4 * v < n ? keys4_global(score, forced, base + 4 * v, n) : uint4{0u, 0u, 0u, 0u};
+        key[4 * v] = k4.x, key[4 * v + 1] = k4.y, key[4 * v + 2] = k4.z, key[4 * v + 3] = k4.w;
+    }
+
+    auto pick_bin = [&](uint32_t remaining, int nbins) {
+        if (threadIdx.x < 64) {
+            const int per = nbins / 64;
+            const int hi = nbins - lane * per;
+            uint32_t sum = 0;
+            for (int i = 0; i < per; i += 4) {
+                const uint4 h4 = *reinterpret_cast<const uint4*>(&hist[hi - per + i]);
+                sum += h4.x + h4.y + h4.z + h4.w;
+            }
+            const uint32_t incl = wave_incl_scan(sum);
+            const int L = __builtin_ctzll(__builtin_amdgcn_ballot_w64(incl >= remaining));
+            const uint32_t before = __builtin_amdgcn_readlane(incl - sum, L);
+            const int hiL = nbins - L * per;
+            const uint32_t c = lane < per ? hist[hiL - 1 - lane] : 0u;
+            const uint32_t ci = wave_incl_scan(c) + before;
+            const int b = __builtin_ctzll(__builtin_amdgcn_ballot_w64(lane < per && ci >= remaining));
+            if (lane == b) {
+                ctl[0] = hiL - 1 - b;
+                ctl[1] = remaining - (ci - c);
+            }
+        }
+        __syncthreads();
+    };
+
+    // Round 1: forced count and the histogram of the top 11 bits.
+    for (int b = tid * 4; b < kCopies * kBins; b += kThreads * 4)
+        *reinterpret_cast<uint4*>(&histc[0][0] + b) = uint4{0u, 0u, 0u, 0u};
+    __syncthreads();
+    uint32_t fcw = 0;  // forced tokens seen by this wave (wave-uniform)
+    uint32_t* myhist = histc[lane % kCopies];
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+        const bool ok = e < nvalid;
+        const bool f = ok && key[e] == kForcedMark;
+        fcw += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(f));
+        if (ok && !f) atomicAdd(&myhist[key[e] >> 21], 1u);
+    }
+    if (lane == 0) wsum[0][threadIdx.x >> 6] = fcw;
+    __syncthreads();
+    uint64_t F = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) F += wsum[0][w];
+    for (int b = tid * 4; b < kBins; b += kThreads * 4) {
+        uint4 h = *reinterpret_cast<const uint4*>(&histc[0][b]);
+#pragma unroll
+        for (int c = 1; c < kCopies; ++c) {
+            const uint4 x = *reinterpret_cast<const uint4*>(&histc[c][b]);
+            h.x += x.x, h.y += x.y, h.z += x.z, h.w += x.w;
+        }
+        *reinterpret_cast<uint4*>(&histc[0][b]) = h;
+    }
+    __syncthreads();
+    int64_t R = (int64_t)k - (int64_t)F;  // prunable tokens to choose
+    if (tid == 0 && dev_status) {
+        int32_t st = 0;
+        if ((int64_t)F != n_forced) st |= TG_STATUS_FORCED_MISMATCH;
+        if (R < 0) st |= TG_STATUS_FORCED_OVER_K;
+        *dev_status = st;
+    }
+    if (R < 0) R = 0;
+
+    uint32_t T = 0xffffffffu, m = 0;  // R == 0: no prunable token is taken
+    if (R > 0) {
+        pick_bin((uint32_t)R, kBins);
+        uint32_t prefix = ctl[0] << 21, pmask = 0x7ffu << 21, remaining = ctl[1];
+        __syncthreads();
+        // Rounds 2 and 3: next 11 bits, then the last 10, over the keys that
+        // share the prefix chosen so far.
+#pragma unroll
+        for (int round = 0; round < 2; ++round) {
+            const int shift = round == 0 ? 10 : 0;
+            const uint32_t dmask = round == 0 ? 0x7ffu : 0x3ffu;
+            for (int b = tid; b < kBins; b += kThreads) hist[b] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) {
+                const uint32_t key_e = key[e];
+                if (e < nvalid && key_e != kForcedMark && (key_e & pmask) == prefix)
+                    atomicAdd(&hist[(key_e >> shift) & dmask], 1u);
+            }
+            __syncthreads();
+            pick_bin(remaining, (int)dmask + 1);
+            prefix |= ctl[0] << shift;
+            pmask |= dmask << shift;
+            remaining = ctl[1];
+            __syncthreads();
+        }
+        T = prefix;
+        m = remaining;
+    }
+
+    // Emit, in index order: slot = (#kind1 before) + min(#ties before, m).
+    uint32_t ka = 0, kb = 0;  // bit e: token base+e is forced or above T / equal to T
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+        if (e < nvalid) {
+            if (key[e] == kForcedMark || key[e] > T) ka |= 1u << e;
+            else if (key[e] == T) kb |= 1u << e;
+        }
+    }
+    // both counts in one word: each is at most KPT per thread and n <= 32768
+    const uint32_t ca = __builtin_popcount(ka), cb = __builtin_popcount(kb);
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan((ca << 16) | cb, wsum[1], &tot);
+    const uint32_t A = ex >> 16, B = ex & 0xffffu;
+    // Only kept tokens are visited: those of kind 1 and the first m - B ties
+    // of this thread (ties before it took B of the m).
+    uint32_t keep = ka;
+    if (B < m) {
+        uint32_t ties = kb;
+        if (m - B < cb) {
+            uint32_t rest = kb;
+            for (uint32_t r = 0; r < m - B; ++r) rest &= rest - 1;
+            ties &= ~rest;
+        }
+        keep |= ties;
+    }
+    while (keep) {
+        const int e = __builtin_ctz(keep);
+        keep &= keep - 1;
+        const uint32_t below = (1u << e) - 1u;
+        const uint32_t a_before = A + __builtin_popcount(ka & below);
+        const uint32_t b_before = B + __builtin_popcount(kb & below);
+        const uint32_t slot = a_before + (b_before < m ? b_before : m);
+        if (slot < k) kept[slot] = (int32_t)(base + e);
+    }
+}
+
+// Longer prompts: the keys are re-read from the scores (L2-resident) in each
+// sweep.
 __global__ __launch_bounds__(kThreads) void select_topk_block(const float* __restrict__ score,
                                                               const uint8_t* __restrict__ forced,
                                                               int64_t n64, int64_t n_forced, int64_t k64,
@@ -122,7 +283,6 @@ __global__ __launch_bounds__(kThreads) void select_topk_block(const float* __res
                                                               int32_t* __restrict__ dev_status) {
     constexpr int kBins = 2048;
     constexpr int kCap = 4096;  // gathered candidates
-    __shared__ __attribute__((aligned(16))) uint32_t keys[kKeysInLds ? kLdsKeys : 4];
     // first-round histogram in three copies (lane % 3 picks one), so lanes of
     // a wave that hit the same bin mostly update different words; copy 0 then
     // holds the sum and serves the later rounds, and the gathered candidates
@@ -141,10 +301,7 @@ __global__ __launch_bounds__(kThreads) void select_topk_block(const float* __res
 
     // Keys of 4 consecutive tokens starting at i (a multiple of 4; entries
     // past n are garbage and skipped by the callers).
-    auto keys4 = [&](uint32_t i) -> uint4 {
-        if (kKeysInLds) return *reinterpret_cast<const uint4*>(&keys[i]);
-        return keys4_global(score, forced, i, n);
-    };
+    auto keys4 = [&](uint32_t i) -> uint4 { return keys4_global(score, forced, i, n); };
     // Sweep every token; f(i, key) for each i < n.
     auto sweep = [&](auto&& f) {
         for (uint32_t c0 = 0; c0 < n; c0 += kStep) {
@@ -207,7 +364,6 @@ __global__ __launch_bounds__(kThreads) void select_topk_block(const float* __res
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const uint32_t i = c0 + (e * kThreads + tid) * 4;
-            if (kKeysInLds && i + 4 <= n) *reinterpret_cast<uint4*>(&keys[i]) = kv[e];
             const uint32_t kk[4] = {kv[e].x, kv[e].y, kv[e].z, kv[e].w};
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -215,7 +371,6 @@ __global__ __launch_bounds__(kThreads) void select_topk_block(const float* __res
                 const bool f = ok && kk[q] == kForcedMark;
                 fcw += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(f));
                 if (ok && !f) atomicAdd(&myhist[kk[q] >> 21], 1u);
-                if (kKeysInLds && ok && i + 4 > n) keys[i + q] = kk[q];
             }
         }
     }
@@ -252,11 +407,10 @@ __global__ __launch_bounds__(kThreads) void select_topk_block(const float* __res
         const uint32_t bucket = hist[ctl[0]];
         __syncthreads();
 
-        // Long prompts (keys re-read from memory in every sweep) gather the
-        // bucket's keys when they fit; with the keys in LDS, and for buckets
-        // too large to gather, the later rounds sweep all keys with a prefix
-        // filter.
-        const bool gathered = !kKeysInLds && bucket <= (uint32_t)kCap;
+        // Gather the bucket's keys when they fit (the later rounds then read
+        // only them); buckets too large to gather (e.g. all scores equal) take
+        // a prefix-filtered sweep of all keys instead.
+        const bool gathered = bucket <= (uint32_t)kCap;
         if (gathered) {
             // each wave reserves room for its matches with one LDS atomic per
             // four keys a lane; a lane's slots follow from ballots of the
@@ -382,12 +536,15 @@ int launch_select_topk(const float* score, const uint8_t* forced, int64_t n, int
                        int64_t k, int32_t* kept_idx, int32_t* dev_status, void* ws, void* stream) {
     (void)ws;
     hipStream_t s = (hipStream_t)stream;
-    if (n <= kLdsKeys)
-        hipLaunchKernelGGL(select_topk_block<true>, dim3(1), dim3(kThreads), 0, s, score, forced, n,
-                           n_forced, k, kept_idx, dev_status);
+    if (n <= kThreads * 16)
+        hipLaunchKernelGGL(select_topk_regs<16>, dim3(1), dim3(kThreads), 0, s, score, forced, n, n_forced, k,
+                           kept_idx, dev_status);
+    else if (n <= kThreads * 32)
+        hipLaunchKernelGGL(select_topk_regs<32>, dim3(1), dim3(kThreads), 0, s, score, forced, n, n_forced, k,
+                           kept_idx, dev_status);
     else
-        hipLaunchKernelGGL(select_topk_block<false>, dim3(1), dim3(kThreads), 0, s, score, forced, n,
-                           n_forced, k, kept_idx, dev_status);
+        hipLaunchKernelGGL(select_topk_block, dim3(1), dim3(kThreads), 0, s, score, forced, n, n_forced, k,
+                           kept_idx, dev_status);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_EDEVICE;
 }
 

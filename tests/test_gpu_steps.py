@@ -97,9 +97,13 @@ def test_select_gaussian(n, k, f):
     assert np.array_equal(got, oracle.select_topk(score, forced, k))
 
 
-def test_select_all_equal_closed_form():
-    n, k, f = 16384, 1024, 64
-    gu.say("select all-equal")
+@pytest.mark.parametrize("n", [16384, 40000])
+def test_select_all_equal_closed_form(n):
+    """All scores equal: the ties go to the lowest indices.  At 40000 tokens
+    (keys re-read from memory) the first round's bucket is too large to
+    gather, so the later rounds take the prefix-filtered sweep."""
+    k, f = 1024, 64
+    gu.say(f"select all-equal n={n}")
     forced = np.zeros(n, np.uint8)
     forced[-f:] = 1
     got, st = _run_select(np.zeros(n, np.float32), forced, k)
