@@ -412,9 +412,12 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
             sacc[4 * i4 + 2] = sgl * sv[i4].z;
             sacc[4 * i4 + 3] = sgl * sv[i4].w;
         }
+        // (the scheduling barriers keep the products inside the raised-priority run)
         __builtin_amdgcn_s_setprio(1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < C::QS; ++s) sacc = tgd::mfma32(ka[s], qreg[s], sacc);
+        __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
         // V operands: the transposing read hands lane jj of each 16-lane group
         // four consecutive keys of one head_dim column; issued before the
