@@ -29,11 +29,11 @@
 //    tokens were kept) is computed as |lambda_t| * (-S): its query and its
 //    key-bias scale change sign, which is exact, so every row has a positive
 //    exp2 scale and one code path serves all rows.
-//  * Per 32-key block a wave issues all its K-operand and score reads, the
-//    eight S^T products, then the transposing V reads before the softmax, so
+//  * Per 32-key block a wave issues all its K-operand and score reads, then
+//    the eight S^T products with the transposing V reads between them, so
 //    LDS latency overlaps the matrix cores; it raises its issue priority
-//    while it feeds the matrix cores, which staggers the two waves of a SIMD
-//    into alternating matrix and vector phases.
+//    while it issues the P.V products, so that the SIMD's other wave, in its
+//    softmax, does not hold them back.
 //  * Work split: a workgroup owns one GQA kv head, HPW of its q heads and a
 //    pair of 32-row query blocks (b, last - b), so every workgroup carries the
 //    same causal work.  The keys of a query block are streamed as super-tiles
@@ -412,13 +412,12 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
             sacc[4 * i4 + 2] = sgl * sv[i4].z;
             sacc[4 * i4 + 3] = sgl * sv[i4].w;
         }
-        // (the scheduling barriers keep the products inside the raised-priority run)
-        __builtin_amdgcn_s_setprio(1);
+        // Scheduling boundary: the operand reads and the bias products above
+        // are issued first; the products below then interleave with the V
+        // reads that follow (the order that measured fastest at 8K-16K keys).
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < C::QS; ++s) sacc = tgd::mfma32(ka[s], qreg[s], sacc);
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_setprio(0);
         // V operands: the transposing read hands lane jj of each 16-lane group
         // four consecutive keys of one head_dim column; issued before the
         // softmax so they land while it runs.
@@ -468,7 +467,7 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
         }
-        // O^T += V^T . P^T
+        // O^T += V^T . P^T, issued at raised priority
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int s = 0; s < 2; ++s)
