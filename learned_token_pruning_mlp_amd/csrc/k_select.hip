@@ -18,11 +18,11 @@
 // One workgroup of 1024 threads does the whole selection (one launch, no
 // workspace traffic).  Up to 32768 tokens each thread keeps the keys of 16
 // (or 32) consecutive tokens in registers after one read of the scores, so
-// every later phase works on registers; the first histogram is built during
-// that read, in eight LDS copies chosen by lane (float keys crowd into a few
-// dozen top-11-bit bins, so lanes of one wave would otherwise collide on the
-// same words), and the later rounds filter the keys by the prefix chosen so
-// far.  Bin searches run in one wave with DPP scans; the emit pass takes one
+// every later phase works on registers; the histogram copies are cleared
+// while that read is in flight, the first histogram goes into eight LDS
+// copies chosen by lane (float keys crowd into a few dozen top-11-bit bins,
+// so lanes of one wave would otherwise collide on the same words), and the
+// later rounds filter the keys by the prefix chosen so far.  Bin searches run in one wave with DPP scans; the emit pass takes one
 // block scan of packed counts and visits only the kept tokens.  Longer
 // prompts re-read the scores (L2-resident) in each sweep and gather the
 // first round's bucket into LDS when it fits.
@@ -126,11 +126,11 @@ __global__ __launch_bounds__(kThreads) void select_topk_regs(const float* __rest
     constexpr int kBins = 2048;
     // first-round histogram in eight copies (lane % 8 picks one), so lanes of
     // a wave that hit the same bin mostly update different words (float keys
-    // crowd into a few dozen top-11-bit bins); copy 0 then holds the sum and
-    // serves the later rounds
+    // crowd into a few dozen top-11-bit bins); copy 0 then holds the sum, and
+    // copies 1 and 2 (cleared while the copies are summed) serve the second
+    // and third rounds
     constexpr int kCopies = 8;
     __shared__ __attribute__((aligned(16))) uint32_t histc[kCopies][kBins];
-    uint32_t* hist = histc[0];
     __shared__ __attribute__((aligned(16))) uint32_t wsum[2][kWaves];
     __shared__ uint32_t ctl[4];
 
@@ -139,14 +139,30 @@ __global__ __launch_bounds__(kThreads) void select_topk_regs(const float* __rest
     const uint32_t base = (uint32_t)tid * KPT;
     const int nvalid = base >= n ? 0 : (int)min((uint32_t)KPT, n - base);  // this thread's tokens
 
-    uint32_t key[KPT];
+    // Scores and forced flags of this thread's tokens are loaded first; the
+    // histogram copies are cleared while the loads are in flight.
+    float4 sc[KPT / 4];
+    uint32_t fm[KPT / 4];
 #pragma unroll
     for (int v = 0; v < KPT / 4; ++v) {
-        const uint4 k4 = base + 4 * v < n ? keys4_global(score, forced, base + 4 * v, n) : uint4{0u, 0u, 0u, 0u};
-        key[4 * v] = k4.x, key[4 * v + 1] = k4.y, key[4 * v + 2] = k4.z, key[4 * v + 3] = k4.w;
+        const uint32_t i = base + 4 * v;
+        if (i + 4 <= n) {
+            sc[v] = *reinterpret_cast<const float4*>(score + i);
+            fm[v] = forced ? *reinterpret_cast<const uint32_t*>(forced + i) : 0u;
+        } else {
+            float t4[4];
+            uint32_t f = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                t4[q] = (i + q < n) ? score[i + q] : 0.0f;
+                if (forced && i + q < n && forced[i + q]) f |= 1u << (8 * q);
+            }
+            sc[v] = float4{t4[0], t4[1], t4[2], t4[3]};
+            fm[v] = f;
+        }
     }
 
-    auto pick_bin = [&](uint32_t remaining, int nbins) {
+    auto pick_bin = [&](const uint32_t* hist, uint32_t remaining, int nbins) {
         if (threadIdx.x < 64) {
             const int per = nbins / 64;
             const int hi = nbins - lane * per;
@@ -173,6 +189,14 @@ __global__ __launch_bounds__(kThreads) void select_topk_regs(const float* __rest
     // Round 1: forced count and the histogram of the top 11 bits.
     for (int b = tid * 4; b < kCopies * kBins; b += kThreads * 4)
         *reinterpret_cast<uint4*>(&histc[0][0] + b) = uint4{0u, 0u, 0u, 0u};
+    uint32_t key[KPT];
+#pragma unroll
+    for (int v = 0; v < KPT / 4; ++v) {
+        const float x[4] = {sc[v].x, sc[v].y, sc[v].z, sc[v].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            key[4 * v + q] = (fm[v] >> (8 * q)) & 0xffu ? kForcedMark : order_key(x[q]);
+    }
     __syncthreads();
     uint32_t fcw = 0;  // forced tokens seen by this wave (wave-uniform)
     uint32_t* myhist = histc[lane % kCopies];
@@ -188,6 +212,8 @@ __global__ __launch_bounds__(kThreads) void select_topk_regs(const float* __rest
     uint64_t F = 0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) F += wsum[0][w];
+    // (each thread also clears the words of copies 1 and 2 it read: the
+    // second and third rounds count into them)
     for (int b = tid * 4; b < kBins; b += kThreads * 4) {
         uint4 h = *reinterpret_cast<const uint4*>(&histc[0][b]);
 #pragma unroll
@@ -196,6 +222,8 @@ __global__ __launch_bounds__(kThreads) void select_topk_regs(const float* __rest
             h.x += x.x, h.y += x.y, h.z += x.z, h.w += x.w;
         }
         *reinterpret_cast<uint4*>(&histc[0][b]) = h;
+        *reinterpret_cast<uint4*>(&histc[1][b]) = uint4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<uint4*>(&histc[2][b]) = uint4{0u, 0u, 0u, 0u};
     }
     __syncthreads();
     int64_t R = (int64_t)k - (int64_t)F;  // prunable tokens to choose
@@ -209,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void select_topk_regs(const float* __rest
 
     uint32_t T = 0xffffffffu, m = 0;  // R == 0: no prunable token is taken
     if (R > 0) {
-        pick_bin((uint32_t)R, kBins);
+        pick_bin(histc[0], (uint32_t)R, kBins);
         uint32_t prefix = ctl[0] << 21, pmask = 0x7ffu << 21, remaining = ctl[1];
         __syncthreads();
         // Rounds 2 and 3: next 11 bits, then the last 10, over the keys that
@@ -218,16 +246,15 @@ __global__ __launch_bounds__(kThreads) void select_topk_regs(const float* __rest
         for (int round = 0; round < 2; ++round) {
             const int shift = round == 0 ? 10 : 0;
             const uint32_t dmask = round == 0 ? 0x7ffu : 0x3ffu;
-            for (int b = tid; b < kBins; b += kThreads) hist[b] = 0;
-            __syncthreads();
+            uint32_t* hr = histc[1 + round];  // cleared during the merge
 #pragma unroll
             for (int e = 0; e < KPT; ++e) {
                 const uint32_t key_e = key[e];
                 if (e < nvalid && key_e != kForcedMark && (key_e & pmask) == prefix)
-                    atomicAdd(&hist[(key_e >> shift) & dmask], 1u);
+                    atomicAdd(&hr[(key_e >> shift) & dmask], 1u);
             }
             __syncthreads();
-            pick_bin(remaining, (int)dmask + 1);
+            pick_bin(hr, remaining, (int)dmask + 1);
             prefix |= ctl[0] << shift;
             pmask |= dmask << shift;
             remaining = ctl[1];
@@ -240,11 +267,12 @@ __global__ __launch_bounds__(kThreads) void select_topk_regs(const float* __rest
     // Emit, in index order: slot = (#kind1 before) + min(#ties before, m).
     uint32_t ka = 0, kb = 0;  // bit e: token base+e is forced or above T / equal to T
 #pragma unroll
-    for (int e = 0; e < KPT; ++e) {
-        if (e < nvalid) {
-            if (key[e] == kForcedMark || key[e] > T) ka |= 1u << e;
-            else if (key[e] == T) kb |= 1u << e;
-        }
+    for (int e = 0; e < KPT; ++e) {  // (no branches: compares and shifts only)
+        const uint32_t ok = e < nvalid ? 1u : 0u;
+        const uint32_t a = ok & ((key[e] == kForcedMark) | (key[e] > T));
+        const uint32_t b = ok & (a ^ 1u) & (key[e] == T);
+        ka |= a << e;
+        kb |= b << e;
     }
     // both counts in one word: each is at most KPT per thread and n <= 32768
     const uint32_t ca = __builtin_popcount(ka), cb = __builtin_popcount(kb);
