@@ -40,6 +40,8 @@ def parse():
                    choices=["n16k", "n32k-k1024", "n32k-k4096", "n32k-k8192", "n128k", "full16k", "tiny"])
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     p.add_argument("--no-attn-sweep", action="store_true", help="skip the attention-only K sweep")
+    p.add_argument("--no-prefill", action="store_true",
+                   help="skip the whole-prompt comparison (28 decoder layers, full against gated)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="also run one plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -236,6 +238,7 @@ def main():
         del src, dst
 
     sweep = None if args.no_attn_sweep else attn_sweep(tg, torch, dev, shp)
+    prefill = None if (args.no_prefill or args.workload != "n16k") else prefill_compare(tg, torch, dev, shp, seed)
 
     result = {
         "metric": METRIC,
@@ -260,12 +263,75 @@ def main():
         "gate_hbm_gbs": gate_gbs,
         "roofline": roof,
         "attn_sweep": sweep,
+        "prefill": prefill,
         "cpu_baseline": None,
     }
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(shp, seed, inp, a)
     print(json.dumps(result), flush=True)
+
+
+def prefill_compare(tg, torch, dev, shp, seed, n_layers=28, gate_layer=1, reps=3):
+    """One prompt through a Qwen3-1.7B-shaped decoder stack (synthetic weights), both ways:
+    full prefill (every layer on all N tokens, plain causal attention) and gated
+    prefill (layer 0 and the gate layer's attention block on N tokens; scorer,
+    top-K, compaction of the residual and of the lower layers' K/V; the gate
+    layer's MLP and the 26 layers above on the K kept tokens, token-gated
+    attention).  Returns wall times per prompt (ms), timed with HIP events on
+    the stream, after one untimed run of each."""
+    from learned_token_pruning_mlp_amd import synth, upper
+
+    s = upper.QWEN3_1P7B_LAYER
+    assert s.d == shp.d and s.hq == shp.hq and s.hkv == shp.hkv and s.head_dim == shp.head_dim
+    inp = synth.gate_inputs(shp, seed)
+
+    def bf(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    gains = (torch.rand(n_layers, shp.hq, generator=g, device=dev) * 1.5 + 0.5).float()
+    pf = upper.Prefill(s, shp.n, n_layers, gate_layer, bf(inp.w1), bf(inp.w2), gains, shp.temp_coef, dev, seed)
+    h = bf(inp.resid)
+    forced = torch.from_numpy(inp.forced).to(dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    full_ms = timed(lambda: pf.full(h))
+    gated_ms = timed(lambda: pf.gated(h, forced, shp.n_forced, shp.k))
+    pf.blas.close()
+    del pf
+    torch.cuda.empty_cache()
+
+    # algorithmic FLOPs: projections 2 * rows * in * out, causal attention 4 hq D R(R+1)/2
+    D, qd, kvd = s.head_dim, s.hq * s.head_dim, s.hkv * s.head_dim
+
+    def attn_part(r):
+        return 2 * r * s.d * (qd + 2 * kvd) + 2 * r * qd * s.d + 4 * s.hq * D * r * (r + 1) / 2
+
+    def mlp_part(r):
+        return 2 * r * s.d * 2 * s.inter + 2 * r * s.inter * s.d
+
+    n, k = shp.n, shp.k
+    full_flop = n_layers * (attn_part(n) + mlp_part(n))
+    gated_flop = (gate_layer * (attn_part(n) + mlp_part(n)) + attn_part(n) + 2 * n * shp.d * shp.hd
+                  + mlp_part(k) + (n_layers - gate_layer - 1) * (attn_part(k) + mlp_part(k)))
+    return {"layers": n_layers, "gate_layer": gate_layer, "n_tokens": n, "kept": k,
+            "full_ms": round(full_ms, 3), "gated_ms": round(gated_ms, 3), "speedup": round(full_ms / gated_ms, 2),
+            "full_tflops": round(full_flop / (full_ms * 1e-3) / 1e12, 1),
+            "gated_tflops": round(gated_flop / (gated_ms * 1e-3) / 1e12, 1),
+            "weights": "synthetic, one set per layer", "reps": reps}
 
 
 def attn_sweep(tg, torch, dev, shp, ks=(4096, 8192, 16384), reps=10):

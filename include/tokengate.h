@@ -10,6 +10,9 @@
  *   tg_rope, tg_rope_qk -> (auxiliary) rotary embedding at the original positions;
  *   tg_gated_attention -> causal attention over the kept tokens only, with a
  *                         per-key importance bias and a per-query temperature.
+ * The rest of an upper decoder layer on the kept rows (see the section at the
+ * end): tg_rmsnorm, tg_swiglu, and tg_linear (a rocBLAS GEMM through a handle
+ * from tg_blas_create).
  *
  * Sources (web pages on the method; cited by the key in brackets):
  *  [P1] fluxbbs.com, "TokenGate 长上下文预填充提速 11.3 倍，斯坦福伯克利开源门控剪枝":
@@ -182,6 +185,59 @@ int tg_gated_attention(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v,
                        const float* key_score, const float* gains, float temp_coef,
                        const int32_t* pos, int64_t n_kept, int32_t hq, int32_t hkv,
                        int32_t head_dim, void* out, int32_t out_dtype, void* stream);
+
+/*
+ * ---- Upper decoder layer on the kept rows ----
+ * Above the gate only the kept tokens go through the backbone's layers
+ * [P1 gate][P5 Fig 1(a)(b)].  With a Qwen3-shaped backbone a layer is:
+ *   x = rmsnorm(h, w_in); q, k, v = linear(x, Wq / Wk / Wv);
+ *   q, k = rmsnorm per head (w_qn, w_kn); rope at the original positions;
+ *   a = gated attention; h2 = linear(a, Wo) + h;
+ *   x2 = rmsnorm(h2, w_post); h3 = linear(swiglu(linear(x2, Wgu)), Wdown) + h2.
+ * These three entry points are the pieces not covered above; a caller chains
+ * them with tg_rope_qk and tg_gated_attention.
+ */
+
+/*
+ * tg_rmsnorm -- y_r = x_r / sqrt(mean_k x_rk^2 + eps) * weight, per row.
+ * x, y [rows, dim] bf16 (y may equal x); weight [dim] bf16.  fp32 arithmetic,
+ * one rounding to bf16 (nearest-even).  A per-head norm is the same call with
+ * rows = tokens * heads and dim = head_dim.
+ * Supported: dim % 8 == 0 and 8 <= dim <= 4096; x, y, weight 16-byte aligned.
+ * rows == 0 is a no-op.
+ */
+int tg_rmsnorm(const tg_bf16* x, const tg_bf16* weight, tg_bf16* y, int64_t rows, int32_t dim, float eps,
+               void* stream);
+
+/*
+ * tg_swiglu -- out_r = silu(g_r) * u_r with silu(g) = g / (1 + e^-g), where
+ * g_r and u_r are the first and second halves of row r of gate_up.
+ * gate_up [rows, 2 * inter] bf16, out [rows, inter] bf16 (no overlap).  fp32
+ * arithmetic, one rounding to bf16.  Supported: inter % 8 == 0; both 16-byte
+ * aligned.  rows == 0 is a no-op.
+ */
+int tg_swiglu(const tg_bf16* gate_up, tg_bf16* out, int64_t rows, int32_t inter, void* stream);
+
+/*
+ * tg_blas_create / tg_blas_destroy -- a rocBLAS handle for tg_linear.  The
+ * handle is the one piece of library-side state and allocation: the caller
+ * creates it once per device (with that device current), owns it, and
+ * destroys it; calls that share a handle must not run concurrently from
+ * several host threads.  Returns TG_EDEVICE if rocBLAS fails.
+ */
+int tg_blas_create(void** handle);
+int tg_blas_destroy(void* handle);
+
+/*
+ * tg_linear -- y = x . W^T (+ residual): x [rows, in_dim], W [out_dim, in_dim]
+ * (row-major, the usual weight layout), residual NULL or [rows, out_dim], y
+ * [rows, out_dim], all bf16; fp32 accumulation, one rounding of the sum (with
+ * the residual) to bf16.  A library GEMM (rocBLAS gemm_ex) on `stream`.
+ * y must not overlap x or W; it may equal residual.  rows, in_dim, out_dim
+ * >= 1 and below 2^31.
+ */
+int tg_linear(void* handle, const tg_bf16* x, const tg_bf16* w, const tg_bf16* residual, tg_bf16* y,
+              int64_t rows, int32_t in_dim, int32_t out_dim, void* stream);
 
 #ifdef __cplusplus
 }

@@ -27,7 +27,8 @@ TG_STATUS_FORCED_OVER_K = 2
 TG_MAX_GATHER = 16
 
 EXPORTS = ("tg_status_string", "tg_abi_version", "tg_workspace_bytes", "tg_gate_score",
-           "tg_select_topk", "tg_compact", "tg_rope", "tg_rope_qk", "tg_gated_attention")
+           "tg_select_topk", "tg_compact", "tg_rope", "tg_rope_qk", "tg_gated_attention",
+           "tg_rmsnorm", "tg_swiglu", "tg_blas_create", "tg_blas_destroy", "tg_linear")
 
 
 class TgGather(ctypes.Structure):
@@ -71,6 +72,16 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
     L.tg_rope_qk.restype = ctypes.c_int
     L.tg_gated_attention.argtypes = [P, P, P, P, P, F, P, I64, I32, I32, I32, P, I32, P]
     L.tg_gated_attention.restype = ctypes.c_int
+    L.tg_rmsnorm.argtypes = [P, P, P, I64, I32, F, P]
+    L.tg_rmsnorm.restype = ctypes.c_int
+    L.tg_swiglu.argtypes = [P, P, I64, I32, P]
+    L.tg_swiglu.restype = ctypes.c_int
+    L.tg_blas_create.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    L.tg_blas_create.restype = ctypes.c_int
+    L.tg_blas_destroy.argtypes = [P]
+    L.tg_blas_destroy.restype = ctypes.c_int
+    L.tg_linear.argtypes = [P, P, P, P, P, I64, I32, I32, P]
+    L.tg_linear.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -226,3 +237,54 @@ def tg_gated_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_sc
     _check("tg_gated_attention", load().tg_gated_attention(
         _ptr(q), _ptr(k), _ptr(v), _ptr(key_score), _ptr(gains), float(temp_coef), _ptr(pos), nk, hq, hkv, D,
         _ptr(out), od, _stream(stream)))
+
+
+def tg_rmsnorm(x: torch.Tensor, weight: torch.Tensor, y: torch.Tensor, eps: float, stream=None) -> None:
+    """Row RMSNorm over the last dimension of x (any leading shape)."""
+    dim = x.shape[-1]
+    rows = x.numel() // dim if dim else 0
+    _need(x, "x", torch.bfloat16)
+    _need(weight, "weight", torch.bfloat16, (dim,))
+    _need(y, "y", torch.bfloat16, tuple(x.shape))
+    _check("tg_rmsnorm", load().tg_rmsnorm(_ptr(x), _ptr(weight), _ptr(y), rows, dim, float(eps), _stream(stream)))
+
+
+def tg_swiglu(gate_up: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    rows, two_inter = gate_up.shape
+    inter = two_inter // 2
+    _need(gate_up, "gate_up", torch.bfloat16, (rows, 2 * inter))
+    _need(out, "out", torch.bfloat16, (rows, inter))
+    _check("tg_swiglu", load().tg_swiglu(_ptr(gate_up), _ptr(out), rows, inter, _stream(stream)))
+
+
+class BlasHandle:
+    """Owner of a rocBLAS handle from tg_blas_create (destroyed with the object)."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        _check("tg_blas_create", load().tg_blas_create(ctypes.byref(h)))
+        self.value = h
+
+    def close(self):
+        if self.value is not None and self.value.value:
+            _check("tg_blas_destroy", load().tg_blas_destroy(self.value))
+        self.value = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def tg_linear(handle: BlasHandle, x: torch.Tensor, w: torch.Tensor, residual: Optional[torch.Tensor],
+              y: torch.Tensor, stream=None) -> None:
+    """y = x . w^T (+ residual); x [rows, in], w [out, in], y and residual [rows, out]."""
+    rows, in_dim = x.shape
+    out_dim = w.shape[0]
+    _need(x, "x", torch.bfloat16, (rows, in_dim))
+    _need(w, "w", torch.bfloat16, (out_dim, in_dim))
+    _need(residual, "residual", torch.bfloat16, (rows, out_dim), optional=True)
+    _need(y, "y", torch.bfloat16, (rows, out_dim))
+    _check("tg_linear", load().tg_linear(handle.value, _ptr(x), _ptr(w), _ptr(residual), _ptr(y), rows, in_dim,
+                                         out_dim, _stream(stream)))

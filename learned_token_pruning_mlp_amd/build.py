@@ -18,9 +18,11 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtokengate.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ROCM_LIB = "/opt/rocm/lib"
 ARCH = "gfx950"
 
-SOURCES = ["k_gate.hip", "k_select.hip", "k_compact.hip", "k_rope.hip", "k_attn.hip", "tg_api.cpp"]
+SOURCES = ["k_gate.hip", "k_select.hip", "k_compact.hip", "k_rope.hip", "k_attn.hip", "k_layer.hip", "tg_blas.cpp",
+           "tg_api.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC, "-Wall",
           "-Wno-unused-function"]
@@ -49,7 +51,9 @@ def build(verbose: bool = True) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Wl,--no-undefined", *objs, "-o", tmp]
+    # rocBLAS serves the plain GEMMs of the upper-layer projections (tg_linear)
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Wl,--no-undefined", *objs, "-L", ROCM_LIB,
+           "-lrocblas", f"-Wl,-rpath,{ROCM_LIB}", "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")

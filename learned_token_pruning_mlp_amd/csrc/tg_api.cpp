@@ -136,4 +136,40 @@ int tg_gated_attention(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, con
                                        out_dtype, stream);
 }
 
+int tg_rmsnorm(const tg_bf16* x, const tg_bf16* weight, tg_bf16* y, int64_t rows, int32_t dim, float eps,
+               void* stream) {
+    if (rows < 0 || rows > kMaxRows || dim < 8 || dim > 4096 || dim % 8 != 0) return TG_EINVAL;
+    if (!finite_nonneg(eps)) return TG_EINVAL;
+    if (rows == 0) return TG_OK;
+    if (!x || !weight || !y) return TG_EINVAL;
+    if (!aligned(x, 16) || !aligned(weight, 16) || !aligned(y, 16)) return TG_EALIGN;
+    return tgi::launch_rmsnorm(x, weight, y, rows, dim, eps, stream);
+}
+
+int tg_swiglu(const tg_bf16* gate_up, tg_bf16* out, int64_t rows, int32_t inter, void* stream) {
+    if (rows < 0 || rows > kMaxRows || inter < 8 || inter % 8 != 0) return TG_EINVAL;
+    if (rows * (int64_t)(inter / 8) > kMaxRows) return TG_EUNSUPPORTED;
+    if (rows == 0) return TG_OK;
+    if (!gate_up || !out) return TG_EINVAL;
+    if (!aligned(gate_up, 16) || !aligned(out, 16)) return TG_EALIGN;
+    return tgi::launch_swiglu(gate_up, out, rows, inter, stream);
+}
+
+int tg_blas_create(void** handle) {
+    if (!handle) return TG_EINVAL;
+    return tgi::blas_create(handle);
+}
+
+int tg_blas_destroy(void* handle) {
+    if (!handle) return TG_EINVAL;
+    return tgi::blas_destroy(handle);
+}
+
+int tg_linear(void* handle, const tg_bf16* x, const tg_bf16* w, const tg_bf16* residual, tg_bf16* y, int64_t rows,
+              int32_t in_dim, int32_t out_dim, void* stream) {
+    if (rows < 1 || rows > kMaxRows || in_dim < 1 || out_dim < 1) return TG_EINVAL;
+    if (!handle || !x || !w || !y) return TG_EINVAL;
+    return tgi::linear(handle, x, w, residual, y, rows, in_dim, out_dim, stream);
+}
+
 }  // extern "C"

@@ -54,4 +54,14 @@ int launch_gated_attention(const uint16_t* q, const uint16_t* k, const uint16_t*
                            const int32_t* pos, int64_t n_kept, int hq, int hkv, int head_dim,
                            void* out, int out_dtype, void* stream);
 
+int launch_rmsnorm(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t rows, int dim, float eps,
+                   void* stream);
+
+int launch_swiglu(const uint16_t* gu, uint16_t* out, int64_t rows, int inter, void* stream);
+
+int blas_create(void** handle);
+int blas_destroy(void* handle);
+int linear(void* handle, const uint16_t* x, const uint16_t* w, const uint16_t* residual, uint16_t* y, int64_t rows,
+           int in_dim, int out_dim, void* stream);
+
 }  // namespace tgi

@@ -175,3 +175,28 @@ def test_attention_checks(lib):
     assert _att(lib, pos=None) == E.TG_EINVAL
     assert _att(lib, q=M) == E.TG_EALIGN
     assert _att(lib, out=A + 8) == E.TG_EALIGN
+
+
+def test_layer_piece_checks(lib):
+    E = binding
+    # tg_rmsnorm(x, w, y, rows, dim, eps, stream)
+    assert lib.tg_rmsnorm(A, A, A, 0, 128, 1e-6, None) == E.TG_OK  # no rows: no-op
+    assert lib.tg_rmsnorm(A, A, A, -1, 128, 1e-6, None) == E.TG_EINVAL
+    assert lib.tg_rmsnorm(A, A, A, 4, 12, 1e-6, None) == E.TG_EINVAL    # dim not a multiple of 8
+    assert lib.tg_rmsnorm(A, A, A, 4, 8192, 1e-6, None) == E.TG_EINVAL  # dim above 4096
+    assert lib.tg_rmsnorm(A, A, A, 4, 128, -1.0, None) == E.TG_EINVAL
+    assert lib.tg_rmsnorm(None, A, A, 4, 128, 1e-6, None) == E.TG_EINVAL
+    assert lib.tg_rmsnorm(M, A, A, 4, 128, 1e-6, None) == E.TG_EALIGN
+    assert lib.tg_rmsnorm(A, A, M, 4, 128, 1e-6, None) == E.TG_EALIGN
+    # tg_swiglu(gate_up, out, rows, inter, stream)
+    assert lib.tg_swiglu(A, A, 0, 512, None) == E.TG_OK
+    assert lib.tg_swiglu(A, A, 4, 12, None) == E.TG_EINVAL
+    assert lib.tg_swiglu(None, A, 4, 512, None) == E.TG_EINVAL
+    assert lib.tg_swiglu(A, M, 4, 512, None) == E.TG_EALIGN
+    # tg_linear(handle, x, w, residual, y, rows, in_dim, out_dim, stream)
+    assert lib.tg_linear(None, A, A, None, A, 4, 64, 64, None) == E.TG_EINVAL  # no handle
+    assert lib.tg_linear(A, A, A, None, A, 0, 64, 64, None) == E.TG_EINVAL
+    assert lib.tg_linear(A, A, A, None, A, 4, 0, 64, None) == E.TG_EINVAL
+    assert lib.tg_linear(A, None, A, None, A, 4, 64, 64, None) == E.TG_EINVAL
+    assert lib.tg_blas_create(None) == E.TG_EINVAL
+    assert lib.tg_blas_destroy(None) == E.TG_EINVAL
