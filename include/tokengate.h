@@ -30,7 +30,9 @@
  *  - bf16 tensors are passed as uint16_t bit patterns (tg_bf16).
  *  - Every tensor pointer is DEVICE memory owned by the caller; the library
  *    allocates nothing, keeps no state between calls, never synchronises the
- *    stream and never reads device data back to the host.  Work is enqueued on
+ *    stream and never reads device data back to the host.  (The one
+ *    exception is the rocBLAS handle of tg_linear, which the caller creates
+ *    and destroys explicitly with tg_blas_create / tg_blas_destroy.)  Work is enqueued on
  *    `stream` (a hipStream_t passed as void*; NULL = the null stream) and is
  *    complete when the stream reaches that point.
  *  - Arguments are checked on the host before anything is enqueued; a
