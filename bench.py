@@ -310,6 +310,10 @@ def prefill_compare(tg, torch, dev, shp, seed, n_layers=28, gate_layer=1, reps=3
 
     full_ms = timed(lambda: pf.full(h))
     gated_ms = timed(lambda: pf.gated(h, forced, shp.n_forced, shp.k))
+    # the same gated prefill captured once as a HIP graph and replayed
+    graph, _ = pf.capture_gated(h, forced, shp.n_forced, shp.k)
+    graph_ms = timed(graph.replay)
+    del graph
     pf.blas.close()
     del pf
     torch.cuda.empty_cache()
@@ -329,6 +333,7 @@ def prefill_compare(tg, torch, dev, shp, seed, n_layers=28, gate_layer=1, reps=3
                   + mlp_part(k) + (n_layers - gate_layer - 1) * (attn_part(k) + mlp_part(k)))
     return {"layers": n_layers, "gate_layer": gate_layer, "n_tokens": n, "kept": k,
             "full_ms": round(full_ms, 3), "gated_ms": round(gated_ms, 3), "speedup": round(full_ms / gated_ms, 2),
+            "gated_graph_ms": round(graph_ms, 3),
             "full_tflops": round(full_flop / (full_ms * 1e-3) / 1e12, 1),
             "gated_tflops": round(gated_flop / (gated_ms * 1e-3) / 1e12, 1),
             "weights": "synthetic, one set per layer", "reps": reps}

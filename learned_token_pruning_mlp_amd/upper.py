@@ -210,3 +210,21 @@ class Prefill:
             decoder_layer(self.blas, s, self.W[l], src, pos_k, score_k, self.gains[l], self.temp_coef, bk, dst)
             src, dst = dst, (hb if dst is ha else ha)
         return src, kept, pos_k, kv_k
+
+    def capture_gated(self, h: torch.Tensor, forced: torch.Tensor, n_forced: int, k: int):
+        """The gated prefill captured as one HIP graph (the budget k fixes every
+        shape, so one graph serves every prompt of n tokens).  One eager run
+        first lets rocBLAS set itself up outside the capture.  Returns the
+        graph and the tensors its replays write (hidden [k, d], kept_idx,
+        pos_k, trimmed K/V); replay with ``graph.replay()`` after writing the
+        next prompt into ``h``."""
+        self.gated(h, forced, n_forced, k)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(graph, stream=side):
+            outs = self.gated(h, forced, n_forced, k)
+        torch.cuda.current_stream().wait_stream(side)
+        return graph, outs
+
