@@ -189,6 +189,37 @@ int tg_gated_attention(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v,
                        int32_t head_dim, void* out, int32_t out_dtype, void* stream);
 
 /*
+ * tg_attention_bwd_workspace_bytes -- device workspace of tg_gated_attention_bwd
+ * (256-byte aligned): about 4 * n_kept * hq * head_dim bytes plus per-row
+ * arrays.
+ */
+size_t tg_attention_bwd_workspace_bytes(int64_t n_kept, int32_t hq, int32_t hkv, int32_t head_dim);
+
+/*
+ * tg_gated_attention_bwd -- gradients of tg_gated_attention [P1 tga][P2 method]
+ * [P3 tga][P5 Fig 1(c)]: the gate is trained through the upper layers'
+ * attention, whose key bias and gains carry the score gradient.  With
+ * U_tj = q_t.k_j/sqrt(head_dim) + gains[h] key_score[j], Z = lambda_t U and
+ * P = softmax_j(Z) (the forward above), given dout = dL/dO:
+ *   dq [n_kept, hq, head_dim], dk / dv [n_kept, hkv, head_dim]  (fp32 out)
+ *   dscore [n_kept]  = dL/dkey_score   (fp32 out; sums over all heads)
+ *   dgains [hq]      = dL/dgains       (fp32 out)
+ *   dtemp  [1]       = dL/dtemp_coef   (fp32 out)
+ * Inputs as in tg_gated_attention (q, k, v, key_score, gains, temp_coef, pos,
+ * same shapes and limits); dout [n_kept, hq, head_dim] bf16 (16-byte
+ * aligned).  Every output is overwritten (nothing accumulates across calls).
+ * The forward is recomputed (fp32, with its per-row log-sum-exp) into the
+ * workspace; probabilities are rebuilt per 32x32 block, never stored.
+ * bf16 matrix-core products with fp32 accumulation; deterministic (fixed
+ * reduction orders, no atomics).  n_kept == 0 is a no-op.
+ */
+int tg_gated_attention_bwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, const float* key_score,
+                           const float* gains, float temp_coef, const int32_t* pos, int64_t n_kept, int32_t hq,
+                           int32_t hkv, int32_t head_dim, const tg_bf16* dout, float* dq, float* dk, float* dv,
+                           float* dscore, float* dgains, float* dtemp, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
  * ---- Upper decoder layer on the kept rows ----
  * Above the gate only the kept tokens go through the backbone's layers
  * [P1 gate][P5 Fig 1(a)(b)].  With a Qwen3-shaped backbone a layer is:

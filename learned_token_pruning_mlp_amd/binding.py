@@ -28,7 +28,8 @@ TG_MAX_GATHER = 16
 
 EXPORTS = ("tg_status_string", "tg_abi_version", "tg_workspace_bytes", "tg_gate_score",
            "tg_select_topk", "tg_compact", "tg_rope", "tg_rope_qk", "tg_gated_attention",
-           "tg_rmsnorm", "tg_swiglu", "tg_blas_create", "tg_blas_destroy", "tg_linear")
+           "tg_rmsnorm", "tg_swiglu", "tg_blas_create", "tg_blas_destroy", "tg_linear",
+           "tg_attention_bwd_workspace_bytes", "tg_gated_attention_bwd")
 
 
 class TgGather(ctypes.Structure):
@@ -82,6 +83,11 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
     L.tg_blas_destroy.restype = ctypes.c_int
     L.tg_linear.argtypes = [P, P, P, P, P, I64, I32, I32, P]
     L.tg_linear.restype = ctypes.c_int
+    L.tg_attention_bwd_workspace_bytes.argtypes = [I64, I32, I32, I32]
+    L.tg_attention_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.tg_gated_attention_bwd.argtypes = [P, P, P, P, P, F, P, I64, I32, I32, I32, P, P, P, P, P, P, P, P,
+                                         ctypes.c_size_t, P]
+    L.tg_gated_attention_bwd.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -288,3 +294,39 @@ def tg_linear(handle: BlasHandle, x: torch.Tensor, w: torch.Tensor, residual: Op
     _need(y, "y", torch.bfloat16, (rows, out_dim))
     _check("tg_linear", load().tg_linear(handle.value, _ptr(x), _ptr(w), _ptr(residual), _ptr(y), rows, in_dim,
                                          out_dim, _stream(stream)))
+
+
+def tg_attention_bwd_workspace_bytes(n_kept: int, hq: int, hkv: int, head_dim: int) -> int:
+    return int(load().tg_attention_bwd_workspace_bytes(int(n_kept), int(hq), int(hkv), int(head_dim)))
+
+
+def tg_gated_attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_score: torch.Tensor,
+                           gains: torch.Tensor, temp_coef: float, pos: torch.Tensor, dout: torch.Tensor,
+                           dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor, dscore: torch.Tensor,
+                           dgains: torch.Tensor, dtemp: torch.Tensor, ws: Optional[torch.Tensor] = None,
+                           stream=None) -> None:
+    """Gradients of tg_gated_attention (fp32 outputs, overwritten)."""
+    nk, hq, D = q.shape
+    hkv = k.shape[1]
+    _need(q, "q", torch.bfloat16, (nk, hq, D))
+    _need(k, "k", torch.bfloat16, (nk, hkv, D))
+    _need(v, "v", torch.bfloat16, (nk, hkv, D))
+    _need(key_score, "key_score", torch.float32, (nk,))
+    _need(gains, "gains", torch.float32, (hq,))
+    _need(pos, "pos", torch.int32, (nk,))
+    _need(dout, "dout", torch.bfloat16, (nk, hq, D))
+    _need(dq, "dq", torch.float32, (nk, hq, D))
+    _need(dk, "dk", torch.float32, (nk, hkv, D))
+    _need(dv, "dv", torch.float32, (nk, hkv, D))
+    _need(dscore, "dscore", torch.float32, (nk,))
+    _need(dgains, "dgains", torch.float32, (hq,))
+    _need(dtemp, "dtemp", torch.float32, (1,))
+    if ws is None:
+        ws = torch.empty(max(1, tg_attention_bwd_workspace_bytes(nk, hq, hkv, D)), dtype=torch.uint8,
+                         device=q.device)
+    _need(ws, "ws", torch.uint8)
+    _check("tg_gated_attention_bwd", load().tg_gated_attention_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(key_score), _ptr(gains), float(temp_coef), _ptr(pos), nk, hq, hkv, D,
+        _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dscore), _ptr(dgains), _ptr(dtemp), _ptr(ws), ws.numel(),
+        _stream(stream)))
+

@@ -177,7 +177,8 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
                                                               const float* __restrict__ gains,
                                                               float temp_coef, const int32_t* __restrict__ pos,
                                                               int nk, int hq, int hkv, int npairs, int per_xcd,
-                                                              int n_items, void* __restrict__ out) {
+                                                              int n_items, void* __restrict__ out,
+                                                              float* __restrict__ lse, int lse_ld) {
     using C = AttnCfg<D, HPW, RB, NS, KB>;
     // one set of LDS objects per pipeline stage, so the compiler can see that
     // reads of one stage never alias the loads in flight into the other
@@ -295,6 +296,7 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
         float l = tgd::half_sum(l_run);  // per query (the half-waves held different keys)
         if constexpr (NS == 1) {
             store_units<D, 0, U, OUT_F32>(o, l, t, nk, hq, h, g, out);
+            if (lse && g == 0 && t < nk) lse[(int64_t)h * lse_ld + t] = m_run + __log2f(l);
         } else {
             const auto slot_ptr = [&](int slot) {
                 const int off = (hr * NS + slot) * C::SLOT_BYTES;
@@ -343,8 +345,10 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
                     m_run = mn;
                     if constexpr (s > 1)
                         self(self, KEEP, IC<s / 2>{}, x ^ s);
-                    else
+                    else {
                         store_units<D, keep, half, OUT_F32>(o, l, t, nk, hq, h, g, out);
+                        if (lse && sp == 0 && g == 0 && t < nk) lse[(int64_t)h * lse_ld + t] = m_run + __log2f(l);
+                    }
                 };
                 if (sp & s)
                     step(IC<lo + half>{});
@@ -516,7 +520,7 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
 template <int D, int HPW, int RB, int NS, int KB>
 int launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* ks, const float* gains,
                 float c, const int32_t* pos, int64_t nk, int hq, int hkv, void* out, int out_dtype,
-                hipStream_t s) {
+                float* lse, int lse_ld, hipStream_t s) {
     using C = AttnCfg<D, HPW, RB, NS, KB>;
     const int nqb = (int)((nk + C::QROWS - 1) / C::QROWS);
     const int npairs = (nqb + 1) / 2;
@@ -525,10 +529,10 @@ int launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const f
     const dim3 grid((unsigned)(per_xcd * kXcds));
     if (out_dtype == 1)
         hipLaunchKernelGGL((gated_attn<D, HPW, RB, NS, KB, true>), grid, dim3(C::THREADS), 0, s, q, k, v, ks, gains,
-                           c, pos, (int)nk, hq, hkv, npairs, per_xcd, n_items, out);
+                           c, pos, (int)nk, hq, hkv, npairs, per_xcd, n_items, out, lse, lse_ld);
     else
         hipLaunchKernelGGL((gated_attn<D, HPW, RB, NS, KB, false>), grid, dim3(C::THREADS), 0, s, q, k, v, ks, gains,
-                           c, pos, (int)nk, hq, hkv, npairs, per_xcd, n_items, out);
+                           c, pos, (int)nk, hq, hkv, npairs, per_xcd, n_items, out, lse, lse_ld);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_EDEVICE;
 }
 
@@ -546,28 +550,28 @@ inline int64_t attn_items(int64_t nk, int hq, int hkv, int hpw, int rb) {
 template <int D, int HPW>
 int launch_attn_h(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* ks, const float* gains,
                   float c, const int32_t* pos, int64_t nk, int hq, int hkv, void* out, int out_dtype,
-                  hipStream_t s) {
+                  float* lse, int lse_ld, hipStream_t s) {
     constexpr int kCUs = 256;
     constexpr int W = HPW == 1 ? 4 : 8 / HPW;  // row blocks x splits
     if constexpr (W >= 4) {
         if (attn_items(nk, hq, hkv, HPW, 4) >= kCUs)
-            return launch_attn<D, HPW, 4, W / 4, 2>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, s);
+            return launch_attn<D, HPW, 4, W / 4, 2>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, lse, lse_ld, s);
     }
     if constexpr (W >= 2) {
         if (attn_items(nk, hq, hkv, HPW, 2) >= kCUs)
-            return launch_attn<D, HPW, 2, W / 2, 2>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, s);
+            return launch_attn<D, HPW, 2, W / 2, 2>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, lse, lse_ld, s);
     }
-    return launch_attn<D, HPW, 1, W, (W >= 4 ? 1 : 2)>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, s);
+    return launch_attn<D, HPW, 1, W, (W >= 4 ? 1 : 2)>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, lse, lse_ld, s);
 }
 
 template <int D>
 int launch_attn_d(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* ks, const float* gains,
                   float c, const int32_t* pos, int64_t nk, int hq, int hkv, void* out, int out_dtype,
-                  hipStream_t s) {
+                  float* lse, int lse_ld, hipStream_t s) {
     const int G = hq / hkv;
-    if (G % 4 == 0) return launch_attn_h<D, 4>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, s);
-    if (G % 2 == 0) return launch_attn_h<D, 2>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, s);
-    return launch_attn_h<D, 1>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, s);
+    if (G % 4 == 0) return launch_attn_h<D, 4>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, lse, lse_ld, s);
+    if (G % 2 == 0) return launch_attn_h<D, 2>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, lse, lse_ld, s);
+    return launch_attn_h<D, 1>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, lse, lse_ld, s);
 }
 
 }  // namespace
@@ -577,13 +581,13 @@ namespace tgi {
 int launch_gated_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                            const float* key_score, const float* gains, float temp_coef,
                            const int32_t* pos, int64_t n_kept, int hq, int hkv, int head_dim,
-                           void* out, int out_dtype, void* stream) {
+                           void* out, int out_dtype, float* lse, int lse_ld, void* stream) {
     hipStream_t s = (hipStream_t)stream;
     switch (head_dim) {
         case 64:
-            return launch_attn_d<64>(q, k, v, key_score, gains, temp_coef, pos, n_kept, hq, hkv, out, out_dtype, s);
+            return launch_attn_d<64>(q, k, v, key_score, gains, temp_coef, pos, n_kept, hq, hkv, out, out_dtype, lse, lse_ld, s);
         case 128:
-            return launch_attn_d<128>(q, k, v, key_score, gains, temp_coef, pos, n_kept, hq, hkv, out, out_dtype, s);
+            return launch_attn_d<128>(q, k, v, key_score, gains, temp_coef, pos, n_kept, hq, hkv, out, out_dtype, lse, lse_ld, s);
         default:
             return TG_EUNSUPPORTED;
     }

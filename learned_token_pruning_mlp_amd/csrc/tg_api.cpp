@@ -133,7 +133,34 @@ int tg_gated_attention(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, con
         !aligned(gains, 4) || !aligned(pos, 4))
         return TG_EALIGN;
     return tgi::launch_gated_attention(q, k, v, key_score, gains, temp_coef, pos, n_kept, hq, hkv, head_dim, out,
-                                       out_dtype, stream);
+                                       out_dtype, nullptr, 0, stream);
+}
+
+size_t tg_attention_bwd_workspace_bytes(int64_t n_kept, int32_t hq, int32_t hkv, int32_t head_dim) {
+    if (n_kept < 0 || hq < 1 || hkv < 1 || head_dim < 1) return 0;
+    return tgi::attn_bwd_ws_bytes(n_kept, hq, hkv, head_dim);
+}
+
+int tg_gated_attention_bwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, const float* key_score,
+                           const float* gains, float temp_coef, const int32_t* pos, int64_t n_kept, int32_t hq,
+                           int32_t hkv, int32_t head_dim, const tg_bf16* dout, float* dq, float* dk, float* dv,
+                           float* dscore, float* dgains, float* dtemp, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    if (n_kept < 0 || n_kept > kMaxRows || hq < 1 || hkv < 1 || hq % hkv != 0) return TG_EINVAL;
+    if (!(temp_coef == temp_coef) || temp_coef > 3.4e38f || temp_coef < -3.4e38f) return TG_EINVAL;
+    if (head_dim != 64 && head_dim != 128) return TG_EUNSUPPORTED;
+    if (n_kept * (int64_t)hkv * head_dim * 2 >= (int64_t)1 << 31) return TG_EUNSUPPORTED;
+    if (n_kept * (int64_t)hq * head_dim * 4 >= (int64_t)1 << 40) return TG_EUNSUPPORTED;
+    if (n_kept == 0) return TG_OK;
+    if (!q || !k || !v || !key_score || !gains || !pos || !dout || !dq || !dk || !dv || !dscore || !dgains || !dtemp)
+        return TG_EINVAL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) || !aligned(dq, 16) ||
+        !aligned(dk, 16) || !aligned(dv, 16))
+        return TG_EALIGN;
+    if (!workspace || workspace_bytes < tgi::attn_bwd_ws_bytes(n_kept, hq, hkv, head_dim)) return TG_EWORKSPACE;
+    if (!aligned(workspace, 256)) return TG_EALIGN;
+    return tgi::launch_gated_attention_bwd(q, k, v, key_score, gains, temp_coef, pos, n_kept, hq, hkv, head_dim, dout,
+                                           dq, dk, dv, dscore, dgains, dtemp, workspace, stream);
 }
 
 int tg_rmsnorm(const tg_bf16* x, const tg_bf16* weight, tg_bf16* y, int64_t rows, int32_t dim, float eps,

@@ -52,7 +52,57 @@ int launch_rope_qk(uint16_t* q, uint16_t* k, const int32_t* pos, int64_t rows, i
 int launch_gated_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                            const float* key_score, const float* gains, float temp_coef,
                            const int32_t* pos, int64_t n_kept, int hq, int hkv, int head_dim,
-                           void* out, int out_dtype, void* stream);
+                           void* out, int out_dtype, float* lse, int lse_ld, void* stream);
+
+// Workspace of the attention backward (fp32 arrays; row arrays padded to kp =
+// n_kept rounded up to 32 rows): the recomputed forward output [n, hq, D], the
+// per-row log2-sum-exp2 [hq, kp], D_t = dO.O [hq, kp], lambda_t and its exp2
+// scale [kp], per-row partials of dc and dg [hq, kp], per-key partials of ds
+// [hkv, kp].
+struct AttnBwdWs {
+    float* out;
+    float* lse;
+    float* dvec;
+    float* lam;
+    float* acoef;
+    float* dlamc;
+    float* dgp;
+    float* dsp;
+    int kp;
+};
+inline int64_t attn_bwd_kp(int64_t n) { return (n + 31) / 32 * 32; }
+inline size_t attn_bwd_ws_bytes(int64_t n, int hq, int hkv, int d) {
+    const size_t kp = (size_t)attn_bwd_kp(n);
+    return align_up(sizeof(float) * (size_t)n * hq * d) + 4 * align_up(sizeof(float) * hq * kp) +
+           2 * align_up(sizeof(float) * kp) + align_up(sizeof(float) * hkv * kp);
+}
+inline AttnBwdWs attn_bwd_ws(void* base, int64_t n, int hq, int hkv, int d) {
+    const size_t kp = (size_t)attn_bwd_kp(n);
+    char* p = (char*)base;
+    AttnBwdWs w;
+    w.kp = (int)kp;
+    w.out = (float*)p;
+    p += align_up(sizeof(float) * (size_t)n * hq * d);
+    w.lse = (float*)p;
+    p += align_up(sizeof(float) * hq * kp);
+    w.dvec = (float*)p;
+    p += align_up(sizeof(float) * hq * kp);
+    w.dlamc = (float*)p;
+    p += align_up(sizeof(float) * hq * kp);
+    w.dgp = (float*)p;
+    p += align_up(sizeof(float) * hq * kp);
+    w.lam = (float*)p;
+    p += align_up(sizeof(float) * kp);
+    w.acoef = (float*)p;
+    p += align_up(sizeof(float) * kp);
+    w.dsp = (float*)p;
+    return w;
+}
+
+int launch_gated_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* key_score,
+                               const float* gains, float temp_coef, const int32_t* pos, int64_t n_kept, int hq,
+                               int hkv, int head_dim, const uint16_t* dout, float* dq, float* dk, float* dv,
+                               float* dscore, float* dgains, float* dtemp, void* workspace, void* stream);
 
 int launch_rmsnorm(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t rows, int dim, float eps,
                    void* stream);
