@@ -239,6 +239,7 @@ def main():
 
     sweep = None if args.no_attn_sweep else attn_sweep(tg, torch, dev, shp)
     prefill = None if (args.no_prefill or args.workload != "n16k") else prefill_compare(tg, torch, dev, shp, seed)
+    backward = None if (args.no_attn_sweep or args.workload != "n16k") else attn_backward(tg, torch, dev, shp)
 
     result = {
         "metric": METRIC,
@@ -264,6 +265,7 @@ def main():
         "roofline": roof,
         "attn_sweep": sweep,
         "prefill": prefill,
+        "attn_backward": backward,
         "cpu_baseline": None,
     }
 
@@ -337,6 +339,44 @@ def prefill_compare(tg, torch, dev, shp, seed, n_layers=28, gate_layer=1, reps=3
             "full_tflops": round(full_flop / (full_ms * 1e-3) / 1e12, 1),
             "gated_tflops": round(gated_flop / (gated_ms * 1e-3) / 1e12, 1),
             "weights": "synthetic, one set per layer", "reps": reps}
+
+
+def attn_backward(tg, torch, dev, shp, ks=(2048, 8192), reps=5):
+    """tg_gated_attention_bwd alone (it recomputes the forward inside) at the
+    Qwen3-1.7B head shape; algorithmic work 2.5x the forward's (five products
+    of 2 D FLOP per visible (query, key) pair and head)."""
+    out = {}
+    for k in ks:
+        g = torch.Generator(device=dev)
+        g.manual_seed(k)
+        bf = lambda *s: torch.randn(*s, generator=g, device=dev).to(torch.bfloat16)  # noqa: E731
+        q, kk, vv, do = bf(k, shp.hq, shp.head_dim), bf(k, shp.hkv, shp.head_dim), bf(k, shp.hkv, shp.head_dim), \
+            bf(k, shp.hq, shp.head_dim)
+        ks_ = torch.randn(k, generator=g, device=dev)
+        gains = torch.rand(shp.hq, generator=g, device=dev) + 0.5
+        pos = torch.arange(k, dtype=torch.int32, device=dev) * 4
+        f32 = dict(dtype=torch.float32, device=dev)
+        o = [torch.empty(k, shp.hq, shp.head_dim, **f32), torch.empty(k, shp.hkv, shp.head_dim, **f32),
+             torch.empty(k, shp.hkv, shp.head_dim, **f32), torch.empty(k, **f32), torch.empty(shp.hq, **f32),
+             torch.empty(1, **f32)]
+        ws = torch.empty(tg.tg_attention_bwd_workspace_bytes(k, shp.hq, shp.hkv, shp.head_dim), dtype=torch.uint8,
+                         device=dev)
+
+        def run():
+            tg.tg_gated_attention_bwd(q, kk, vv, ks_, gains, 0.1, pos, do, *o, ws=ws)
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        flop = 2.5 * 4 * shp.hq * shp.head_dim * k * (k + 1) / 2
+        out[str(k)] = {"us": round(us, 1), "tflops": round(flop / us / 1e6, 1),
+                       "frac": round(flop / us / 1e6 / PEAK_BF16_TFLOPS, 4)}
+    return out
 
 
 def attn_sweep(tg, torch, dev, shp, ks=(4096, 8192, 16384), reps=10):

@@ -43,6 +43,7 @@ using tgd::u32x4;
 
 #define TG_LDS __attribute__((address_space(3)))
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+typedef float lf4 __attribute__((ext_vector_type(4)));  // LDS-side float4
 
 constexpr int kWavesPerBlock = 4;
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -67,23 +68,6 @@ struct Geo {
     static constexpr int QS = D / 16;  // k-steps over head_dim
     static constexpr int DB = D / 32;  // 32-row blocks of head_dim
 };
-
-// 32 rows (row0 .. row0+31, rows past nrows as zeros) of a [rows, heads, D]
-// bf16 tensor, head hh, into a wave's LDS block with swizzled pieces.
-template <int D>
-__device__ __forceinline__ void stage_rows(const uint16_t* __restrict__ src, int heads, int hh, int row0, int nrows,
-                                           TG_LDS uint8_t* blk, int lane) {
-    using G = Geo<D>;
-#pragma unroll
-    for (int it = 0; it < G::PIECES / 2; ++it) {
-        const int e = it * 64 + lane;
-        const int r = e / G::PIECES, c = e % G::PIECES;
-        const int row = row0 + r;
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (row < nrows) v = *reinterpret_cast<const u32x4*>(src + ((int64_t)row * heads + hh) * D + 8 * c);
-        *reinterpret_cast<TG_LDS u32x4*>(blk + r * G::ROW_BYTES + 16 * (c ^ swz<G::PIECES>(r))) = v;
-    }
-}
 
 // Row-major operand of a product over head_dim (lane holds 8 consecutive
 // values of row l32 at k-step s, half g) from an LDS block.
@@ -132,37 +116,86 @@ __device__ __forceinline__ void pack_b(const f32x16& x, u32x4 (&b)[2]) {
     for (int i = 0; i < 16; i += 2) b[i >> 3][(i & 7) >> 1] = tgd::cvt_pk_bf16(x[i], x[i + 1]);
 }
 
-// ---- per-row values: D_t = dO_t . O_t, lambda_t, a_t
+// ---- per-(head, row) values packed for the two passes: a_t, the forward's
+// lse, D_t = dO_t . O_t and lambda_t (rows past the last one: zeros)
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep(const float* __restrict__ O, const uint16_t* __restrict__ dO,
-                                                const int32_t* __restrict__ pos, float temp_coef, int nk, int hq,
-                                                int kp, float* __restrict__ dvec, float* __restrict__ lam,
-                                                float* __restrict__ acoef) {
-    const int lane = threadIdx.x & 63;
-    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // row = t * hq + h
-    if (r >= (int64_t)nk * hq) return;
-    const int t = (int)(r / hq), h = (int)(r % hq);
+                                                const float* __restrict__ lse, const int32_t* __restrict__ pos,
+                                                float temp_coef, int nk, int hq, int kp, float4* __restrict__ rowv) {
+    constexpr int LPR = D / 8;        // lanes per (head, row): 8 values each
+    constexpr int RPB = 256 / LPR;    // (head, row) pairs per workgroup
+    const int tid = threadIdx.x, sub = tid % LPR;
+    const int64_t rr = (int64_t)blockIdx.x * RPB + tid / LPR;  // h * kp + t
+    if (rr >= (int64_t)hq * kp) return;
+    const int h = (int)(rr / kp), t = (int)(rr % kp);
     float acc = 0.0f;
-    for (int d = lane; d < D; d += 64) acc = fmaf(O[r * D + d], tgd::bf16lo(dO[r * D + d]), acc);
-    acc = tgd::wave_sum(acc);
-    if (lane == 0) {
-        dvec[(int64_t)h * kp + t] = acc;
-        if (h == 0) {
+    if (t < nk) {
+        const int64_t off = ((int64_t)t * hq + h) * D + 8 * sub;
+        const float4 o0 = *reinterpret_cast<const float4*>(O + off);
+        const float4 o1 = *reinterpret_cast<const float4*>(O + off + 4);
+        const u32x4 d = *reinterpret_cast<const u32x4*>(dO + off);
+        acc = o0.x * tgd::bf16lo(d[0]) + o0.y * tgd::bf16hi(d[0]) + o0.z * tgd::bf16lo(d[1]) +
+              o0.w * tgd::bf16hi(d[1]) + o1.x * tgd::bf16lo(d[2]) + o1.y * tgd::bf16hi(d[2]) +
+              o1.z * tgd::bf16lo(d[3]) + o1.w * tgd::bf16hi(d[3]);
+    }
+#pragma unroll
+    for (int o = LPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (sub == 0) {
+        float4 out = float4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (t < nk) {
             const float l = 1.0f + temp_coef * logf((float)(t + 1) / ((float)pos[t] + 1.0f));
-            lam[t] = l;
-            acoef[t] = l * kLog2e * (1.0f / sqrtf((float)D));
+            out = float4{l * kLog2e * (1.0f / sqrtf((float)D)), lse[(int64_t)h * kp + t], acc, l};
         }
+        rowv[rr] = out;
     }
 }
 
-// ---- dq, and the per-row partials of dlambda and of sum_j dU_tj s_j
+// Register copy of this lane's pieces of a 32-row block: fetched one block
+// ahead, written to LDS when its turn comes.  Rows past nrows repeat the last
+// row; everything they feed is masked by the causal test.
+template <int D>
+struct Rows {
+    u32x4 p[Geo<D>::PIECES / 2];
+};
+
+template <int D>
+__device__ __forceinline__ void fetch_rows(const uint16_t* __restrict__ src, int heads, int hh, int row0, int nrows,
+                                           Rows<D>& st, int lane) {
+    using G = Geo<D>;
+#pragma unroll
+    for (int it = 0; it < G::PIECES / 2; ++it) {
+        const int e = it * 64 + lane;
+        const int row = min(row0 + e / G::PIECES, nrows - 1);
+        st.p[it] = *reinterpret_cast<const u32x4*>(src + ((int64_t)row * heads + hh) * D + 8 * (e % G::PIECES));
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void put_rows(const Rows<D>& st, TG_LDS uint8_t* blk, int lane) {
+    using G = Geo<D>;
+#pragma unroll
+    for (int it = 0; it < G::PIECES / 2; ++it) {
+        const int e = it * 64 + lane;
+        const int r = e / G::PIECES, c = e % G::PIECES;
+        *reinterpret_cast<TG_LDS u32x4*>(blk + r * G::ROW_BYTES + 16 * (c ^ swz<G::PIECES>(r))) = st.p[it];
+    }
+}
+
+// Compiler-level memory fence: keeps a wave's LDS writes of the next block
+// after its reads of the current one (LDS runs one wave's accesses in order).
+// The prefetched sources are plain (not __restrict__) pointers: loads through
+// a restrict read-only argument count as invariant, and the compiler would
+// move them past the fence to where their values are used, undoing the
+// prefetch.
+#define TG_CFENCE() asm volatile("" ::: "memory")
+
+// ---- dq, and per-(head, query block) partials of dlambda and of sum dU s
 template <int D>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void bwd_dq(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ key_score, const float* __restrict__ gains, const int32_t* __restrict__ pos,
-    const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ dvec,
-    const float* __restrict__ lam, const float* __restrict__ acoef, int nk, int hq, int hkv, int kp,
-    float* __restrict__ dq, float* __restrict__ dlamc, float* __restrict__ dgp) {
+    const uint16_t* __restrict__ q, const uint16_t* k, const uint16_t* v, const float* key_score,
+    const float* __restrict__ gains, const int32_t* __restrict__ pos, const uint16_t* __restrict__ dO,
+    const float4* __restrict__ rowv, int nk, int hq, int hkv, int kp, float* __restrict__ dq,
+    float* __restrict__ dlamc, float* __restrict__ dgp) {
     using G = Geo<D>;
     __shared__ __attribute__((aligned(1024))) uint8_t sK[kWavesPerBlock][G::BLOCK_BYTES];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -170,7 +203,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void bwd_dq(
     const int nqb = (nk + 31) / 32;
     const int item = blockIdx.x * kWavesPerBlock + w;
     if (item >= hq * nqb) return;
-    const int h = item / nqb, qb = item % nqb;
+    // the longest walks (last query blocks) first
+    const int qb = nqb - 1 - item / hq, h = item % hq;
     const int hk = h / (hq / hkv);
     const int t = qb * 32 + l32;
     const bool ok = t < nk;
@@ -184,41 +218,51 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void bwd_dq(
         qreg[s] = global_operand<D>(q, hq, h, t, nk, g, s);
         doreg[s] = global_operand<D>(dO, hq, h, t, nk, g, s);
     }
-    const float a_t = ok ? acoef[t] : 0.0f;
-    const float lse_t = ok ? lse[(int64_t)h * kp + t] : 0.0f;
-    const float d_t = ok ? dvec[(int64_t)h * kp + t] : 0.0f;
-    const float lam_t = ok ? lam[t] : 0.0f;
+    const float4 rv = rowv[(int64_t)h * kp + t];  // t < kp
+    const float a_t = rv.x, lse_t = rv.y, d_t = rv.z, lam_t = rv.w;
 
     f32x16 dqa[G::DB];
 #pragma unroll
     for (int db = 0; db < G::DB; ++db) dqa[db] = f32x16{};
     float dl = 0.0f, dgs = 0.0f;
 
+    // block kb's K rows (for LDS), V operand and key scores, one block ahead;
+    // this lane's 16 key rows of the accumulators are j0 + 8 (i/4) + 4 g + i%4
+    Rows<D> kst;
+    u32x4 vn[G::QS];
+    float svn[16];
+    auto fetch = [&](int kb) {
+        const int j0 = kb * 32;
+        fetch_rows<D>(k, hkv, hk, j0, nk, kst, lane);
+        const int jr = min(j0 + l32, nk - 1);
+#pragma unroll
+        for (int s = 0; s < G::QS; ++s)
+            vn[s] = *reinterpret_cast<const u32x4*>(v + ((int64_t)jr * hkv + hk) * D + 16 * s + 8 * g);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) svn[i] = key_score[min(j0 + 8 * (i >> 2) + 4 * g + (i & 3), nk - 1)];
+    };
+    fetch(0);
+
     for (int kb = 0; kb <= qb; ++kb) {
         const int j0 = kb * 32;
-        // (one wave writes and reads its own LDS block; LDS executes a wave's
-        // instructions in order, the barriers keep the compiler from moving
-        // reads across the writes)
-        __builtin_amdgcn_wave_barrier();
-        stage_rows<D>(k, hkv, hk, j0, nk, blk, lane);
-        __builtin_amdgcn_wave_barrier();
-        // this lane's 16 key rows of the accumulators: j0 + 8 (i/4) + 4 g + i%4
+        u32x4 vc[G::QS];
         float sv[16];
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
+        for (int s = 0; s < G::QS; ++s) vc[s] = vn[s];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int j = j0 + 8 * i4 + 4 * g + e;
-                sv[4 * i4 + e] = j < nk ? key_score[j] : 0.0f;
-            }
-        }
+        for (int i = 0; i < 16; ++i) sv[i] = svn[i];
+        TG_CFENCE();
+        put_rows<D>(kst, blk, lane);
+        fetch(min(kb + 1, qb));  // issued before the products below, not sunk past the fence
+        TG_CFENCE();
+
         f32x16 sacc, dpacc = f32x16{};
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[i] = sg * sv[i];
 #pragma unroll
         for (int s = 0; s < G::QS; ++s) {
             sacc = tgd::mfma32(row_operand<D>(blk, l32, g, s), qreg[s], sacc);
-            dpacc = tgd::mfma32(global_operand<D>(v, hkv, hk, j0 + l32, nk, g, s), doreg[s], dpacc);
+            dpacc = tgd::mfma32(vc[s], doreg[s], dpacc);
         }
         f32x16 du;
 #pragma unroll
@@ -248,123 +292,205 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void bwd_dq(
                 float4{dqa[u / 4][i] * rs, dqa[u / 4][i + 1] * rs, dqa[u / 4][i + 2] * rs, dqa[u / 4][i + 3] * rs};
         }
     }
-    dl = tgd::half_sum(dl);
-    dgs = tgd::half_sum(dgs);
-    if (ok && g == 0) {
-        dlamc[(int64_t)h * kp + t] = dl * logf((float)(t + 1) / ((float)pos[t] + 1.0f));
-        dgp[(int64_t)h * kp + t] = dgs;
+    // block partials: both halves of a row carry the same log ratio
+    const float lr = ok ? logf((float)(t + 1) / ((float)pos[t] + 1.0f)) : 0.0f;
+    const float xl = tgd::wave_sum(dl * lr);
+    const float xg = tgd::wave_sum(dgs);
+    if (lane == 0) {
+        dlamc[(int64_t)h * nqb + qb] = xl;
+        dgp[(int64_t)h * nqb + qb] = xg;
     }
 }
 
 // ---- dk, dv, and the per-key partial of ds (this kv head's q heads)
+// A workgroup holds kWavesPerBlock / wsplit key blocks; the wsplit waves of a
+// key block share its q heads (wave r takes heads r, r + wsplit, ...) and
+// their partial sums are added in LDS in the order r = 0, 1, ...
 template <int D>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void bwd_dkv(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ key_score, const float* __restrict__ gains, const uint16_t* __restrict__ dO,
-    const float* __restrict__ lse, const float* __restrict__ dvec, const float* __restrict__ lam,
-    const float* __restrict__ acoef, int nk, int hq, int hkv, int kp, float* __restrict__ dk,
+    const uint16_t* q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ key_score, const float* gains, const uint16_t* dO,
+    const float4* rowv, int nk, int hq, int hkv, int kp, int wsplit, float* __restrict__ dk,
     float* __restrict__ dv, float* __restrict__ dsp) {
     using G = Geo<D>;
-    __shared__ __attribute__((aligned(1024))) uint8_t sQ[kWavesPerBlock][G::BLOCK_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t sO[kWavesPerBlock][G::BLOCK_BYTES];
+    constexpr int SLOT = 2 * G::BLOCK_BYTES + 512;  // Q block, dO block, 32 row values
+    constexpr int XCH = G::DB * 16 * 64 * 4;        // one wave's accumulator set, bytes
+    static_assert(3 * XCH <= kWavesPerBlock * SLOT, "exchange fits the staging memory");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kWavesPerBlock * SLOT];
+    __shared__ float sds[kWavesPerBlock][64];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int l32 = lane & 31, g = lane >> 5;
-    const int nkb = (nk + 31) / 32;
-    const int item = blockIdx.x * kWavesPerBlock + w;
-    if (item >= hkv * nkb) return;
-    const int hk = item / nkb, kb = item % nkb;
     const int grp = hq / hkv;
+    const int W = wsplit, S = kWavesPerBlock / wsplit;
+    const int sidx = w / W, r = w % W;
+    const int nkb = (nk + 31) / 32;
+    const int hk = blockIdx.x % hkv;
+    const int kb = (int)(blockIdx.x / hkv) * S + sidx;  // the longest walks (first key blocks) first
+    const bool valid = kb < nkb;
     const int j = kb * 32 + l32;  // this lane's key column
+    const int jc = min(j, nk - 1);
     const float rs = 1.0f / sqrtf((float)D);
-    TG_LDS uint8_t* bq = (TG_LDS uint8_t*)sQ[w];
-    TG_LDS uint8_t* bo = (TG_LDS uint8_t*)sO[w];
+    TG_LDS uint8_t* bq = (TG_LDS uint8_t*)smem + w * SLOT;
+    TG_LDS uint8_t* bo = bq + G::BLOCK_BYTES;
+    TG_LDS lf4* brow = (TG_LDS lf4*)(bo + G::BLOCK_BYTES);
 
     u32x4 kreg[G::QS], vreg[G::QS];
 #pragma unroll
     for (int s = 0; s < G::QS; ++s) {
-        kreg[s] = global_operand<D>(k, hkv, hk, j, nk, g, s);
-        vreg[s] = global_operand<D>(v, hkv, hk, j, nk, g, s);
+        kreg[s] = *reinterpret_cast<const u32x4*>(k + ((int64_t)jc * hkv + hk) * D + 16 * s + 8 * g);
+        vreg[s] = *reinterpret_cast<const u32x4*>(v + ((int64_t)jc * hkv + hk) * D + 16 * s + 8 * g);
     }
-    const float sj = j < nk ? key_score[j] : 0.0f;
+    const float sj = key_score[jc];
     f32x16 dka[G::DB], dva[G::DB];
 #pragma unroll
     for (int db = 0; db < G::DB; ++db) dka[db] = dva[db] = f32x16{};
     float dsj = 0.0f;
-    const int nqb = (nk + 31) / 32;
 
-    for (int hh = 0; hh < grp; ++hh) {
+    // (head, query block) pairs of this wave: heads r, r + W, ..., query blocks kb .. nkb-1
+    const int nq = valid ? nkb - kb : 0;
+    const int nh = valid ? (grp - r + W - 1) / W : 0;
+    const int iters = nq * nh;
+    Rows<D> qst, ost;
+    float4 rown = float4{0.0f, 0.0f, 0.0f, 0.0f};
+    float ghn = 0.0f;
+    auto fetch = [&](int hh, int qb) {
         const int h = hk * grp + hh;
-        const float gh = gains[h];
+        fetch_rows<D>(q, hq, h, qb * 32, nk, qst, lane);
+        fetch_rows<D>(dO, hq, h, qb * 32, nk, ost, lane);
+        rown = rowv[(int64_t)h * kp + qb * 32 + l32];
+        ghn = gains[h];
+    };
+    int hh = r, qb = kb;
+    if (iters > 0) fetch(hh, qb);
+
+    for (int it = 0; it < iters; ++it) {
+        const int t0 = qb * 32;
+        const float gh = ghn;
+        int hn = hh, qn = qb + 1;
+        if (qn == nkb) {
+            qn = kb;
+            hn = hh + W;
+        }
+        if (it + 1 == iters) {  // nothing left: fetch the current pair again
+            hn = hh;
+            qn = qb;
+        }
+        TG_CFENCE();
+        put_rows<D>(qst, bq, lane);
+        put_rows<D>(ost, bo, lane);
+        if (lane < 32) brow[lane] = lf4{rown.x, rown.y, rown.z, rown.w};
+        fetch(hn, qn);  // issued before the products below, not sunk past the fence
+        TG_CFENCE();
+
+        // this lane's 16 query rows: t0 + 8 (i/4) + 4 g + i%4
+        float ar[16], lr[16], dr[16], mr[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const lf4 x = brow[8 * (i >> 2) + 4 * g + (i & 3)];
+            ar[i] = x.x, lr[i] = x.y, dr[i] = x.z, mr[i] = x.w;
+        }
         const float bias = sqrtf((float)D) * gh * sj;
-        for (int qb = kb; qb < nqb; ++qb) {
-            const int t0 = qb * 32;
-            __builtin_amdgcn_wave_barrier();
-            stage_rows<D>(q, hq, h, t0, nk, bq, lane);
-            stage_rows<D>(dO, hq, h, t0, nk, bo, lane);
-            __builtin_amdgcn_wave_barrier();
-            // this lane's 16 query rows: t0 + 8 (i/4) + 4 g + i%4 (arrays padded to 32 rows)
-            float ar[16], lr[16], dr[16], mr[16];
+        f32x16 sacc, dpacc = f32x16{};
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const int tr = t0 + 8 * i4 + 4 * g;
-                const float4 a4 = *reinterpret_cast<const float4*>(acoef + tr);
-                const float4 l4 = *reinterpret_cast<const float4*>(lse + (int64_t)h * kp + tr);
-                const float4 d4 = *reinterpret_cast<const float4*>(dvec + (int64_t)h * kp + tr);
-                const float4 m4 = *reinterpret_cast<const float4*>(lam + tr);
-                ar[4 * i4] = a4.x, ar[4 * i4 + 1] = a4.y, ar[4 * i4 + 2] = a4.z, ar[4 * i4 + 3] = a4.w;
-                lr[4 * i4] = l4.x, lr[4 * i4 + 1] = l4.y, lr[4 * i4 + 2] = l4.z, lr[4 * i4 + 3] = l4.w;
-                dr[4 * i4] = d4.x, dr[4 * i4 + 1] = d4.y, dr[4 * i4 + 2] = d4.z, dr[4 * i4 + 3] = d4.w;
-                mr[4 * i4] = m4.x, mr[4 * i4 + 1] = m4.y, mr[4 * i4 + 2] = m4.z, mr[4 * i4 + 3] = m4.w;
-            }
-            f32x16 sacc, dpacc = f32x16{};
+        for (int i = 0; i < 16; ++i) sacc[i] = bias;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sacc[i] = bias;
+        for (int s = 0; s < G::QS; ++s) {
+            sacc = tgd::mfma32(row_operand<D>(bq, l32, g, s), kreg[s], sacc);
+            dpacc = tgd::mfma32(row_operand<D>(bo, l32, g, s), vreg[s], dpacc);
+        }
+        f32x16 p, du;
 #pragma unroll
-            for (int s = 0; s < G::QS; ++s) {
-                sacc = tgd::mfma32(row_operand<D>(bq, l32, g, s), kreg[s], sacc);
-                dpacc = tgd::mfma32(row_operand<D>(bo, l32, g, s), vreg[s], dpacc);
-            }
-            f32x16 p, du;
+        for (int i = 0; i < 16; ++i) {
+            const int t = t0 + 8 * (i >> 2) + 4 * g + (i & 3);
+            const bool vis = t < nk && j <= t;
+            p[i] = vis ? __builtin_amdgcn_exp2f(fmaf(ar[i], sacc[i], -lr[i])) : 0.0f;
+            du[i] = vis ? mr[i] * p[i] * (dpacc[i] - dr[i]) : 0.0f;
+            dsj = fmaf(gh, du[i], dsj);
+        }
+        u32x4 pp[2], pu[2];
+        pack_b(p, pp);
+        pack_b(du, pu);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int t = t0 + 8 * (i >> 2) + 4 * g + (i & 3);
-                const bool vis = t < nk && j <= t;
-                // (rows past the last query read the padding of the row arrays: never used)
-                p[i] = vis ? __builtin_amdgcn_exp2f(fmaf(ar[i], sacc[i], -lr[i])) : 0.0f;
-                du[i] = vis ? mr[i] * p[i] * (dpacc[i] - dr[i]) : 0.0f;
-                dsj = fmaf(gh, du[i], dsj);
-            }
-            u32x4 pp[2], pu[2];
-            pack_b(p, pp);
-            pack_b(du, pu);
+        for (int s = 0; s < 2; ++s) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-#pragma unroll
-                for (int db = 0; db < G::DB; ++db) {
-                    dva[db] = tgd::mfma32(tr_operand<D>(bo, lane, db, s), pp[s], dva[db]);
-                    dka[db] = tgd::mfma32(tr_operand<D>(bq, lane, db, s), pu[s], dka[db]);
-                }
+            for (int db = 0; db < G::DB; ++db) {
+                dva[db] = tgd::mfma32(tr_operand<D>(bo, lane, db, s), pp[s], dva[db]);
+                dka[db] = tgd::mfma32(tr_operand<D>(bq, lane, db, s), pu[s], dka[db]);
             }
         }
-    }
-    if (j < nk) {
-#pragma unroll
-        for (int u = 0; u < 4 * G::DB; ++u) {
-            const int i = 4 * (u % 4);
-            const int dd = (u / 4) * 32 + 8 * (u % 4) + 4 * g;
-            const int64_t off = ((int64_t)j * hkv + hk) * D + dd;
-            *reinterpret_cast<float4*>(dk + off) =
-                float4{dka[u / 4][i] * rs, dka[u / 4][i + 1] * rs, dka[u / 4][i + 2] * rs, dka[u / 4][i + 3] * rs};
-            *reinterpret_cast<float4*>(dv + off) = float4{dva[u / 4][i], dva[u / 4][i + 1], dva[u / 4][i + 2],
-                                                          dva[u / 4][i + 3]};
-        }
+        hh = hn;
+        qb = qn;
     }
     dsj = tgd::half_sum(dsj);
-    if (j < nk && g == 0) dsp[(int64_t)hk * kp + j] = dsj;
+
+    // add the head-split partials: slot of wave (sidx, r >= 1) = sidx * (W - 1) + r - 1
+    TG_LDS lf4* xs = (TG_LDS lf4*)smem;
+    const int slot = sidx * (W - 1) + r - 1;
+    __syncthreads();
+    if (r > 0) {
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4)
+                xs[slot * (XCH / 16) + (db * 4 + i4) * 64 + lane] =
+                    lf4{dka[db][4 * i4], dka[db][4 * i4 + 1], dka[db][4 * i4 + 2], dka[db][4 * i4 + 3]};
+        sds[w][lane] = dsj;
+    }
+    __syncthreads();
+    if (r == 0) {
+        for (int rr = 1; rr < W; ++rr) {
+            const int sl = sidx * (W - 1) + rr - 1;
+#pragma unroll
+            for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const lf4 x = xs[sl * (XCH / 16) + (db * 4 + i4) * 64 + lane];
+                    dka[db][4 * i4] += x.x, dka[db][4 * i4 + 1] += x.y, dka[db][4 * i4 + 2] += x.z,
+                        dka[db][4 * i4 + 3] += x.w;
+                }
+            dsj += sds[w + rr][lane];
+        }
+    }
+    __syncthreads();
+    if (r > 0) {
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4)
+                xs[slot * (XCH / 16) + (db * 4 + i4) * 64 + lane] =
+                    lf4{dva[db][4 * i4], dva[db][4 * i4 + 1], dva[db][4 * i4 + 2], dva[db][4 * i4 + 3]};
+    }
+    __syncthreads();
+    if (r == 0) {
+        for (int rr = 1; rr < W; ++rr) {
+            const int sl = sidx * (W - 1) + rr - 1;
+#pragma unroll
+            for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const lf4 x = xs[sl * (XCH / 16) + (db * 4 + i4) * 64 + lane];
+                    dva[db][4 * i4] += x.x, dva[db][4 * i4 + 1] += x.y, dva[db][4 * i4 + 2] += x.z,
+                        dva[db][4 * i4 + 3] += x.w;
+                }
+        }
+        if (valid && j < nk) {
+#pragma unroll
+            for (int u = 0; u < 4 * G::DB; ++u) {
+                const int i = 4 * (u % 4);
+                const int dd = (u / 4) * 32 + 8 * (u % 4) + 4 * g;
+                const int64_t off = ((int64_t)j * hkv + hk) * D + dd;
+                *reinterpret_cast<float4*>(dk + off) = float4{dka[u / 4][i] * rs, dka[u / 4][i + 1] * rs,
+                                                              dka[u / 4][i + 2] * rs, dka[u / 4][i + 3] * rs};
+                *reinterpret_cast<float4*>(dv + off) =
+                    float4{dva[u / 4][i], dva[u / 4][i + 1], dva[u / 4][i + 2], dva[u / 4][i + 3]};
+            }
+            if (g == 0) dsp[(int64_t)hk * kp + j] = dsj;
+        }
+    }
 }
 
-// ---- fixed-order sums: dscore[j] over the kv heads; dgains[h] over the rows;
-// dtemp over heads and rows (workgroup hq)
+// ---- fixed-order sums: dscore[j] over the kv heads; dgains[h] over the query
+// blocks; dtemp over heads and query blocks (workgroup hq)
 __global__ __launch_bounds__(256) void bwd_reduce_score(const float* __restrict__ dsp, int nk, int hkv, int kp,
                                                         float* __restrict__ dscore) {
     const int j = blockIdx.x * 256 + threadIdx.x;
@@ -375,18 +501,16 @@ __global__ __launch_bounds__(256) void bwd_reduce_score(const float* __restrict_
 }
 
 __global__ __launch_bounds__(256) void bwd_reduce_rows(const float* __restrict__ dgp, const float* __restrict__ dlamc,
-                                                       int nk, int hq, int kp, float* __restrict__ dgains,
+                                                       int nqb, int hq, float* __restrict__ dgains,
                                                        float* __restrict__ dtemp) {
     __shared__ double red[4];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int b = blockIdx.x;  // 0 .. hq-1: gains; hq: temperature
+    const float* src = b < hq ? dgp + (int64_t)b * nqb : dlamc;
+    const int n = b < hq ? nqb : hq * nqb;
     double acc = 0.0;
-    if (b < hq) {
-        for (int t = tid; t < nk; t += 256) acc += (double)dgp[(int64_t)b * kp + t];
-    } else {
-        for (int hh = 0; hh < hq; ++hh)
-            for (int t = tid; t < nk; t += 256) acc += (double)dlamc[(int64_t)hh * kp + t];
-    }
+#pragma unroll 8
+    for (int i = tid; i < n; i += 256) acc += (double)src[i];
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
     if (lane == 0) red[w] = acc;
@@ -410,19 +534,22 @@ int launch_bwd_d(const uint16_t* q, const uint16_t* k, const uint16_t* v, const 
     int rc = tgi::launch_gated_attention(q, k, v, key_score, gains, temp_coef, pos, nk, hq, hkv, D, ws.out, 1, ws.lse,
                                          kp, s);
     if (rc != TG_OK) return rc;
-    const int64_t rows = (int64_t)nk * hq;
-    hipLaunchKernelGGL(bwd_prep<D>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, ws.out, dout, pos, temp_coef,
-                       nk, hq, kp, ws.dvec, ws.lam, ws.acoef);
+    float4* rowv = reinterpret_cast<float4*>(ws.rowv);
+    constexpr int RPB = 256 / (D / 8);
+    hipLaunchKernelGGL(bwd_prep<D>, dim3((unsigned)(((int64_t)hq * kp + RPB - 1) / RPB)), dim3(256), 0, s, ws.out,
+                       dout, ws.lse, pos, temp_coef, nk, hq, kp, rowv);
     const int nqb = (nk + 31) / 32;
     hipLaunchKernelGGL(bwd_dq<D>, dim3((unsigned)((hq * nqb + kWavesPerBlock - 1) / kWavesPerBlock)),
-                       dim3(64 * kWavesPerBlock), 0, s, q, k, v, key_score, gains, pos, dout, ws.lse, ws.dvec, ws.lam,
-                       ws.acoef, nk, hq, hkv, kp, dq, ws.dlamc, ws.dgp);
-    hipLaunchKernelGGL(bwd_dkv<D>, dim3((unsigned)((hkv * nqb + kWavesPerBlock - 1) / kWavesPerBlock)),
-                       dim3(64 * kWavesPerBlock), 0, s, q, k, v, key_score, gains, dout, ws.lse, ws.dvec, ws.lam,
-                       ws.acoef, nk, hq, hkv, kp, dk, dv, ws.dsp);
+                       dim3(64 * kWavesPerBlock), 0, s, q, k, v, key_score, gains, pos, dout, rowv, nk, hq, hkv, kp,
+                       dq, ws.dlamc, ws.dgp);
+    const int grp = hq / hkv;
+    const int wsplit = grp >= 4 ? 4 : (grp >= 2 ? 2 : 1);
+    const int kbs = kWavesPerBlock / wsplit;
+    hipLaunchKernelGGL(bwd_dkv<D>, dim3((unsigned)(hkv * ((nqb + kbs - 1) / kbs))), dim3(64 * kWavesPerBlock), 0, s,
+                       q, k, v, key_score, gains, dout, rowv, nk, hq, hkv, kp, wsplit, dk, dv, ws.dsp);
     hipLaunchKernelGGL(bwd_reduce_score, dim3((unsigned)((nk + 255) / 256)), dim3(256), 0, s, ws.dsp, nk, hkv, kp,
                        dscore);
-    hipLaunchKernelGGL(bwd_reduce_rows, dim3((unsigned)(hq + 1)), dim3(256), 0, s, ws.dgp, ws.dlamc, nk, hq, kp, dgains,
+    hipLaunchKernelGGL(bwd_reduce_rows, dim3((unsigned)(hq + 1)), dim3(256), 0, s, ws.dgp, ws.dlamc, nqb, hq, dgains,
                        dtemp);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_EDEVICE;
 }

@@ -60,21 +60,20 @@ int launch_gated_attention(const uint16_t* q, const uint16_t* k, const uint16_t*
 // scale [kp], per-row partials of dc and dg [hq, kp], per-key partials of ds
 // [hkv, kp].
 struct AttnBwdWs {
-    float* out;
-    float* lse;
-    float* dvec;
-    float* lam;
-    float* acoef;
-    float* dlamc;
-    float* dgp;
-    float* dsp;
+    float* out;     // [n, hq, d] forward output, fp32
+    float* lse;     // [hq][kp] forward per-row log2-sum-exp2
+    float* rowv;    // [hq][kp] float4 per row: a_t, lse, D_t = dO.O, lambda_t
+    float* dlamc;   // [hq][kp / 32] per-block partial of the temperature gradient
+    float* dgp;     // [hq][kp / 32] per-block partial of the gain gradient
+    float* dsp;     // [hkv][kp] per-kv-head partial of the score gradient
     int kp;
 };
 inline int64_t attn_bwd_kp(int64_t n) { return (n + 31) / 32 * 32; }
 inline size_t attn_bwd_ws_bytes(int64_t n, int hq, int hkv, int d) {
     const size_t kp = (size_t)attn_bwd_kp(n);
-    return align_up(sizeof(float) * (size_t)n * hq * d) + 4 * align_up(sizeof(float) * hq * kp) +
-           2 * align_up(sizeof(float) * kp) + align_up(sizeof(float) * hkv * kp);
+    return align_up(sizeof(float) * (size_t)n * hq * d) + align_up(sizeof(float) * hq * kp) +
+           align_up(4 * sizeof(float) * hq * kp) + 2 * align_up(sizeof(float) * hq * (kp / 32)) +
+           align_up(sizeof(float) * hkv * kp);
 }
 inline AttnBwdWs attn_bwd_ws(void* base, int64_t n, int hq, int hkv, int d) {
     const size_t kp = (size_t)attn_bwd_kp(n);
@@ -85,17 +84,14 @@ inline AttnBwdWs attn_bwd_ws(void* base, int64_t n, int hq, int hkv, int d) {
     p += align_up(sizeof(float) * (size_t)n * hq * d);
     w.lse = (float*)p;
     p += align_up(sizeof(float) * hq * kp);
-    w.dvec = (float*)p;
-    p += align_up(sizeof(float) * hq * kp);
+    w.rowv = (float*)p;
+    p += align_up(4 * sizeof(float) * hq * kp);
     w.dlamc = (float*)p;
-    p += align_up(sizeof(float) * hq * kp);
+    p += align_up(sizeof(float) * hq * (kp / 32));
     w.dgp = (float*)p;
-    p += align_up(sizeof(float) * hq * kp);
-    w.lam = (float*)p;
-    p += align_up(sizeof(float) * kp);
-    w.acoef = (float*)p;
-    p += align_up(sizeof(float) * kp);
+    p += align_up(sizeof(float) * hq * (kp / 32));
     w.dsp = (float*)p;
+    (void)hkv;
     return w;
 }
 

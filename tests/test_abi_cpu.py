@@ -200,3 +200,31 @@ def test_layer_piece_checks(lib):
     assert lib.tg_linear(A, None, A, None, A, 4, 64, 64, None) == E.TG_EINVAL
     assert lib.tg_blas_create(None) == E.TG_EINVAL
     assert lib.tg_blas_destroy(None) == E.TG_EINVAL
+
+
+def _bwd(lib, n=64, hq=4, hkv=2, D=64, c=0.1, ws=A, ws_bytes=WS, **over):
+    p = dict(q=A, k=A, v=A, s=A, g=A, pos=A, dout=A, dq=A, dk=A, dv=A, ds=A, dg=A, dc=A)
+    p.update(over)
+    return lib.tg_gated_attention_bwd(p["q"], p["k"], p["v"], p["s"], p["g"], c, p["pos"], n, hq, hkv, D, p["dout"],
+                                      p["dq"], p["dk"], p["dv"], p["ds"], p["dg"], p["dc"], ws, ws_bytes, None)
+
+
+def test_attention_backward_checks(lib):
+    E = binding
+    need = lib.tg_attention_bwd_workspace_bytes(64, 4, 2, 64)
+    assert 0 < need <= WS
+    # the workspace grows with the kept rows and the heads
+    assert lib.tg_attention_bwd_workspace_bytes(4096, 16, 8, 128) > lib.tg_attention_bwd_workspace_bytes(64, 16, 8, 128)
+    assert lib.tg_attention_bwd_workspace_bytes(-1, 4, 2, 64) == 0
+    assert _bwd(lib, n=0) == E.TG_OK  # nothing kept: no-op
+    assert _bwd(lib, n=-1) == E.TG_EINVAL
+    assert _bwd(lib, hq=3, hkv=2) == E.TG_EINVAL
+    assert _bwd(lib, D=96) == E.TG_EUNSUPPORTED
+    assert _bwd(lib, c=float("nan")) == E.TG_EINVAL
+    assert _bwd(lib, q=None) == E.TG_EINVAL
+    assert _bwd(lib, dc=None) == E.TG_EINVAL
+    assert _bwd(lib, dout=M) == E.TG_EALIGN
+    assert _bwd(lib, dk=M) == E.TG_EALIGN
+    assert _bwd(lib, ws=None) == E.TG_EWORKSPACE
+    assert _bwd(lib, ws_bytes=need - 1) == E.TG_EWORKSPACE
+    assert _bwd(lib, ws=A + 16) == E.TG_EALIGN  # workspace must be 256-byte aligned

@@ -58,8 +58,7 @@ def _rel(a, b):
 # (150, ..., 0.5) spread 40x: lambda < 0 on the early rows
 @pytest.mark.parametrize("nk,hq,hkv,D,c,seed,spread", [(200, 4, 2, 64, 0.1, 1, 4), (333, 8, 1, 128, 0.1, 2, 4),
                                                        (256, 16, 8, 128, 0.1, 3, 4), (31, 2, 2, 64, 0.0, 4, 4),
-                                                       (97, 4, 2, 128, -0.9, 5, 40), (150, 4, 2, 64, 0.5, 8, 40),
-                                                       (1, 2, 1, 64, 0.1, 6, 4)])
+                                                       (97, 4, 2, 128, -0.9, 5, 40), (150, 4, 2, 64, 0.5, 8, 40)])
 def test_attention_backward_matches_oracle(nk, hq, hkv, D, c, seed, spread):
     q, k, v, dout, ks, gains, pos, c = _case(seed, nk, hq, hkv, D, c, pos_spread=spread)
     t = np.arange(nk)
@@ -77,6 +76,24 @@ def test_attention_backward_matches_oracle(nk, hq, hkv, D, c, seed, spread):
     for n in ("ds", "dg"):
         assert errs[n] <= TOL_SG, n
     assert abs(got["dc"][0] - dc) <= TOL_C * max(abs(dc), 1e-6), "dc"
+
+
+@pytest.mark.parametrize("hq,hkv,D", [(2, 1, 64), (4, 2, 128)])
+def test_attention_backward_single_token(hq, hkv, D):
+    """One kept token: every softmax row is the constant 1, so O = v_0, the
+    value gradient is the sum of the group's output gradients, and every other
+    gradient is zero (dP - D_t cancels exactly).  Zero is checked in absolute
+    terms: the fp32 cancellation leaves ~1e-7 of |dO| |v|."""
+    q, k, v, dout, ks, gains, pos, c = _case(6, 1, hq, hkv, D, 0.1)
+    gu.say(f"attention backward single token hq={hq} hkv={hkv} D={D}")
+    got = _run(q, k, v, dout, ks, gains, pos, c)
+    w = oracle.widen_bf16
+    G = hq // hkv
+    want_dv = w(dout).reshape(1, hkv, G, D).sum(axis=2)
+    assert np.allclose(got["dv"], want_dv, rtol=1e-6, atol=1e-6)
+    scale = float(np.linalg.norm(w(dout)) * np.linalg.norm(w(v)))
+    for n in ("dq", "dk", "ds", "dg", "dc"):
+        assert np.max(np.abs(got[n])) <= 1e-5 * scale, n
 
 
 def test_attention_backward_is_deterministic():
