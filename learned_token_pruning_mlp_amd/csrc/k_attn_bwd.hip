@@ -150,54 +150,55 @@ __global__ __launch_bounds__(256) void bwd_prep(const float* __restrict__ O, con
     }
 }
 
-// Register copy of this lane's pieces of a 32-row block: fetched one block
-// ahead, written to LDS when its turn comes.  Rows past nrows repeat the last
-// row; everything they feed is masked by the causal test.
-template <int D>
-struct Rows {
-    u32x4 p[Geo<D>::PIECES / 2];
-};
+// Direct loads from memory into LDS: `SIZE` bytes per lane from base + voff
+// land at lds + SIZE * lane, through a raw buffer resource covering `bytes`
+// bytes, so offsets at or past the end read as zero (rows past the last one).
+constexpr int kBufferWord3 = 0x00020000;
 
+template <int SIZE>
+__device__ __forceinline__ void lds_load(const void* base, uint32_t bytes, TG_LDS uint8_t* lds, uint32_t voff) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+    static_assert(SIZE == 16 || SIZE == 4, "direct-load size");
+    if constexpr (SIZE == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (TG_LDS void*)lds, 16, voff, 0, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (TG_LDS void*)lds, 4, voff, 0, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+#define TG_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+
+// 32 rows (row0 ..) of head hh of a [rows, heads, D] bf16 tensor into an LDS
+// block: instruction `it` fills bytes it*1024 .. +1023, lane L the 16-byte slot
+// (it*64 + L) of the block, i.e. row r, slot c'; it reads piece c' ^ swz(r) of
+// that row, which gives the swizzled layout the operand reads expect.
 template <int D>
-__device__ __forceinline__ void fetch_rows(const uint16_t* __restrict__ src, int heads, int hh, int row0, int nrows,
-                                           Rows<D>& st, int lane) {
+__device__ __forceinline__ void load_block(const uint16_t* src, uint32_t bytes, int heads, int hh, int row0,
+                                           TG_LDS uint8_t* blk, int lane) {
     using G = Geo<D>;
 #pragma unroll
     for (int it = 0; it < G::PIECES / 2; ++it) {
         const int e = it * 64 + lane;
-        const int row = min(row0 + e / G::PIECES, nrows - 1);
-        st.p[it] = *reinterpret_cast<const u32x4*>(src + ((int64_t)row * heads + hh) * D + 8 * (e % G::PIECES));
+        const int r = e / G::PIECES, c = (e % G::PIECES) ^ swz<G::PIECES>(r);
+        const uint32_t voff = ((uint32_t)(row0 + r) * (uint32_t)heads + (uint32_t)hh) * (uint32_t)G::ROW_BYTES + 16u * c;
+        lds_load<16>(src, bytes, blk + it * 1024, voff);
     }
 }
-
-template <int D>
-__device__ __forceinline__ void put_rows(const Rows<D>& st, TG_LDS uint8_t* blk, int lane) {
-    using G = Geo<D>;
-#pragma unroll
-    for (int it = 0; it < G::PIECES / 2; ++it) {
-        const int e = it * 64 + lane;
-        const int r = e / G::PIECES, c = e % G::PIECES;
-        *reinterpret_cast<TG_LDS u32x4*>(blk + r * G::ROW_BYTES + 16 * (c ^ swz<G::PIECES>(r))) = st.p[it];
-    }
-}
-
-// Compiler-level memory fence: keeps a wave's LDS writes of the next block
-// after its reads of the current one (LDS runs one wave's accesses in order).
-// The prefetched sources are plain (not __restrict__) pointers: loads through
-// a restrict read-only argument count as invariant, and the compiler would
-// move them past the fence to where their values are used, undoing the
-// prefetch.
-#define TG_CFENCE() asm volatile("" ::: "memory")
 
 // ---- dq, and per-(head, query block) partials of dlambda and of sum dU s
+// Each wave streams its key blocks through two LDS stages of its own (K
+// block, V block, 64 key scores): the loads of block kb+1 fly while block kb
+// is multiplied.
 template <int D>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void bwd_dq(
-    const uint16_t* __restrict__ q, const uint16_t* k, const uint16_t* v, const float* key_score,
-    const float* __restrict__ gains, const int32_t* __restrict__ pos, const uint16_t* __restrict__ dO,
-    const float4* __restrict__ rowv, int nk, int hq, int hkv, int kp, float* __restrict__ dq,
-    float* __restrict__ dlamc, float* __restrict__ dgp) {
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ key_score, const float* __restrict__ gains, const int32_t* __restrict__ pos,
+    const uint16_t* __restrict__ dO, const float4* __restrict__ rowv, int nk, int hq, int hkv, int kp,
+    float* __restrict__ dq, float* __restrict__ dlamc, float* __restrict__ dgp) {
     using G = Geo<D>;
-    __shared__ __attribute__((aligned(1024))) uint8_t sK[kWavesPerBlock][G::BLOCK_BYTES];
+    constexpr int STAGE = 2 * G::BLOCK_BYTES + 256;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kWavesPerBlock * 2 * STAGE];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int l32 = lane & 31, g = lane >> 5;
     const int nqb = (nk + 31) / 32;
@@ -210,7 +211,9 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void bwd_dq(
     const bool ok = t < nk;
     const float rs = 1.0f / sqrtf((float)D);
     const float sg = sqrtf((float)D) * gains[h];
-    TG_LDS uint8_t* blk = (TG_LDS uint8_t*)sK[w];
+    TG_LDS uint8_t* st0 = (TG_LDS uint8_t*)smem + w * 2 * STAGE;
+    TG_LDS uint8_t* st1 = st0 + STAGE;
+    const uint32_t kv_bytes = (uint32_t)nk * (uint32_t)hkv * (uint32_t)G::ROW_BYTES;
 
     u32x4 qreg[G::QS], doreg[G::QS];
 #pragma unroll
@@ -226,43 +229,33 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void bwd_dq(
     for (int db = 0; db < G::DB; ++db) dqa[db] = f32x16{};
     float dl = 0.0f, dgs = 0.0f;
 
-    // block kb's K rows (for LDS), V operand and key scores, one block ahead;
-    // this lane's 16 key rows of the accumulators are j0 + 8 (i/4) + 4 g + i%4
-    Rows<D> kst;
-    u32x4 vn[G::QS];
-    float svn[16];
-    auto fetch = [&](int kb) {
+    auto issue = [&](int kb, TG_LDS uint8_t* __restrict__ nb) {
         const int j0 = kb * 32;
-        fetch_rows<D>(k, hkv, hk, j0, nk, kst, lane);
-        const int jr = min(j0 + l32, nk - 1);
-#pragma unroll
-        for (int s = 0; s < G::QS; ++s)
-            vn[s] = *reinterpret_cast<const u32x4*>(v + ((int64_t)jr * hkv + hk) * D + 16 * s + 8 * g);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) svn[i] = key_score[min(j0 + 8 * (i >> 2) + 4 * g + (i & 3), nk - 1)];
+        load_block<D>(k, kv_bytes, hkv, hk, j0, nb, lane);
+        load_block<D>(v, kv_bytes, hkv, hk, j0, nb + G::BLOCK_BYTES, lane);
+        lds_load<4>(key_score, (uint32_t)nk * 4u, nb + 2 * G::BLOCK_BYTES, (uint32_t)(j0 + lane) * 4u);
     };
-    fetch(0);
-
-    for (int kb = 0; kb <= qb; ++kb) {
+    auto step = [&](int kb, TG_LDS uint8_t* __restrict__ cb, TG_LDS uint8_t* __restrict__ nb) {
+        TG_WAIT_VMCNT(0);  // this block is in LDS
+        if (kb < qb) issue(kb + 1, nb);
         const int j0 = kb * 32;
-        u32x4 vc[G::QS];
+        TG_LDS uint8_t* kblk = cb;
+        TG_LDS uint8_t* vblk = cb + G::BLOCK_BYTES;
+        const TG_LDS lf4* sblk = (const TG_LDS lf4*)(cb + 2 * G::BLOCK_BYTES);
+        // this lane's 16 key rows of the accumulators: j0 + 8 (i/4) + 4 g + i%4
         float sv[16];
 #pragma unroll
-        for (int s = 0; s < G::QS; ++s) vc[s] = vn[s];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sv[i] = svn[i];
-        TG_CFENCE();
-        put_rows<D>(kst, blk, lane);
-        fetch(min(kb + 1, qb));  // issued before the products below, not sunk past the fence
-        TG_CFENCE();
-
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const lf4 x = sblk[2 * i4 + g];
+            sv[4 * i4] = x.x, sv[4 * i4 + 1] = x.y, sv[4 * i4 + 2] = x.z, sv[4 * i4 + 3] = x.w;
+        }
         f32x16 sacc, dpacc = f32x16{};
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[i] = sg * sv[i];
 #pragma unroll
         for (int s = 0; s < G::QS; ++s) {
-            sacc = tgd::mfma32(row_operand<D>(blk, l32, g, s), qreg[s], sacc);
-            dpacc = tgd::mfma32(vc[s], doreg[s], dpacc);
+            sacc = tgd::mfma32(row_operand<D>(kblk, l32, g, s), qreg[s], sacc);
+            dpacc = tgd::mfma32(row_operand<D>(vblk, l32, g, s), doreg[s], dpacc);
         }
         f32x16 du;
 #pragma unroll
@@ -280,7 +273,13 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void bwd_dq(
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
-            for (int db = 0; db < G::DB; ++db) dqa[db] = tgd::mfma32(tr_operand<D>(blk, lane, db, s), pb[s], dqa[db]);
+            for (int db = 0; db < G::DB; ++db)
+                dqa[db] = tgd::mfma32(tr_operand<D>(kblk, lane, db, s), pb[s], dqa[db]);
+    };
+    issue(0, st0);
+    for (int kb = 0; kb <= qb; kb += 2) {
+        step(kb, st0, st1);
+        if (kb + 1 <= qb) step(kb + 1, st1, st0);
     }
     // dq_t[d]: accumulator unit u holds head_dim rows 32 (u/4) + 8 (u%4) + 4 g .. +3
     if (ok) {
@@ -308,15 +307,15 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void bwd_dq(
 // their partial sums are added in LDS in the order r = 0, 1, ...
 template <int D>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void bwd_dkv(
-    const uint16_t* q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ key_score, const float* gains, const uint16_t* dO,
-    const float4* rowv, int nk, int hq, int hkv, int kp, int wsplit, float* __restrict__ dk,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ key_score, const float* __restrict__ gains, const uint16_t* __restrict__ dO,
+    const float4* __restrict__ rowv, int nk, int hq, int hkv, int kp, int wsplit, float* __restrict__ dk,
     float* __restrict__ dv, float* __restrict__ dsp) {
     using G = Geo<D>;
-    constexpr int SLOT = 2 * G::BLOCK_BYTES + 512;  // Q block, dO block, 32 row values
-    constexpr int XCH = G::DB * 16 * 64 * 4;        // one wave's accumulator set, bytes
-    static_assert(3 * XCH <= kWavesPerBlock * SLOT, "exchange fits the staging memory");
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[kWavesPerBlock * SLOT];
+    constexpr int STAGE = 2 * G::BLOCK_BYTES + 1024;  // Q block, dO block, 64 row values (32 used)
+    constexpr int XCH = G::DB * 16 * 64 * 4;          // one wave's accumulator set, bytes
+    static_assert(3 * XCH <= kWavesPerBlock * 2 * STAGE, "exchange fits the staging memory");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kWavesPerBlock * 2 * STAGE];
     __shared__ float sds[kWavesPerBlock][64];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int l32 = lane & 31, g = lane >> 5;
@@ -330,9 +329,10 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void bwd_dkv(
     const int j = kb * 32 + l32;  // this lane's key column
     const int jc = min(j, nk - 1);
     const float rs = 1.0f / sqrtf((float)D);
-    TG_LDS uint8_t* bq = (TG_LDS uint8_t*)smem + w * SLOT;
-    TG_LDS uint8_t* bo = bq + G::BLOCK_BYTES;
-    TG_LDS lf4* brow = (TG_LDS lf4*)(bo + G::BLOCK_BYTES);
+    TG_LDS uint8_t* st0 = (TG_LDS uint8_t*)smem + w * 2 * STAGE;
+    TG_LDS uint8_t* st1 = st0 + STAGE;
+    const uint32_t q_bytes = (uint32_t)nk * (uint32_t)hq * (uint32_t)G::ROW_BYTES;
+    const uint32_t row_bytes = (uint32_t)hq * (uint32_t)kp * 16u;
 
     u32x4 kreg[G::QS], vreg[G::QS];
 #pragma unroll
@@ -346,41 +346,33 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void bwd_dkv(
     for (int db = 0; db < G::DB; ++db) dka[db] = dva[db] = f32x16{};
     float dsj = 0.0f;
 
-    // (head, query block) pairs of this wave: heads r, r + W, ..., query blocks kb .. nkb-1
+    // (head, query block) pairs of this wave: heads r, r + W, ..., query
+    // blocks kb .. nkb-1, streamed through two LDS stages of its own
     const int nq = valid ? nkb - kb : 0;
     const int nh = valid ? (grp - r + W - 1) / W : 0;
     const int iters = nq * nh;
-    Rows<D> qst, ost;
-    float4 rown = float4{0.0f, 0.0f, 0.0f, 0.0f};
-    float ghn = 0.0f;
-    auto fetch = [&](int hh, int qb) {
+    int ch = r, cq = kb;  // the current pair
+    float gh_c = 0.0f, gh_n = 0.0f;
+    auto issue = [&](int hh, int qb, TG_LDS uint8_t* __restrict__ nb) -> float {
         const int h = hk * grp + hh;
-        fetch_rows<D>(q, hq, h, qb * 32, nk, qst, lane);
-        fetch_rows<D>(dO, hq, h, qb * 32, nk, ost, lane);
-        rown = rowv[(int64_t)h * kp + qb * 32 + l32];
-        ghn = gains[h];
+        load_block<D>(q, q_bytes, hq, h, qb * 32, nb, lane);
+        load_block<D>(dO, q_bytes, hq, h, qb * 32, nb + G::BLOCK_BYTES, lane);
+        lds_load<16>(rowv, row_bytes, nb + 2 * G::BLOCK_BYTES, ((uint32_t)h * (uint32_t)kp + qb * 32 + lane) * 16u);
+        return gains[h];
     };
-    int hh = r, qb = kb;
-    if (iters > 0) fetch(hh, qb);
-
-    for (int it = 0; it < iters; ++it) {
-        const int t0 = qb * 32;
-        const float gh = ghn;
-        int hn = hh, qn = qb + 1;
+    auto step = [&](int it, TG_LDS uint8_t* __restrict__ cb, TG_LDS uint8_t* __restrict__ nb) {
+        TG_WAIT_VMCNT(0);  // this pair's blocks are in LDS
+        int hn = ch, qn = cq + 1;
         if (qn == nkb) {
             qn = kb;
-            hn = hh + W;
+            hn = ch + W;
         }
-        if (it + 1 == iters) {  // nothing left: fetch the current pair again
-            hn = hh;
-            qn = qb;
-        }
-        TG_CFENCE();
-        put_rows<D>(qst, bq, lane);
-        put_rows<D>(ost, bo, lane);
-        if (lane < 32) brow[lane] = lf4{rown.x, rown.y, rown.z, rown.w};
-        fetch(hn, qn);  // issued before the products below, not sunk past the fence
-        TG_CFENCE();
+        if (it + 1 < iters) gh_n = issue(hn, qn, nb);
+        const float gh = gh_c;
+        const int t0 = cq * 32;
+        TG_LDS uint8_t* bq = cb;
+        TG_LDS uint8_t* bo = cb + G::BLOCK_BYTES;
+        const TG_LDS lf4* brow = (const TG_LDS lf4*)(cb + 2 * G::BLOCK_BYTES);
 
         // this lane's 16 query rows: t0 + 8 (i/4) + 4 g + i%4
         float ar[16], lr[16], dr[16], mr[16];
@@ -418,8 +410,14 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void bwd_dkv(
                 dka[db] = tgd::mfma32(tr_operand<D>(bq, lane, db, s), pu[s], dka[db]);
             }
         }
-        hh = hn;
-        qb = qn;
+        ch = hn;
+        cq = qn;
+        gh_c = gh_n;
+    };
+    if (iters > 0) gh_c = issue(ch, cq, st0);
+    for (int it = 0; it < iters; it += 2) {
+        step(it, st0, st1);
+        if (it + 1 < iters) step(it + 1, st1, st0);
     }
     dsj = tgd::half_sum(dsj);
 
