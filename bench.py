@@ -239,7 +239,8 @@ def main():
 
     sweep = None if args.no_attn_sweep else attn_sweep(tg, torch, dev, shp)
     prefill = None if (args.no_prefill or args.workload != "n16k") else prefill_compare(tg, torch, dev, shp, seed)
-    backward = None if (args.no_attn_sweep or args.workload != "n16k") else attn_backward(tg, torch, dev, shp)
+    backward = None if (args.no_attn_sweep or args.workload != "n16k") else \
+        {"attention": attn_backward(tg, torch, dev, shp), "scorer": gate_backward(tg, torch, dev, shp)}
 
     result = {
         "metric": METRIC,
@@ -265,7 +266,7 @@ def main():
         "roofline": roof,
         "attn_sweep": sweep,
         "prefill": prefill,
-        "attn_backward": backward,
+        "backward": backward,
         "cpu_baseline": None,
     }
 
@@ -377,6 +378,45 @@ def attn_backward(tg, torch, dev, shp, ks=(2048, 8192), reps=5):
         out[str(k)] = {"us": round(us, 1), "tflops": round(flop / us / 1e6, 1),
                        "frac": round(flop / us / 1e6 / PEAK_BF16_TFLOPS, 4)}
     return out
+
+
+def gate_backward(tg, torch, dev, shape, reps=5):
+    """tg_gate_score_bwd at the gate layer's shape: three GEMMs of 2 n d hd
+    FLOP each (z again, dz W1, dz^T h); algorithmic bytes = the residual read
+    once (bf16) + its gradient written (fp32)."""
+    n, d, hd, k = shape.n, shape.d, shape.hd, shape.k
+    g = torch.Generator(device=dev)
+    g.manual_seed(n)
+    resid = torch.randn(n, d, generator=g, device=dev).to(torch.bfloat16)
+    w1 = (torch.randn(hd, d, generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    w2 = (torch.randn(hd, generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    s_raw = torch.randn(n, generator=g, device=dev)
+    kept = torch.randperm(n, generator=g, device=dev)[:k].sort().values.to(torch.int32)
+    dsk = torch.randn(k, generator=g, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = [torch.empty(n, d, **f32), torch.empty(hd, d, **f32), torch.empty(hd, **f32), torch.empty(hd, **f32),
+           torch.empty(1, **f32)]
+    ws = torch.empty(tg.tg_gate_score_bwd_workspace_bytes(n, d, hd), dtype=torch.uint8, device=dev)
+    blas = tg.BlasHandle()
+    try:
+        def run():
+            tg.tg_gate_score_bwd(blas, resid, w1, None, w2, 1e-6, 1e-6, s_raw, dsk, kept, *out, ws=ws)
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+    finally:
+        blas.close()
+    flop = 3 * 2.0 * n * d * hd
+    byts = n * d * 2 + n * d * 4
+    return {"n": n, "us": round(us, 1), "tflops": round(flop / us / 1e6, 1),
+            "mfma_frac": round(flop / us / 1e6 / PEAK_BF16_TFLOPS, 4), "hbm_gbs": round(byts / us / 1e3, 1),
+            "hbm_frac": round(byts / us / 1e3 / PEAK_HBM_GBS, 4)}
 
 
 def attn_sweep(tg, torch, dev, shp, ks=(4096, 8192, 16384), reps=10):

@@ -31,7 +31,7 @@
  *  - Every tensor pointer is DEVICE memory owned by the caller; the library
  *    allocates nothing, keeps no state between calls, never synchronises the
  *    stream and never reads device data back to the host.  (The one
- *    exception is the rocBLAS handle of tg_linear, which the caller creates
+ *    exception is the rocBLAS handle of tg_linear and tg_gate_score_bwd, which the caller creates
  *    and destroys explicitly with tg_blas_create / tg_blas_destroy.)  Work is enqueued on
  *    `stream` (a hipStream_t passed as void*; NULL = the null stream) and is
  *    complete when the stream reaches that point.
@@ -220,6 +220,47 @@ int tg_gated_attention_bwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v,
                            void* stream);
 
 /*
+ * tg_gate_score_bwd_workspace_bytes -- device workspace of tg_gate_score_bwd
+ * (256-byte aligned): about 6 * n * hd bytes, per-row arrays and up to 17
+ * partial copies of dw1 (4 * hd * d bytes each).
+ */
+size_t tg_gate_score_bwd_workspace_bytes(int64_t n, int32_t d, int32_t hd);
+
+/*
+ * tg_gate_score_bwd -- gradients of tg_gate_score's normalised scores with
+ * respect to the residual and the scorer's weights [P1 gate][P1 tga]
+ * [P2 method][P5 Fig 1(a)(b)]: the gate is trained end to end through the
+ * attention bias of the kept tokens, so the incoming gradient is
+ * dscore_kept[t] = dL/dscore_norm[kept_idx[t]] (what tg_gated_attention_bwd
+ * returns as dscore, in kept order) and zero for every pruned token.
+ * With the forward of tg_gate_score (r_i, a_ij, s_i, rho as documented there):
+ *   ds_i   = dshat_i / rho - s_i (sum_m dshat_m s_m) / (n rho^3)
+ *   dw2_j  = sum_i ds_i GELU(a_ij),   db2 = sum_i ds_i
+ *   da_ij  = ds_i w2_j GELU'(a_ij),   db1_j = sum_i da_ij
+ *   dw1    = (r da)^T resid
+ *   dresid_i = (r_i da_i) w1 - (sum_j da_ij (resid_i . w1_j)) r_i^3 resid_i / d
+ * blas: a handle from tg_blas_create (three rocBLAS GEMMs run through it:
+ *   resid w1^T again, the w1 product of dresid and dw1).
+ * resid, w1, b1 (or NULL), w2, n, d, hd, eps_row, eps_seq: as given to
+ *   tg_gate_score.  score_raw [n] fp32: its raw-score output.
+ * dscore_kept [k] fp32, kept_idx [k] int32: distinct indices in [0, n)
+ *   (entries outside are skipped); k may be 0 (then only the pruned-token
+ *   paths remain and every gradient is zero).
+ * dresid [n, d] fp32 out, dw1 [hd, d] fp32 out (both 16-byte aligned), db1 [hd],
+ *   dw2 [hd], db2 [1] fp32 out; all overwritten.  db1 is written also when
+ *   b1 is NULL (the gradient of a zero bias).
+ * Supported: hd in {64, 128, 256}; d % 64 == 0, 64 <= d <= 4096; resid
+ * 16-byte aligned.  n == 0 is a no-op.  dz = r da enters the two gradient
+ * GEMMs in bf16 (fp32 accumulation); the rest is fp32 with fp64 sums.
+ * Deterministic: fixed reduction orders, and the handle's GEMMs run with
+ * atomics disabled.
+ */
+int tg_gate_score_bwd(void* blas, const tg_bf16* resid, const tg_bf16* w1, const tg_bf16* b1, const tg_bf16* w2,
+                      int64_t n, int32_t d, int32_t hd, float eps_row, float eps_seq, const float* score_raw,
+                      const float* dscore_kept, const int32_t* kept_idx, int64_t k, float* dresid, float* dw1,
+                      float* db1, float* dw2, float* db2, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * ---- Upper decoder layer on the kept rows ----
  * Above the gate only the kept tokens go through the backbone's layers
  * [P1 gate][P5 Fig 1(a)(b)].  With a Qwen3-shaped backbone a layer is:
@@ -252,7 +293,8 @@ int tg_rmsnorm(const tg_bf16* x, const tg_bf16* weight, tg_bf16* y, int64_t rows
 int tg_swiglu(const tg_bf16* gate_up, tg_bf16* out, int64_t rows, int32_t inter, void* stream);
 
 /*
- * tg_blas_create / tg_blas_destroy -- a rocBLAS handle for tg_linear.  The
+ * tg_blas_create / tg_blas_destroy -- a rocBLAS handle for tg_linear (and
+ * tg_gate_score_bwd), created with atomics disabled.  The
  * handle is the one piece of library-side state and allocation: the caller
  * creates it once per device (with that device current), owns it, and
  * destroys it; calls that share a handle must not run concurrently from

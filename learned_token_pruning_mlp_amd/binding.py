@@ -29,7 +29,8 @@ TG_MAX_GATHER = 16
 EXPORTS = ("tg_status_string", "tg_abi_version", "tg_workspace_bytes", "tg_gate_score",
            "tg_select_topk", "tg_compact", "tg_rope", "tg_rope_qk", "tg_gated_attention",
            "tg_rmsnorm", "tg_swiglu", "tg_blas_create", "tg_blas_destroy", "tg_linear",
-           "tg_attention_bwd_workspace_bytes", "tg_gated_attention_bwd")
+           "tg_attention_bwd_workspace_bytes", "tg_gated_attention_bwd", "tg_gate_score_bwd_workspace_bytes",
+           "tg_gate_score_bwd")
 
 
 class TgGather(ctypes.Structure):
@@ -88,6 +89,11 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
     L.tg_gated_attention_bwd.argtypes = [P, P, P, P, P, F, P, I64, I32, I32, I32, P, P, P, P, P, P, P, P,
                                          ctypes.c_size_t, P]
     L.tg_gated_attention_bwd.restype = ctypes.c_int
+    L.tg_gate_score_bwd_workspace_bytes.argtypes = [I64, I32, I32]
+    L.tg_gate_score_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.tg_gate_score_bwd.argtypes = [P, P, P, P, P, I64, I32, I32, F, F, P, P, P, I64, P, P, P, P, P, P,
+                                    ctypes.c_size_t, P]
+    L.tg_gate_score_bwd.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -330,3 +336,37 @@ def tg_gated_attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ke
         _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dscore), _ptr(dgains), _ptr(dtemp), _ptr(ws), ws.numel(),
         _stream(stream)))
 
+
+
+def tg_gate_score_bwd_workspace_bytes(n: int, d: int, hd: int) -> int:
+    return int(load().tg_gate_score_bwd_workspace_bytes(int(n), int(d), int(hd)))
+
+
+def tg_gate_score_bwd(handle: BlasHandle, resid: torch.Tensor, w1: torch.Tensor, b1: Optional[torch.Tensor],
+                      w2: torch.Tensor, eps_row: float, eps_seq: float, score_raw: torch.Tensor,
+                      dscore_kept: torch.Tensor, kept_idx: torch.Tensor, dresid: torch.Tensor, dw1: torch.Tensor,
+                      db1: torch.Tensor, dw2: torch.Tensor, db2: torch.Tensor, ws: Optional[torch.Tensor] = None,
+                      stream=None) -> None:
+    """Gradients of tg_gate_score's normalised scores (fp32 outputs, overwritten)."""
+    n, d = resid.shape
+    hd = w1.shape[0]
+    k = kept_idx.shape[0]
+    _need(resid, "resid", torch.bfloat16, (n, d))
+    _need(w1, "w1", torch.bfloat16, (hd, d))
+    _need(b1, "b1", torch.bfloat16, (hd,), optional=True)
+    _need(w2, "w2", torch.bfloat16, (hd,))
+    _need(score_raw, "score_raw", torch.float32, (n,))
+    _need(dscore_kept, "dscore_kept", torch.float32, (k,))
+    _need(kept_idx, "kept_idx", torch.int32, (k,))
+    _need(dresid, "dresid", torch.float32, (n, d))
+    _need(dw1, "dw1", torch.float32, (hd, d))
+    _need(db1, "db1", torch.float32, (hd,))
+    _need(dw2, "dw2", torch.float32, (hd,))
+    _need(db2, "db2", torch.float32, (1,))
+    if ws is None:
+        ws = torch.empty(max(1, tg_gate_score_bwd_workspace_bytes(n, d, hd)), dtype=torch.uint8, device=resid.device)
+    _need(ws, "ws", torch.uint8)
+    _check("tg_gate_score_bwd", load().tg_gate_score_bwd(
+        handle.value, _ptr(resid), _ptr(w1), _ptr(b1), _ptr(w2), n, d, hd, float(eps_row), float(eps_seq),
+        _ptr(score_raw), _ptr(dscore_kept), _ptr(kept_idx), k, _ptr(dresid), _ptr(dw1), _ptr(db1), _ptr(dw2),
+        _ptr(db2), _ptr(ws), ws.numel(), _stream(stream)))

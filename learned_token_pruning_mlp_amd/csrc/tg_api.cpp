@@ -163,6 +163,30 @@ int tg_gated_attention_bwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v,
                                            dq, dk, dv, dscore, dgains, dtemp, workspace, stream);
 }
 
+size_t tg_gate_score_bwd_workspace_bytes(int64_t n, int32_t d, int32_t hd) {
+    if (n < 0 || d < 1 || hd < 1) return 0;
+    return tgi::gate_bwd_ws_bytes(n, hd, d);
+}
+
+int tg_gate_score_bwd(void* blas, const tg_bf16* resid, const tg_bf16* w1, const tg_bf16* b1, const tg_bf16* w2,
+                      int64_t n, int32_t d, int32_t hd, float eps_row, float eps_seq, const float* score_raw,
+                      const float* dscore_kept, const int32_t* kept_idx, int64_t k, float* dresid, float* dw1,
+                      float* db1, float* dw2, float* db2, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!blas) return TG_EINVAL;
+    if (n < 0 || n > kMaxRows || k < 0 || k > n) return TG_EINVAL;
+    if (!finite_nonneg(eps_row) || !finite_nonneg(eps_seq)) return TG_EINVAL;
+    if (hd != 64 && hd != 128 && hd != 256) return TG_EUNSUPPORTED;
+    if (d < 64 || d % 64 != 0 || d > 4096) return TG_EUNSUPPORTED;
+    if (n == 0) return TG_OK;
+    if (!resid || !w1 || !w2 || !score_raw || !dresid || !dw1 || !db1 || !dw2 || !db2) return TG_EINVAL;
+    if (k > 0 && (!dscore_kept || !kept_idx)) return TG_EINVAL;
+    if (!aligned(resid, 16) || !aligned(dresid, 16) || !aligned(dw1, 16)) return TG_EALIGN;
+    if (!workspace || workspace_bytes < tgi::gate_bwd_ws_bytes(n, hd, d)) return TG_EWORKSPACE;
+    if (!aligned(workspace, 256)) return TG_EALIGN;
+    return tgi::launch_gate_score_bwd(blas, resid, w1, b1, w2, n, d, hd, eps_row, eps_seq, score_raw, dscore_kept,
+                                      kept_idx, k, dresid, dw1, db1, dw2, db2, workspace, stream);
+}
+
 int tg_rmsnorm(const tg_bf16* x, const tg_bf16* weight, tg_bf16* y, int64_t rows, int32_t dim, float eps,
                void* stream) {
     if (rows < 0 || rows > kMaxRows || dim < 8 || dim > 4096 || dim % 8 != 0) return TG_EINVAL;

@@ -100,6 +100,69 @@ int launch_gated_attention_bwd(const uint16_t* q, const uint16_t* k, const uint1
                                int hkv, int head_dim, const uint16_t* dout, float* dq, float* dk, float* dv,
                                float* dscore, float* dgains, float* dtemp, void* workspace, void* stream);
 
+// Backward of the scorer: per-wave row count and the workspace layout.
+constexpr int kGateBwdRowsPerWave = 16;
+inline int64_t gate_bwd_waves(int64_t n) { return (n + kGateBwdRowsPerWave - 1) / kGateBwdRowsPerWave; }
+// dW1 = dz^T h is split over the tokens into this many equal chunks (plus a
+// remainder chunk), summed afterwards in a fixed order.
+inline int gate_bwd_splits(int64_t n) {
+    const int64_t s = n / 2048;
+    return (int)(s < 1 ? 1 : (s > 16 ? 16 : s));
+}
+struct GateBwdWs {
+    float* dsh;     // [n] dense dshat
+    float* sc;      // {1/rho, sequence-norm coefficient}
+    float* z;       // [n, hd] h W1^T, fp32
+    uint16_t* dz;   // [n, hd] bf16
+    float* dw2p;    // [waves, hd] partials
+    float* db1p;    // [waves, hd]
+    float* db2p;    // [waves]
+    float* w1p;     // [splits + 1, hd, d] partial dW1
+};
+inline size_t gate_bwd_ws_bytes(int64_t n, int hd, int d) {
+    const size_t nw = (size_t)gate_bwd_waves(n);
+    return align_up(sizeof(float) * (size_t)n) + align_up(2 * sizeof(float)) + align_up(sizeof(float) * (size_t)n * hd) +
+           align_up(sizeof(uint16_t) * (size_t)n * hd) + 2 * align_up(sizeof(float) * nw * hd) +
+           align_up(sizeof(float) * nw) + align_up(sizeof(float) * (size_t)(gate_bwd_splits(n) + 1) * hd * d);
+}
+inline GateBwdWs gate_bwd_ws(void* base, int64_t n, int hd, int d) {
+    const size_t nw = (size_t)gate_bwd_waves(n);
+    char* p = (char*)base;
+    GateBwdWs w;
+    w.dsh = (float*)p;
+    p += align_up(sizeof(float) * (size_t)n);
+    w.sc = (float*)p;
+    p += align_up(2 * sizeof(float));
+    w.z = (float*)p;
+    p += align_up(sizeof(float) * (size_t)n * hd);
+    w.dz = (uint16_t*)p;
+    p += align_up(sizeof(uint16_t) * (size_t)n * hd);
+    w.dw2p = (float*)p;
+    p += align_up(sizeof(float) * nw * hd);
+    w.db1p = (float*)p;
+    p += align_up(sizeof(float) * nw * hd);
+    w.db2p = (float*)p;
+    p += align_up(sizeof(float) * nw);
+    w.w1p = (float*)p;
+    (void)d;
+    return w;
+}
+
+int launch_gate_score_bwd(void* blas, const uint16_t* resid, const uint16_t* w1, const uint16_t* b1,
+                          const uint16_t* w2, int64_t n, int d, int hd, float eps_row, float eps_seq,
+                          const float* score_raw, const float* dscore_kept, const int32_t* kept_idx, int64_t k,
+                          float* dresid, float* dw1, float* db1, float* dw2, float* db2, void* workspace,
+                          void* stream);
+
+// Column-major rocBLAS GEMM, bf16 A and B, fp32 C = D (in place when beta != 0):
+// D[m x n] = op(A) op(B) + beta D, op = transpose when the flag is set.
+int gemm_bf16_f32(void* handle, bool trans_a, bool trans_b, int m, int n, int k, const uint16_t* a, int lda,
+                  const uint16_t* b, int ldb, float beta, float* d, int ldd, void* stream);
+// The same with beta = 0 over `batch` equal problems at fixed strides.
+int gemm_bf16_f32_batched(void* handle, bool trans_a, bool trans_b, int m, int n, int k, const uint16_t* a,
+                          int lda, int64_t stride_a, const uint16_t* b, int ldb, int64_t stride_b, float* d, int ldd,
+                          int64_t stride_d, int batch, void* stream);
+
 int launch_rmsnorm(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t rows, int dim, float eps,
                    void* stream);
 

@@ -228,3 +228,36 @@ def test_attention_backward_checks(lib):
     assert _bwd(lib, ws=None) == E.TG_EWORKSPACE
     assert _bwd(lib, ws_bytes=need - 1) == E.TG_EWORKSPACE
     assert _bwd(lib, ws=A + 16) == E.TG_EALIGN  # workspace must be 256-byte aligned
+
+
+def _gbw(lib, blas=A, n=64, d=128, hd=64, k=8, er=1e-6, es=1e-6, ws=A, ws_bytes=WS, **over):
+    p = dict(resid=A, w1=A, b1=None, w2=A, s=A, dsk=A, idx=A, dres=A, dw1=A, db1=A, dw2=A, db2=A)
+    p.update(over)
+    return lib.tg_gate_score_bwd(blas, p["resid"], p["w1"], p["b1"], p["w2"], n, d, hd, er, es, p["s"], p["dsk"],
+                                 p["idx"], k, p["dres"], p["dw1"], p["db1"], p["dw2"], p["db2"], ws, ws_bytes, None)
+
+
+def test_gate_score_backward_checks(lib):
+    E = binding
+    need = lib.tg_gate_score_bwd_workspace_bytes(64, 128, 64)
+    assert 0 < need <= WS
+    assert lib.tg_gate_score_bwd_workspace_bytes(16384, 2048, 256) > lib.tg_gate_score_bwd_workspace_bytes(64, 2048, 256)
+    assert lib.tg_gate_score_bwd_workspace_bytes(-1, 128, 64) == 0
+    assert _gbw(lib, n=0, k=0) == E.TG_OK  # no tokens: no-op
+    assert _gbw(lib, blas=None) == E.TG_EINVAL  # no rocBLAS handle
+    assert _gbw(lib, n=-1) == E.TG_EINVAL
+    assert _gbw(lib, k=65) == E.TG_EINVAL  # more kept than tokens
+    assert _gbw(lib, er=-1.0) == E.TG_EINVAL
+    assert _gbw(lib, es=float("nan")) == E.TG_EINVAL
+    assert _gbw(lib, hd=96) == E.TG_EUNSUPPORTED
+    assert _gbw(lib, d=96) == E.TG_EUNSUPPORTED
+    assert _gbw(lib, d=8192) == E.TG_EUNSUPPORTED
+    assert _gbw(lib, resid=None) == E.TG_EINVAL
+    assert _gbw(lib, db2=None) == E.TG_EINVAL
+    assert _gbw(lib, idx=None) == E.TG_EINVAL  # k > 0 needs the kept indices
+    assert _gbw(lib, resid=M) == E.TG_EALIGN
+    assert _gbw(lib, dres=A + 4) == E.TG_EALIGN
+    assert _gbw(lib, dw1=A + 8) == E.TG_EALIGN
+    assert _gbw(lib, ws=None) == E.TG_EWORKSPACE
+    assert _gbw(lib, ws_bytes=need - 1) == E.TG_EWORKSPACE
+    assert _gbw(lib, ws=A + 16) == E.TG_EALIGN
