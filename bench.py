@@ -241,6 +241,7 @@ def main():
     prefill = None if (args.no_prefill or args.workload != "n16k") else prefill_compare(tg, torch, dev, shp, seed)
     backward = None if (args.no_attn_sweep or args.workload != "n16k") else \
         {"attention": attn_backward(tg, torch, dev, shp), "scorer": gate_backward(tg, torch, dev, shp)}
+    hybrid = None if (args.no_attn_sweep or args.workload != "n16k") else hybrid_mixer(tg, torch, dev, shp)
 
     result = {
         "metric": METRIC,
@@ -267,6 +268,7 @@ def main():
         "attn_sweep": sweep,
         "prefill": prefill,
         "backward": backward,
+        "hybrid_mixer": hybrid,
         "cpu_baseline": None,
     }
 
@@ -417,6 +419,35 @@ def gate_backward(tg, torch, dev, shape, reps=5):
     return {"n": n, "us": round(us, 1), "tflops": round(flop / us / 1e6, 1),
             "mfma_frac": round(flop / us / 1e6 / PEAK_BF16_TFLOPS, 4), "hbm_gbs": round(byts / us / 1e3, 1),
             "hbm_frac": round(byts / us / 1e3 / PEAK_HBM_GBS, 4)}
+
+
+def hybrid_mixer(tg, torch, dev, shape, reps=5):
+    """tg_gated_delta_rule with 16 heads of 128 x 128 state over the kept
+    tokens (K) and over the whole prompt (N): what pruning saves in an upper
+    recurrent layer of the hybrid backbone."""
+    heads, dk = 16, 128
+    res = {}
+    for name, t in (("kept", shape.k), ("full", shape.n)):
+        g = torch.Generator(device=dev)
+        g.manual_seed(t)
+        qk = torch.nn.functional.normalize(torch.randn(2, t, heads, dk, generator=g, device=dev), dim=-1)
+        q, k = qk[0].to(torch.bfloat16), qk[1].to(torch.bfloat16)
+        v = torch.randn(t, heads, dk, generator=g, device=dev).to(torch.bfloat16)
+        alpha = 0.9 + 0.1 * torch.rand(t, heads, generator=g, device=dev)
+        beta = torch.rand(t, heads, generator=g, device=dev)
+        out = torch.empty(t, heads, dk, dtype=torch.float32, device=dev)
+        tg.tg_gated_delta_rule(q, k, v, alpha, beta, out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            tg.tg_gated_delta_rule(q, k, v, alpha, beta, out)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        res[name] = {"tokens": t, "us": round(us, 1), "ns_per_token": round(us * 1e3 / t, 1)}
+    res["speedup"] = round(res["full"]["us"] / res["kept"]["us"], 2)
+    return res
 
 
 def attn_sweep(tg, torch, dev, shp, ks=(4096, 8192, 16384), reps=10):

@@ -10,6 +10,8 @@
  *   tg_rope, tg_rope_qk -> (auxiliary) rotary embedding at the original positions;
  *   tg_gated_attention -> causal attention over the kept tokens only, with a
  *                         per-key importance bias and a per-query temperature.
+ * Training-side gradients: tg_gated_attention_bwd, tg_gate_score_bwd.  The
+ * hybrid backbone's recurrent mixer over the kept tokens: tg_gated_delta_rule.
  * The rest of an upper decoder layer on the kept rows (see the section at the
  * end): tg_rmsnorm, tg_swiglu, and tg_linear (a rocBLAS GEMM through a handle
  * from tg_blas_create).
@@ -259,6 +261,33 @@ int tg_gate_score_bwd(void* blas, const tg_bf16* resid, const tg_bf16* w1, const
                       int64_t n, int32_t d, int32_t hd, float eps_row, float eps_seq, const float* score_raw,
                       const float* dscore_kept, const int32_t* kept_idx, int64_t k, float* dresid, float* dw1,
                       float* db1, float* dw2, float* db2, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * tg_gated_delta_rule -- the recurrent mixer of the hybrid backbone over a
+ * token sequence [P1 hybrid][P3 hybrid FAQ][P5 hybrid state]: in a hybrid
+ * (Gated-DeltaNet + attention) backbone the gate may follow a recurrent
+ * layer, and above it the recurrent mixers see only the kept tokens, in
+ * order, while the lower layers' state has read every token.  The mixer's
+ * core is the gated delta rule (Yang, Kautz and Hatamizadeh, "Gated Delta
+ * Networks", 2024), per v head h with state S [dv, dk]:
+ *   S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *   out_t = S_t q_t.
+ * q, k   [n, hk, dk] bf16 (16-byte aligned); v head h uses q/k head
+ *        h / (hv / hk).  The mixer normalises q and k before this step; keys
+ *        with |k| > 1 make the recurrence expansive.
+ * v      [n, hv, dv] bf16.   alpha, beta [n, hv] fp32 (decay in (0, 1],
+ *        write strength in [0, 1]).
+ * state_in  [hv, dv, dk] fp32 or NULL (= zeros); state_out [hv, dv, dk] fp32
+ *        or NULL (the state after the last token; may equal state_in).
+ *        Both 16-byte aligned.
+ * out    [n, hv, dv] fp32.
+ * Supported: dk, dv in {64, 128}; hv % hk == 0.  n == 0 copies state_in (or
+ * zeros) to state_out if given.  fp32 state and arithmetic; deterministic.
+ * The scan is sequential over tokens: one wave per 8 rows of a head's state.
+ */
+int tg_gated_delta_rule(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, const float* alpha, const float* beta,
+                        const float* state_in, int64_t n, int32_t hk, int32_t hv, int32_t dk, int32_t dv, float* out,
+                        float* state_out, void* stream);
 
 /*
  * ---- Upper decoder layer on the kept rows ----

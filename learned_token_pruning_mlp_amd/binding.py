@@ -30,7 +30,7 @@ EXPORTS = ("tg_status_string", "tg_abi_version", "tg_workspace_bytes", "tg_gate_
            "tg_select_topk", "tg_compact", "tg_rope", "tg_rope_qk", "tg_gated_attention",
            "tg_rmsnorm", "tg_swiglu", "tg_blas_create", "tg_blas_destroy", "tg_linear",
            "tg_attention_bwd_workspace_bytes", "tg_gated_attention_bwd", "tg_gate_score_bwd_workspace_bytes",
-           "tg_gate_score_bwd")
+           "tg_gate_score_bwd", "tg_gated_delta_rule")
 
 
 class TgGather(ctypes.Structure):
@@ -94,6 +94,8 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
     L.tg_gate_score_bwd.argtypes = [P, P, P, P, P, I64, I32, I32, F, F, P, P, P, I64, P, P, P, P, P, P,
                                     ctypes.c_size_t, P]
     L.tg_gate_score_bwd.restype = ctypes.c_int
+    L.tg_gated_delta_rule.argtypes = [P, P, P, P, P, P, I64, I32, I32, I32, I32, P, P, P]
+    L.tg_gated_delta_rule.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -370,3 +372,22 @@ def tg_gate_score_bwd(handle: BlasHandle, resid: torch.Tensor, w1: torch.Tensor,
         handle.value, _ptr(resid), _ptr(w1), _ptr(b1), _ptr(w2), n, d, hd, float(eps_row), float(eps_seq),
         _ptr(score_raw), _ptr(dscore_kept), _ptr(kept_idx), k, _ptr(dresid), _ptr(dw1), _ptr(db1), _ptr(dw2),
         _ptr(db2), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def tg_gated_delta_rule(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
+                        out: torch.Tensor, state_in: Optional[torch.Tensor] = None,
+                        state_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Gated delta rule over the token sequence (fp32 out and state)."""
+    n, hk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    _need(q, "q", torch.bfloat16, (n, hk, dk))
+    _need(k, "k", torch.bfloat16, (n, hk, dk))
+    _need(v, "v", torch.bfloat16, (n, hv, dv))
+    _need(alpha, "alpha", torch.float32, (n, hv))
+    _need(beta, "beta", torch.float32, (n, hv))
+    _need(out, "out", torch.float32, (n, hv, dv))
+    _need(state_in, "state_in", torch.float32, (hv, dv, dk), optional=True)
+    _need(state_out, "state_out", torch.float32, (hv, dv, dk), optional=True)
+    _check("tg_gated_delta_rule", load().tg_gated_delta_rule(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in), n, hk, hv, dk, dv, _ptr(out),
+        _ptr(state_out), _stream(stream)))

@@ -21,7 +21,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ROCM_LIB = "/opt/rocm/lib"
 ARCH = "gfx950"
 
-SOURCES = ["k_gate.hip", "k_select.hip", "k_compact.hip", "k_rope.hip", "k_attn.hip", "k_layer.hip", "k_attn_bwd.hip", "k_gate_bwd.hip", "tg_blas.cpp",
+SOURCES = ["k_gate.hip", "k_select.hip", "k_compact.hip", "k_rope.hip", "k_attn.hip", "k_layer.hip", "k_attn_bwd.hip", "k_gate_bwd.hip", "k_gdn.hip", "tg_blas.cpp",
            "tg_api.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC, "-Wall",

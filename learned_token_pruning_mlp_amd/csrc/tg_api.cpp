@@ -187,6 +187,19 @@ int tg_gate_score_bwd(void* blas, const tg_bf16* resid, const tg_bf16* w1, const
                                       kept_idx, k, dresid, dw1, db1, dw2, db2, workspace, stream);
 }
 
+int tg_gated_delta_rule(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, const float* alpha, const float* beta,
+                        const float* state_in, int64_t n, int32_t hk, int32_t hv, int32_t dk, int32_t dv, float* out,
+                        float* state_out, void* stream) {
+    if (n < 0 || n > kMaxRows || hk < 1 || hv < 1 || hv % hk != 0) return TG_EINVAL;
+    if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return TG_EUNSUPPORTED;
+    if (n * (int64_t)hv * dv >= (int64_t)1 << 40) return TG_EUNSUPPORTED;
+    if (n == 0 && !state_out) return TG_OK;
+    if (n > 0 && (!q || !k || !v || !alpha || !beta || !out)) return TG_EINVAL;
+    if ((n > 0 && (!aligned(q, 16) || !aligned(k, 16))) || !aligned(state_in, 16) || !aligned(state_out, 16))
+        return TG_EALIGN;
+    return tgi::launch_gated_delta_rule(q, k, v, alpha, beta, state_in, n, hk, hv, dk, dv, out, state_out, stream);
+}
+
 int tg_rmsnorm(const tg_bf16* x, const tg_bf16* weight, tg_bf16* y, int64_t rows, int32_t dim, float eps,
                void* stream) {
     if (rows < 0 || rows > kMaxRows || dim < 8 || dim > 4096 || dim % 8 != 0) return TG_EINVAL;

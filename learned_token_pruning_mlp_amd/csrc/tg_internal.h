@@ -163,6 +163,10 @@ int gemm_bf16_f32_batched(void* handle, bool trans_a, bool trans_b, int m, int n
                           int lda, int64_t stride_a, const uint16_t* b, int ldb, int64_t stride_b, float* d, int ldd,
                           int64_t stride_d, int batch, void* stream);
 
+int launch_gated_delta_rule(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* alpha,
+                            const float* beta, const float* state_in, int64_t n, int hk, int hv, int dk, int dv,
+                            float* out, float* state_out, void* stream);
+
 int launch_rmsnorm(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t rows, int dim, float eps,
                    void* stream);
 

@@ -261,3 +261,22 @@ def test_gate_score_backward_checks(lib):
     assert _gbw(lib, ws=None) == E.TG_EWORKSPACE
     assert _gbw(lib, ws_bytes=need - 1) == E.TG_EWORKSPACE
     assert _gbw(lib, ws=A + 16) == E.TG_EALIGN
+
+
+def test_gated_delta_rule_checks(lib):
+    E = binding
+
+    def call(n=16, hk=2, hv=4, dk=128, dv=128, q=A, k=A, v=A, al=A, be=A, si=None, out=A, so=None):
+        return lib.tg_gated_delta_rule(q, k, v, al, be, si, n, hk, hv, dk, dv, out, so, None)
+    assert call(n=0) == E.TG_OK  # no tokens, no state out: no-op
+    assert call(n=-1) == E.TG_EINVAL
+    assert call(hk=3, hv=4) == E.TG_EINVAL
+    assert call(hk=0) == E.TG_EINVAL
+    assert call(dk=96) == E.TG_EUNSUPPORTED
+    assert call(dv=256) == E.TG_EUNSUPPORTED
+    assert call(q=None) == E.TG_EINVAL
+    assert call(be=None) == E.TG_EINVAL
+    assert call(out=None) == E.TG_EINVAL
+    assert call(k=M) == E.TG_EALIGN
+    assert call(si=A + 4) == E.TG_EALIGN
+    assert call(so=A + 8) == E.TG_EALIGN
