@@ -281,9 +281,11 @@ int tg_gate_score_bwd(void* blas, const tg_bf16* resid, const tg_bf16* w1, const
  *        or NULL (the state after the last token; may equal state_in).
  *        Both 16-byte aligned.
  * out    [n, hv, dv] fp32.
- * Supported: dk, dv in {64, 128}; hv % hk == 0.  n == 0 copies state_in (or
- * zeros) to state_out if given.  fp32 state and arithmetic; deterministic.
- * The scan is sequential over tokens: one wave per 8 rows of a head's state.
+ * Supported: dk, dv in {64, 128}; hv % hk == 0; n * hk * dk and n * hv * dv
+ * below 2^30.  n == 0 copies state_in (or zeros) to state_out if given.  fp32
+ * state and arithmetic; deterministic.  The scan is sequential over tokens:
+ * one workgroup per 8 rows of a head's state, tokens staged through LDS in
+ * chunks of 32.
  */
 int tg_gated_delta_rule(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, const float* alpha, const float* beta,
                         const float* state_in, int64_t n, int32_t hk, int32_t hv, int32_t dk, int32_t dv, float* out,

@@ -192,7 +192,9 @@ int tg_gated_delta_rule(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, co
                         float* state_out, void* stream) {
     if (n < 0 || n > kMaxRows || hk < 1 || hv < 1 || hv % hk != 0) return TG_EINVAL;
     if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return TG_EUNSUPPORTED;
-    if (n * (int64_t)hv * dv >= (int64_t)1 << 40) return TG_EUNSUPPORTED;
+    // (token rows are read through 32-bit buffer offsets)
+    if (n * (int64_t)hk * dk * 2 >= (int64_t)1 << 31 || n * (int64_t)hv * dv * 2 >= (int64_t)1 << 31)
+        return TG_EUNSUPPORTED;
     if (n == 0 && !state_out) return TG_OK;
     if (n > 0 && (!q || !k || !v || !alpha || !beta || !out)) return TG_EINVAL;
     if ((n > 0 && (!aligned(q, 16) || !aligned(k, 16))) || !aligned(state_in, 16) || !aligned(state_out, 16))
