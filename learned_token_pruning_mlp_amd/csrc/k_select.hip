@@ -186,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void select_topk_regs(const float* __rest
         __syncthreads();
     };
 
-    // Round 1: forced count and the histogram of the top 11 bits.
+    // Radix pass 1: forced count and the histogram of the top 11 bits.
     for (int b = tid * 4; b < kCopies * kBins; b += kThreads * 4)
         *reinterpret_cast<uint4*>(&histc[0][0] + b) = uint4{0u, 0u, 0u, 0u};
     uint32_t key[KPT];
@@ -429,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void select_topk_block(const float* __res
 
     uint32_t T = 0xffffffffu, m = 0;  // R == 0: no prunable token is taken
     if (R > 0) {
-        // Round 1: top 11 bits.
+        // Radix pass 1: top 11 bits.
         pick_bin((uint32_t)R, kBins);
         uint32_t prefix = ctl[0] << 21, pmask = 0x7ffu << 21, remaining = ctl[1];
         const uint32_t bucket = hist[ctl[0]];
