@@ -84,9 +84,9 @@ __global__ __launch_bounds__(64 * kWaves) void gdn_scan(const uint16_t* __restri
                                                         const uint16_t* __restrict__ v,
                                                         const float* __restrict__ alpha,
                                                         const float* __restrict__ beta,
-                                                        const float* __restrict__ state_in, int64_t n, int hk,
-                                                        int hv, float* __restrict__ out,
-                                                        float* __restrict__ state_out) {
+                                                        const float* state_in, int64_t n, int hk, int hv,
+                                                        float* __restrict__ out,
+                                                        float* state_out) {  // state_out may be state_in
     using C = Gdn<DK, DV>;
     constexpr int CPL = C::CPL;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::STAGE];

@@ -90,3 +90,16 @@ def test_gated_delta_rule_state_carries_over_a_split():
     o2, s2 = _run(q[m:], k[m:], v[m:], alpha[m:], beta[m:], s1.astype(np.float32))
     assert np.array_equal(np.concatenate([o1, o2]), o_all)
     assert np.array_equal(s2, s_all)
+
+
+def test_gated_delta_rule_state_in_place():
+    """state_out may be the state_in buffer: the state is updated in place."""
+    q, k, v, alpha, beta, s0 = _case(9, 150, 2, 4, 128, 128, True)
+    gu.say("gated delta rule in-place state")
+    want_o, want_s = _run(q, k, v, alpha, beta, s0)
+    st = gu.f32(s0)
+    out = torch.empty(150, 4, 128, dtype=torch.float32, device=gu.dev())
+    tg.tg_gated_delta_rule(gu.bf16(q), gu.bf16(k), gu.bf16(v), gu.f32(alpha), gu.f32(beta), out, st, st)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), want_o)
+    assert np.array_equal(st.cpu().numpy().astype(np.float64), want_s)
