@@ -41,6 +41,9 @@
  *    negative status means nothing was enqueued (except TG_EDEVICE, which
  *    reports a launch failure).
  *  - Layouts are row-major and dense unless a stride is given.
+ *  - Outputs must not overlap inputs, the workspace or each other, except
+ *    where an entry point says otherwise (in-place RoPE, tg_linear's
+ *    residual, tg_gated_delta_rule's state).
  *  - Batch size is 1 (one prompt per call), as in the pages' measurements.
  */
 #ifndef TOKENGATE_H
