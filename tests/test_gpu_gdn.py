@@ -103,3 +103,27 @@ def test_gated_delta_rule_state_in_place():
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy().astype(np.float64), want_o)
     assert np.array_equal(st.cpu().numpy().astype(np.float64), want_s)
+
+
+def test_gated_delta_rule_over_compacted_kept_tokens():
+    """Above the gate the recurrent mixer sees only the kept tokens, in order:
+    q, k, v and the gates gathered by tg_compact, then scanned, equal the
+    oracle's scan over the kept subsequence (and, bit for bit, a scan over
+    the same rows gathered on the host)."""
+    n, K = 1024, 192
+    q, k, v, alpha, beta, _ = _case(10, n, 2, 4, 128, 128, False)
+    kept = np.sort(np.random.default_rng(11).choice(n, size=K, replace=False)).astype(np.int32)
+    dev = gu.dev()
+    src = [gu.bf16(q), gu.bf16(k), gu.bf16(v), gu.f32(alpha), gu.f32(beta)]
+    dst = [torch.empty((K,) + tuple(t.shape[1:]), dtype=t.dtype, device=dev) for t in src]
+    gu.say("gated delta rule over compacted kept tokens n=1024 K=192")
+    tg.tg_compact(gu.i32(kept), n, None, None, None, None, None, None, extra=list(zip(src, dst)))
+    out = torch.empty(K, 4, 128, dtype=torch.float32, device=dev)
+    tg.tg_gated_delta_rule(*dst, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    w = oracle.widen_bf16
+    want, _ = gdn.gated_delta_rule(w(q[kept]), w(k[kept]), w(v[kept]), alpha[kept], beta[kept])
+    assert _rel(got, want) <= TOL
+    host_o, _ = _run(q[kept], k[kept], v[kept], alpha[kept], beta[kept], None)
+    assert np.array_equal(got, host_o)
