@@ -22,14 +22,18 @@
 //    lane owns a query column, so the row values are per-lane scalars), then
 //    dq^T += K^T.dU^T with K^T read from LDS by the transposing read, and the
 //    per-row partials of dlambda and of sum_j dU s_j.
-//  * bwd_dkv: one wave per (kv head, 32-key block) walks the query blocks
-//    from the diagonal on, for every q head of the group: S = Q.K^T and
+//  * bwd_dkv: one wave per (kv head, 32-key block, share of the group's q
+//    heads) walks the query blocks from the diagonal on: S = Q.K^T and
 //    dP = dO.V^T (a lane owns a key column), then dv^T += dO^T.P and
 //    dk^T += Q^T.dU with Q^T and dO^T read transposed from LDS, and the
-//    per-key partial of ds.
-//  * bwd_reduce: the per-row and per-key partials summed in a fixed order.
+//    per-key partial of ds; the waves sharing a key block add their partial
+//    dk, dv and ds in LDS in a fixed order.
+//  * bwd_reduce: the per-kv-head and per-block partials summed in a fixed
+//    order.
 // No atomics: results are deterministic.  P and dU enter the matrix cores as
-// bf16 (fp32 accumulation).  Each wave stages its blocks in LDS of its own.
+// bf16 (fp32 accumulation).  Each wave streams its blocks through two LDS
+// stages of its own, filled by direct loads one block ahead; rows past the
+// end read as zeros through the buffer bounds.
 #include <hip/hip_runtime.h>
 
 #include "tg_device.h"
