@@ -21,7 +21,7 @@
 //    to the diagonal: S^T = K.Q^T and dP^T = V.dO^T on the matrix cores (a
 //    lane owns a query column, so the row values are per-lane scalars), then
 //    dq^T += K^T.dU^T with K^T read from LDS by the transposing read, and the
-//    per-row partials of dlambda and of sum_j dU s_j.
+//    per-(head, query block) partials of dlambda and of sum_j dU s_j.
 //  * bwd_dkv: one wave per (kv head, 32-key block, share of the group's q
 //    heads) walks the query blocks from the diagonal on: S = Q.K^T and
 //    dP = dO.V^T (a lane owns a key column), then dv^T += dO^T.P and
