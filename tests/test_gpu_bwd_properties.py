@@ -1,0 +1,76 @@
+"""Backward passes at full size, checked through properties that hold at any
+size (the fp64 oracle would be too slow here).
+
+* Attention backward at K = 8192 (Qwen3-1.7B heads): adding a constant to
+  every key score adds the same constant to every logit of a row, so the
+  output is unchanged and the score gradient sums to zero.  The GPU sum is
+  held to 1e-3 of sum |ds| (fp32 terms of both signs, bf16 P and dU).
+* Scorer backward at N = 16384, d = 2048, hd = 256 with eps_row = 0: a
+  token's score depends on its residual only through h_i / |h_i|, so every
+  row of the residual gradient is orthogonal to its row: |dh_i . h_i| is held
+  to 2e-2 of |dh_i| |h_i| (dz enters the GEMM in bf16, and the dot product
+  cancels two terms of similar size).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as gu
+from learned_token_pruning_mlp_amd import binding as tg
+
+pytestmark = pytest.mark.gpu
+
+
+def test_attention_backward_score_gradient_sums_to_zero_at_8k():
+    K, hq, hkv, D = 8192, 16, 8, 128
+    dev = gu.dev()
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    bf = lambda *s: torch.randn(*s, generator=g, device=dev).to(torch.bfloat16)  # noqa: E731
+    q, k, v, do = bf(K, hq, D), bf(K, hkv, D), bf(K, hkv, D), bf(K, hq, D)
+    ks = torch.randn(K, generator=g, device=dev)
+    gains = torch.rand(hq, generator=g, device=dev) + 0.5
+    pos = torch.arange(K, dtype=torch.int32, device=dev) * 2
+    f32 = dict(dtype=torch.float32, device=dev)
+    o = [torch.empty(K, hq, D, **f32), torch.empty(K, hkv, D, **f32), torch.empty(K, hkv, D, **f32),
+         torch.empty(K, **f32), torch.empty(hq, **f32), torch.empty(1, **f32)]
+    gu.say("attention backward K=8192 score-shift property")
+    tg.tg_gated_attention_bwd(q, k, v, ks, gains, 0.1, pos, do, *o)
+    torch.cuda.synchronize()
+    ds = o[3].double()
+    assert torch.isfinite(ds).all()
+    assert abs(ds.sum().item()) <= 1e-3 * ds.abs().sum().item()
+    assert ds.abs().sum().item() > 0
+
+
+def test_scorer_backward_rows_orthogonal_at_16k():
+    n, d, hd, K = 16384, 2048, 256, 2048
+    dev = gu.dev()
+    g = torch.Generator(device=dev)
+    g.manual_seed(6)
+    resid = torch.randn(n, d, generator=g, device=dev).to(torch.bfloat16)
+    w1 = (torch.randn(hd, d, generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    b1 = (torch.randn(hd, generator=g, device=dev) * 0.5).to(torch.bfloat16)
+    w2 = (torch.randn(hd, generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    f32 = dict(dtype=torch.float32, device=dev)
+    snorm, sraw = torch.empty(n, **f32), torch.empty(n, **f32)
+    ws = tg.workspace(n)
+    gu.say("scorer backward n=16384 row-orthogonality property")
+    tg.tg_gate_score(resid, w1, b1, w2, 0.0, 0.0, 1e-6, snorm, sraw, ws)
+    kept = torch.randperm(n, generator=g, device=dev)[:K].sort().values.to(torch.int32)
+    dsk = torch.randn(K, generator=g, device=dev)
+    out = [torch.empty(n, d, **f32), torch.empty(hd, d, **f32), torch.empty(hd, **f32), torch.empty(hd, **f32),
+           torch.empty(1, **f32)]
+    blas = tg.BlasHandle()
+    try:
+        tg.tg_gate_score_bwd(blas, resid, w1, b1, w2, 0.0, 1e-6, sraw, dsk, kept, *out)
+        torch.cuda.synchronize()
+    finally:
+        blas.close()
+    dh = out[0].double()
+    h = resid.double()
+    dots = (dh * h).sum(dim=1).abs()
+    scale = dh.norm(dim=1) * h.norm(dim=1)
+    assert torch.isfinite(dh).all()
+    assert (dots <= 2e-2 * scale + 1e-30).all(), float((dots / scale.clamp_min(1e-30)).max())
+    assert dh.abs().max().item() > 0
