@@ -1,21 +1,25 @@
 """Throughput of the TokenGate gated-prefill hot path on one MI355X.
 
 One step = one pass of the whole path over one prompt (batch 1):
-    tg_gate_score -> tg_select_topk -> tg_compact -> tg_rope_qk -> tg_gated_attention
-at the Qwen3-1.7B-shaped gate layer: d_model 2048, scorer 2048->256->1,
-N = 16384 tokens (last 64 forced-keep), K = 2048 kept, 16 q / 8 kv heads,
-head_dim 128, one upper layer of token-gated attention.  Inputs are seeded
-synthetic tensors already resident in HBM; the residual is rotated over six
-copies (384 MB > the 256 MB MALL) so the scorer reads it from HBM.
+    tg_gate_score -> tg_select_topk -> tg_compact -> (tg_rope_qk -> tg_gated_attention) per upper layer
+Default workload (n16k): the Qwen3-1.7B-shaped gate layer, d_model 2048,
+scorer 2048->256->1, N = 16384 tokens (last 64 forced-keep), K = 2048 kept,
+16 q / 8 kv heads, head_dim 128, one upper layer of token-gated attention.
+--workload selects the other sizes: N = 32768 with K = 1024 / 4096 / 8192
+(Student-t scores into select), N = 131072 with K = 8192 over 26 upper
+layers (and the lower layers' K/V trimmed by the compaction), and K = N.
+Inputs are seeded synthetic tensors already resident in HBM; the residual is
+rotated over copies whose total exceeds the 256 MB MALL, so the scorer reads
+it from HBM.
 
-Prints one JSON line.  `value` = N / (ms_per_step) in tokens/s.
+Prints one JSON line.  `value` = N / ms_per_step in tokens/s, where
+ms_per_step is the wall time of exactly --steps steps over their count.
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -28,7 +32,6 @@ sys.path.insert(0, ROOT)
 METRIC = "gated-prefill tokens/s at N=16k Qwen3-1.7B shape; attn MFMA % of bf16 peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-N_RESID_COPIES = 6
 
 
 def parse():
@@ -36,10 +39,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="n16k",
-                   choices=["n16k", "n32k-k1024", "n32k-k4096", "n32k-k8192", "n128k", "full16k", "tiny"])
+    p.add_argument("--workload", default="n16k", choices=sorted(WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
-    p.add_argument("--no-attn-sweep", action="store_true", help="skip the attention-only K sweep")
+    p.add_argument("--no-attn-sweep", action="store_true",
+                   help="skip the attention-only K sweep, the backward passes and the recurrent mixer")
     p.add_argument("--no-prefill", action="store_true",
                    help="skip the whole-prompt comparison (28 decoder layers, full against gated)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
@@ -47,21 +50,32 @@ def parse():
     return p.parse_args()
 
 
-def workload(name):
+# name -> (shape factory, description, upper layers, Student-t scores for select/compact/attention)
+def _shape(n, k, n_forced=64, layout="tail"):
     from learned_token_pruning_mlp_amd import synth
     base = synth.QWEN3_1P7B_N16K
-    if name == "n16k":
-        return base, "qwen3-1.7b gate layer, N=16384, F=64, K=2048, 1 upper layer"
-    if name.startswith("n32k"):
-        k = int(name.split("k")[-1])
-        shp = synth.GateShape(**{**base.__dict__, "n": 32768, "k": k})
-        return shp, f"qwen3-1.7b gate layer, N=32768, F=64, K={k}, 1 upper layer"
-    if name == "n128k":
-        return synth.QWEN3_1P7B_N128K, "qwen3-1.7b gate layer, N=131072, F=128, K=8192, 1 upper layer"
-    if name == "full16k":
-        shp = synth.GateShape(**{**base.__dict__, "k": base.n})
-        return shp, "qwen3-1.7b gate layer, N=16384, K=N (no pruning), 1 upper layer"
-    return synth.TINY, "tiny gate layer, N=512, d=256, K=128"
+    return synth.GateShape(**{**base.__dict__, "n": n, "k": k, "n_forced": n_forced, "forced_layout": layout})
+
+
+WORKLOADS = {
+    "tiny": (lambda: __import__("learned_token_pruning_mlp_amd.synth", fromlist=["TINY"]).TINY,
+             "tiny gate layer, N=512, d=256, F=32, K=128, 1 upper layer", 1, False),
+    "n16k": (lambda: _shape(16384, 2048),
+             "qwen3-1.7b gate layer, N=16384, F=64, K=2048, 1 upper layer", 1, False),
+    "n32k-k1024": (lambda: _shape(32768, 1024),
+                   "qwen3-1.7b gate layer, N=32768, F=64, K=1024, 1 upper layer, Student-t(3) scores", 1, True),
+    "n32k-k4096": (lambda: _shape(32768, 4096),
+                   "qwen3-1.7b gate layer, N=32768, F=64, K=4096, 1 upper layer, Student-t(3) scores", 1, True),
+    "n32k-k8192": (lambda: _shape(32768, 8192),
+                   "qwen3-1.7b gate layer, N=32768, F=64, K=8192, 1 upper layer, Student-t(3) scores", 1, True),
+    "n128k": (lambda: _shape(131072, 8192, 128, "scatter_tail"),
+              "qwen3-1.7b gate layer, N=131072, F=128 scattered over the last 1024, K=8192, 26 upper layers of "
+              "kept-row K/V, 2 lower layers' K/V trimmed", 26, False),
+    "full16k": (lambda: _shape(16384, 16384),
+                "qwen3-1.7b gate layer, N=16384, F=64, K=N (no pruning), 1 upper layer", 1, False),
+}
+N_LOWER_KV_LAYERS = 2   # layers below the gate whose full-length K/V the n128k step trims
+EV_STRIDE = 8           # the dominant kernel is bracketed by events on every 8th timed step
 
 
 def attn_flops(shp):
@@ -69,13 +83,14 @@ def attn_flops(shp):
 
 
 def gate_bytes(shp):
-    # residual read once, W1 once, b1/w2 tiny, raw + normalised scores written/read
+    # residual read once, W1 once, raw scores written and read back, normalised scores written
     return shp.n * shp.d * 2 + shp.hd * shp.d * 2 + shp.n * 4 * 3
 
 
-def compact_bytes(shp):
-    # kept residual rows read + written, index, position and score per kept row
-    return shp.k * (shp.d * 2 * 2 + 4 * 4)
+def compact_bytes(shp, extra_row_bytes=0):
+    # kept residual rows read + written, index read, position and score read + written,
+    # plus each extra stream's kept rows read + written
+    return shp.k * (shp.d * 2 * 2 + 4 * 5 + 2 * extra_row_bytes)
 
 
 def source_sha(name):
@@ -100,6 +115,92 @@ def traffic_for(kernel_file, workload_name):
         return None
 
 
+class Path:
+    """Inputs resident in HBM and one step of the whole path over them:
+    tg_gate_score -> tg_select_topk -> tg_compact -> (tg_rope_qk ->
+    tg_gated_attention) for each upper layer."""
+
+    STAGES = ["gate_score", "select_topk", "compact", "rope", "gated_attention"]
+
+    def __init__(self, tg, torch, dev, name, seed):
+        from learned_token_pruning_mlp_amd import synth
+        make, self.desc, self.layers, t_scores = WORKLOADS[name]
+        self.shp = shp = make()
+        self.name, self.tg, self.torch = name, tg, torch
+        self.inp = inp = synth.gate_inputs(shp, seed)
+        bf = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)  # noqa
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        # the residual rotates over copies whose total exceeds the 256 MB MALL,
+        # so the scorer reads it from HBM on every step
+        copies = max(2, min(6, -(-(384 << 20) // (shp.n * shp.d * 2))))
+        self.resid = [bf(inp.resid)] + [torch.randn((shp.n, shp.d), generator=g, device=dev).to(torch.bfloat16)
+                                        for _ in range(copies - 1)]
+        self.w1, self.w2 = bf(inp.w1), bf(inp.w2)
+        self.forced = torch.from_numpy(inp.forced).to(dev)
+        self.pos = torch.from_numpy(inp.pos).to(dev)
+        n, k = shp.n, shp.k
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.s_norm = torch.empty(n, **f32)
+        # Student-t(3) scores drawn directly for select, compaction and attention
+        self.t_scores = torch.from_numpy(synth.student_t_scores(n, seed)).to(dev) if t_scores else None
+        self.ws = tg.workspace(n, dev)
+        self.kept = torch.empty(k, dtype=torch.int32, device=dev)
+        self.resid_k = torch.empty((k, shp.d), dtype=torch.bfloat16, device=dev)
+        self.pos_k = torch.empty(k, dtype=torch.int32, device=dev)
+        self.score_k = torch.empty(k, **f32)
+        self.a = a = synth.attn_inputs(k, shp.hq, shp.hkv, shp.head_dim, seed)
+        self.gains = torch.from_numpy(a.gains).to(dev)
+        L = self.layers
+        if L == 1:
+            self.q, self.kk, self.vv = [bf(a.q)], [bf(a.k)], [bf(a.v)]
+        else:
+            # per upper layer: its q and its kept-row K/V, stacked [L, K, Hkv, D]
+            self.q = [torch.randn((k, shp.hq, shp.head_dim), generator=g, device=dev).to(torch.bfloat16)
+                      for _ in range(L)]
+            kv = [torch.randn((L, k, shp.hkv, shp.head_dim), generator=g, device=dev).to(torch.bfloat16)
+                  for _ in range(2)]
+            self.kk, self.vv = list(kv[0]), list(kv[1])
+        self.extra = []
+        if name == "n128k":
+            # the lower layers' full-length K and V, trimmed to the kept rows
+            for _ in range(2 * N_LOWER_KV_LAYERS):
+                src = torch.randn((n, shp.hkv, shp.head_dim), generator=g, device=dev).to(torch.bfloat16)
+                self.extra.append((src, torch.empty((k, shp.hkv, shp.head_dim), dtype=torch.bfloat16, device=dev)))
+        self.out = torch.empty((k, shp.hq, shp.head_dim), dtype=torch.bfloat16, device=dev)
+        self.stream = torch.cuda.current_stream()
+
+    def extra_row_bytes(self):
+        return sum(s[0].numel() * s.element_size() for s, _ in self.extra)
+
+    def step(self, i, ev=None):
+        """One pass of the path.  ev: optional list of 6 events (or None
+        entries) recorded between the stages; the rope / attention marks go
+        around the first upper layer's launches."""
+        tg, shp = self.tg, self.shp
+
+        def mark(j):
+            if ev is not None and ev[j] is not None:
+                ev[j].record(self.stream)
+        r = self.resid[i % len(self.resid)]
+        mark(0)
+        tg.tg_gate_score(r, self.w1, None, self.w2, 0.0, 1e-6, 1e-6, self.s_norm, None, self.ws)
+        mark(1)
+        sc = self.s_norm if self.t_scores is None else self.t_scores
+        tg.tg_select_topk(sc, self.forced, shp.n_forced, shp.k, self.kept, None, self.ws)
+        mark(2)
+        tg.tg_compact(self.kept, shp.n, r, self.resid_k, self.pos, self.pos_k, sc, self.score_k, extra=self.extra)
+        mark(3)
+        for L in range(self.layers):
+            tg.tg_rope_qk(self.q[L], self.kk[L], self.pos_k, shp.rope_theta)
+            if L == 0:
+                mark(4)
+            tg.tg_gated_attention(self.q[L], self.kk[L], self.vv[L], self.score_k, self.gains, shp.temp_coef,
+                                  self.pos_k, self.out)
+            if L == 0:
+                mark(5)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -110,92 +211,53 @@ def main():
     import torch
 
     from learned_token_pruning_mlp_amd import binding as tg
-    from learned_token_pruning_mlp_amd import synth
 
     tg.load()
     dev = torch.device("cuda:0")
-    shp, desc = workload(args.workload)
     seed = 2
-
-    def bf(x):
-        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    # ---- inputs, resident in HBM before timing
-    inp = synth.gate_inputs(shp, seed)
-    resid = [bf(inp.resid)]
-    g = torch.Generator(device=dev)
-    g.manual_seed(seed)
-    for _ in range(N_RESID_COPIES - 1):
-        resid.append(torch.randn(resid[0].shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16))
-    w1, w2 = bf(inp.w1), bf(inp.w2)
-    forced = torch.from_numpy(inp.forced).to(dev)
-    pos = torch.from_numpy(inp.pos).to(dev)
+    path = Path(tg, torch, dev, args.workload, seed)
+    shp, stream, stages = path.shp, path.stream, Path.STAGES
     n, k = shp.n, shp.k
-    a = synth.attn_inputs(k, shp.hq, shp.hkv, shp.head_dim, seed)
-    q, kk, vv = bf(a.q), bf(a.k), bf(a.v)
-    gains = torch.from_numpy(a.gains).to(dev)
-    # outputs and workspace
-    s_norm = torch.empty(n, dtype=torch.float32, device=dev)
-    ws = tg.workspace(n, dev)
-    kept = torch.empty(k, dtype=torch.int32, device=dev)
-    resid_k = torch.empty((k, shp.d), dtype=torch.bfloat16, device=dev)
-    pos_k = torch.empty(k, dtype=torch.int32, device=dev)
-    score_k = torch.empty(k, dtype=torch.float32, device=dev)
-    out = torch.empty((k, shp.hq, shp.head_dim), dtype=torch.bfloat16, device=dev)
-    stream = torch.cuda.current_stream()
-
-    stages = ["gate_score", "select_topk", "compact", "rope", "gated_attention"]
-
-    def mark(ev, j):
-        if ev is not None and ev[j] is not None:
-            ev[j].record(stream)
-
-    def step(i, ev=None):
-        r = resid[i % N_RESID_COPIES]
-        mark(ev, 0)
-        tg.tg_gate_score(r, w1, None, w2, 0.0, 1e-6, 1e-6, s_norm, None, ws)
-        mark(ev, 1)
-        tg.tg_select_topk(s_norm, forced, shp.n_forced, k, kept, None, ws)
-        mark(ev, 2)
-        tg.tg_compact(kept, n, r, resid_k, pos, pos_k, s_norm, score_k)
-        mark(ev, 3)
-        tg.tg_rope_qk(q, kk, pos_k, shp.rope_theta)
-        mark(ev, 4)
-        tg.tg_gated_attention(q, kk, vv, score_k, gains, shp.temp_coef, pos_k, out)
-        mark(ev, 5)
+    Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     for i in range(args.warmup):
-        step(i)
+        path.step(i)
     torch.cuda.synchronize()
 
-    # ---- per-stage breakdown (outside the timed region): events between all launches
-    n_diag = max(1, min(20, args.steps))
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_diag)]
+    # ---- per-stage breakdown and per-step times, outside the timed region:
+    # events between all launches of a step (stage times, first upper layer
+    # for rope and attention), then steps bracketed one by one (median step)
+    n_diag = max(5, min(20, args.steps))
+    evs = [[Ev() for _ in range(6)] for _ in range(n_diag)]
     for i in range(n_diag):
-        step(i, evs[i])
+        path.step(i, evs[i])
     torch.cuda.synchronize()
-    per_stage = {s: 0.0 for s in stages}
-    for e in evs:
-        for j, s in enumerate(stages):
-            per_stage[s] += e[j].elapsed_time(e[j + 1])
-    per_stage = {s: v / n_diag for s, v in per_stage.items()}  # ms per step
+    per_stage = {s: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / n_diag for j, s in enumerate(stages)}
     dom = max(per_stage, key=per_stage.get)
     dom_j = stages.index(dom)
+    bounds = [Ev() for _ in range(n_diag + 1)]
+    bounds[0].record(stream)
+    for i in range(n_diag):
+        path.step(i)
+        bounds[i + 1].record(stream)
+    torch.cuda.synchronize()
+    step_ms = sorted(bounds[i].elapsed_time(bounds[i + 1]) for i in range(n_diag))
+    median_step_ms = step_ms[n_diag // 2] if n_diag % 2 else 0.5 * (step_ms[n_diag // 2 - 1] + step_ms[n_diag // 2])
 
-    # ---- timed region: exactly `steps` steps, synchronised on both sides.  Only
-    # the dominant stage is bracketed by events (on the stream its kernel runs
-    # on), and only on every `ev_stride`-th step: each event record adds a
-    # barrier packet and a timestamp to the queue (about 2.5 us per step for
-    # the pair), which is instrumentation, not work of the path.
-    ev_stride = max(1, args.steps // 25)
-    ev_steps = list(range(0, args.steps, ev_stride))
-    dom_ev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in ev_steps}
+    # ---- timed region: exactly `steps` steps, synchronised on both sides.
+    # Only the dominant stage's first launch is bracketed by events (on the
+    # stream its kernel runs on), on every EV_STRIDE-th step whatever the
+    # step count: each event record adds a barrier packet and a timestamp to
+    # the queue, which is instrumentation, not work of the path.
+    ev_steps = list(range(0, args.steps, EV_STRIDE))
+    dom_ev = {i: (Ev(), Ev()) for i in ev_steps}
 
     def timed_step(i):
-        marks = [None] * 6
+        marks = None
         if i in dom_ev:
+            marks = [None] * 6
             marks[dom_j], marks[dom_j + 1] = dom_ev[i]
-        step(i, marks)
+        path.step(i, marks)
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -218,15 +280,14 @@ def main():
                 "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                 "traffic": traffic_for("k_gate.hip", args.workload)}
     else:
-        achieved = compact_bytes(shp) / (dom_ms * 1e-3) / 1e9
+        achieved = compact_bytes(shp, path.extra_row_bytes()) / (dom_ms * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS, "traffic": None}
     roof["launch_us"] = dom_ms * 1e3
     roof["timed_launches"] = len(dom_ev)
-    per_stage[dom] = dom_ms
     attn_tflops = attn_flops(shp) / (per_stage["gated_attention"] * 1e-3) / 1e12
     gate_gbs = gate_bytes(shp) / (per_stage["gate_score"] * 1e-3) / 1e9
-    event_ms = sum(per_stage.values())
+    compact_gbs = compact_bytes(shp, path.extra_row_bytes()) / (per_stage["compact"] * 1e-3) / 1e9
 
     if args.copy_probe_mib:
         # counter calibration: one elementwise kernel that reads and writes exactly
@@ -237,11 +298,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    sweep = None if args.no_attn_sweep else attn_sweep(tg, torch, dev, shp)
-    prefill = None if (args.no_prefill or args.workload != "n16k") else prefill_compare(tg, torch, dev, shp, seed)
-    backward = None if (args.no_attn_sweep or args.workload != "n16k") else \
+    headline = args.workload == "n16k"
+    sweep = None if (args.no_attn_sweep or not headline) else attn_sweep(tg, torch, dev, shp)
+    prefill = None if (args.no_prefill or not headline) else prefill_compare(tg, torch, dev, shp, seed)
+    backward = None if (args.no_attn_sweep or not headline) else \
         {"attention": attn_backward(tg, torch, dev, shp), "scorer": gate_backward(tg, torch, dev, shp)}
-    hybrid = None if (args.no_attn_sweep or args.workload != "n16k") else hybrid_mixer(tg, torch, dev, shp)
+    hybrid = None if (args.no_attn_sweep or not headline) else hybrid_mixer(tg, torch, dev, shp)
 
     result = {
         "metric": METRIC,
@@ -256,14 +318,16 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; random-init scorer weights, N(0,1) residual and q/k/v)",
-        "config": {"workload": desc, "n_tokens": n, "kept": k, "forced": shp.n_forced, "d_model": shp.d,
+        "config": {"workload": path.desc, "n_tokens": n, "kept": k, "forced": shp.n_forced, "d_model": shp.d,
                    "scorer_hidden": shp.hd, "q_heads": shp.hq, "kv_heads": shp.hkv, "head_dim": shp.head_dim,
-                   "batch": 1},
+                   "upper_layers": path.layers, "batch": 1},
+        "median_step_ms": median_step_ms,
         "attn_mfma_pct": 100.0 * attn_tflops / PEAK_BF16_TFLOPS,
         "stage_us": {s: round(v * 1e3, 3) for s, v in per_stage.items()},
-        "stage_event_sum_ms": event_ms,
+        "stage_event_sum_ms": sum(per_stage.values()),
         "attn_tflops": attn_tflops,
         "gate_hbm_gbs": gate_gbs,
+        "compact_hbm_gbs": compact_gbs,
         "roofline": roof,
         "attn_sweep": sweep,
         "prefill": prefill,
@@ -273,7 +337,7 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(shp, seed, inp, a)
+        result["cpu_baseline"] = cpu_baseline(path, seed)
     print(json.dumps(result), flush=True)
 
 
@@ -487,20 +551,42 @@ def attn_sweep(tg, torch, dev, shp, ks=(4096, 8192, 16384), reps=10):
     return res
 
 
-def cpu_baseline(shp, seed, inp, a):
-    """The fp64 oracle, as it stands, over one full step of the same workload."""
+def cpu_baseline(path, seed, sample_rows=384):
+    """The fp64 oracle, as it stands, on the host cores over the same workload:
+    scorer, sequence norm, select, compaction and RoPE in full; attention in
+    full for kept lists up to 2048, else on a seeded uniform sample of query
+    rows of one upper layer, scaled to all rows and layers (a query row's
+    cost is linear in its index, so a uniform sample estimates the mean)."""
     from oracle import oracle
+    shp, inp, a = path.shp, path.inp, path.a
     threads = oracle.default_threads()
     t0 = time.perf_counter()
     s_norm, _ = oracle.gate_score(inp.resid, inp.w1, inp.b1, inp.w2, inp.b2, nthreads=threads)
-    kept = oracle.select_topk(s_norm, inp.forced, shp.k)
+    sc = s_norm if path.t_scores is None else path.t_scores.cpu().numpy()
+    kept = oracle.select_topk(sc, inp.forced, shp.k)
     oracle.gather_rows(inp.resid, kept)
+    t_path = time.perf_counter() - t0
+    t1 = time.perf_counter()
     qr = oracle.rope(a.q, kept, shp.rope_theta)
     kr = oracle.rope(a.k, kept, shp.rope_theta)
-    oracle.gated_attention(qr, kr, a.v, s_norm[kept], a.gains, shp.temp_coef, kept, nthreads=threads)
-    dt = time.perf_counter() - t0
+    t_path += (time.perf_counter() - t1) * path.layers
+    if shp.k <= 2048 and path.layers == 1:
+        t1 = time.perf_counter()
+        oracle.gated_attention(qr, kr, a.v, sc[kept], a.gains, shp.temp_coef, kept, nthreads=threads)
+        t_attn = time.perf_counter() - t1
+        sample = f"one full step of the same workload (N={shp.n}, K={shp.k}), fp64"
+    else:
+        rows = np.sort(np.random.default_rng(seed).choice(shp.k, size=sample_rows, replace=False))
+        t1 = time.perf_counter()
+        oracle.gated_attention(qr, kr, a.v, sc[kept], a.gains, shp.temp_coef, kept, rows=rows, nthreads=threads)
+        t_attn = (time.perf_counter() - t1) * (shp.k / sample_rows) * path.layers
+        sample = (f"scorer, select, compaction in full (N={shp.n}, K={shp.k}), RoPE of one layer x {path.layers}; "
+                  f"attention on "
+                  f"{sample_rows} uniformly drawn query rows of one upper layer, scaled to {shp.k} rows x "
+                  f"{path.layers} layer(s); fp64")
+    dt = t_path + t_attn
     return {"value": shp.n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"one full step of the same workload (N={shp.n}, K={shp.k}), fp64, {dt:.2f} s"}
+            "sample": f"{sample}, {dt:.2f} s per step ({t_path:.2f} s measured before attention)"}
 
 
 if __name__ == "__main__":

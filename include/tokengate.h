@@ -212,7 +212,9 @@ size_t tg_attention_bwd_workspace_bytes(int64_t n_kept, int32_t hq, int32_t hkv,
  *   dtemp  [1]       = dL/dtemp_coef   (fp32 out)
  * Inputs as in tg_gated_attention (q, k, v, key_score, gains, temp_coef, pos,
  * same shapes and limits); dout [n_kept, hq, head_dim] bf16 (16-byte
- * aligned).  Every output is overwritten (nothing accumulates across calls).
+ * aligned).  Q and dout must also each stay under 2 GiB
+ * (n_kept * hq * head_dim * 2 < 2^31; else TG_EUNSUPPORTED).  Every output
+ * is overwritten (nothing accumulates across calls).
  * The forward is recomputed (fp32, with its per-row log-sum-exp) into the
  * workspace; probabilities are rebuilt per 32x32 block, never stored.
  * bf16 matrix-core products with fp32 accumulation; deterministic (fixed

@@ -168,6 +168,24 @@ def tg_gate_score(resid: torch.Tensor, w1: torch.Tensor, b1: Optional[torch.Tens
         _ptr(score_norm), _ptr(score_raw), _ptr(ws), ws.numel(), _stream(stream)))
 
 
+def kept_budget(n: int, n_forced: int, max_kept: int) -> int:
+    """The total kept count K for a prompt of n tokens under a user budget of
+    at most max_kept kept tokens (news.farwalk.ai, "How do you deploy
+    TokenGate?": generation takes a maximum kept-prefill-token budget, and the
+    question span is never pruned): K = min(max_kept, n).  A budget smaller
+    than the n_forced question tokens cannot be met and raises ValueError,
+    as does a budget below 1 or n_forced outside [0, n]."""
+    n, n_forced, max_kept = int(n), int(n_forced), int(max_kept)
+    if n < 1 or not 0 <= n_forced <= n:
+        raise ValueError(f"prompt of {n} tokens with {n_forced} forced")
+    if max_kept < 1:
+        raise ValueError(f"kept budget {max_kept} < 1")
+    k = min(max_kept, n)
+    if k < n_forced:
+        raise ValueError(f"kept budget {max_kept} is smaller than the {n_forced} tokens that are never pruned")
+    return k
+
+
 def tg_select_topk(score: torch.Tensor, forced: Optional[torch.Tensor], n_forced: int, k: int,
                    kept_idx: torch.Tensor, dev_status: Optional[torch.Tensor], ws: torch.Tensor,
                    stream=None) -> None:

@@ -33,8 +33,11 @@ __device__ __forceinline__ float hi16(uint32_t w) { return __uint_as_float(w & 0
 
 // LANES lanes per row (a power of two, <= 64): each lane holds PER pieces of
 // 8 values; the row sum goes through a butterfly inside the lane group.
+// y may equal x (the per-head norms of q and k run in place), so neither is
+// declared restrict: every lane reads its pieces before any lane of the row
+// writes, and a row is read and written by one lane group only.
 template <int LANES, int PER>
-__global__ __launch_bounds__(kThreads) void rmsnorm_rows(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(kThreads) void rmsnorm_rows(const uint16_t* x,
                                                          const uint16_t* __restrict__ w, uint16_t* y,
                                                          int64_t rows, int dim, float eps) {
     constexpr int RPB = kThreads / LANES;  // rows per workgroup

@@ -149,8 +149,9 @@ int tg_gated_attention_bwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v,
     if (n_kept < 0 || n_kept > kMaxRows || hq < 1 || hkv < 1 || hq % hkv != 0) return TG_EINVAL;
     if (!(temp_coef == temp_coef) || temp_coef > 3.4e38f || temp_coef < -3.4e38f) return TG_EINVAL;
     if (head_dim != 64 && head_dim != 128) return TG_EUNSUPPORTED;
+    // K and V, and Q and dout (read by the key pass), go through 32-bit buffer offsets
     if (n_kept * (int64_t)hkv * head_dim * 2 >= (int64_t)1 << 31) return TG_EUNSUPPORTED;
-    if (n_kept * (int64_t)hq * head_dim * 4 >= (int64_t)1 << 40) return TG_EUNSUPPORTED;
+    if (n_kept * (int64_t)hq * head_dim * 2 >= (int64_t)1 << 31) return TG_EUNSUPPORTED;
     if (n_kept == 0) return TG_OK;
     if (!q || !k || !v || !key_score || !gains || !pos || !dout || !dq || !dk || !dv || !dscore || !dgains || !dtemp)
         return TG_EINVAL;

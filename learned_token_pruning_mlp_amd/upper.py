@@ -174,10 +174,12 @@ class Prefill:
             src, dst = dst, (self.hb if dst is self.ha else self.ha)
         return src
 
-    def gated(self, h: torch.Tensor, forced: torch.Tensor, n_forced: int, k: int):
+    def gated(self, h: torch.Tensor, forced: torch.Tensor, n_forced: int, max_kept: int):
         """Layers below the gate on n tokens, the gate on the gate layer's post-attention
-        residual, then k tokens above.  Returns (hidden [k, d], kept_idx, pos_k, trimmed K/V)."""
+        residual, then K = min(max_kept, n) tokens above (tg.kept_budget).  Returns
+        (hidden [K, d], kept_idx, pos_k, trimmed K/V)."""
         s, n, dev = self.s, self.n, h.device
+        k = tg.kept_budget(n, n_forced, max_kept)
         src, dst = h, self.ha
         for l in range(self.gl):
             attention_block(self.blas, s, self.W[l], src, self.arange, self.zeros_n, self.zero_gains, 0.0,

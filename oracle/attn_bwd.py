@@ -76,3 +76,34 @@ def gated_attention_grads(q, k, v, key_score, gains, temp_coef: float, pos, dout
         dg[h] = np.sum(dU * s[None, :])
         dc += float(np.sum(dlam * logratio))
     return out, dq, dk, dv, ds, dg, dc
+
+
+def gated_attention_dq_rows(q, k, v, key_score, gains, temp_coef: float, pos, dout, rows):
+    """dq for the given query rows only, in float64: every quantity the query
+    gradient of row t uses (P_t, dP_t, D_t, dU_t) belongs to row t, so it is
+    formed from that row's keys j <= t alone, with the same definitions as
+    ``gated_attention_grads``.  Returns dq[rows] as [len(rows), hq, D]."""
+    q, k, v, dout = (np.asarray(a, dtype=np.float64) for a in (q, k, v, dout))
+    s = np.asarray(key_score, dtype=np.float64)
+    g = np.asarray(gains, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.float64)
+    K, hq, D = q.shape
+    G = hq // k.shape[1]
+    rs = 1.0 / np.sqrt(D)
+    rows = np.asarray(rows, dtype=np.int64)
+    dq = np.zeros((rows.size, hq, D))
+    for i, t in enumerate(rows):
+        lam = 1.0 + float(temp_coef) * np.log((t + 1.0) / (pos[t] + 1.0))
+        kt, vt, st = k[: t + 1], v[: t + 1], s[: t + 1]
+        for h in range(hq):
+            hk = h // G
+            U = kt[:, hk, :] @ q[t, h, :] * rs + g[h] * st
+            Z = lam * U
+            E = np.exp(Z - Z.max())
+            P = E / E.sum()
+            O = P @ vt[:, hk, :]
+            dP = vt[:, hk, :] @ dout[t, h, :]
+            Dt = float(dout[t, h, :] @ O)
+            dU = lam * P * (dP - Dt)
+            dq[i, h, :] = dU @ kt[:, hk, :] * rs
+    return dq

@@ -228,6 +228,10 @@ def test_attention_backward_checks(lib):
     assert _bwd(lib, ws=None) == E.TG_EWORKSPACE
     assert _bwd(lib, ws_bytes=need - 1) == E.TG_EWORKSPACE
     assert _bwd(lib, ws=A + 16) == E.TG_EALIGN  # workspace must be 256-byte aligned
+    # Q and dout are read through 32-bit buffer offsets: 2 GiB each at most
+    # (64 q heads of 128 over 131072 rows is exactly 2 GiB; 8 kv heads keep K/V at 256 MiB)
+    assert _bwd(lib, n=131072, hq=64, hkv=8, D=128) == E.TG_EUNSUPPORTED
+    assert _bwd(lib, n=131071, hq=64, hkv=8, D=128, ws_bytes=0) == E.TG_EWORKSPACE  # sizes pass, then the workspace check
 
 
 def _gbw(lib, blas=A, n=64, d=128, hd=64, k=8, er=1e-6, es=1e-6, ws=A, ws_bytes=WS, **over):
@@ -280,3 +284,15 @@ def test_gated_delta_rule_checks(lib):
     assert call(k=M) == E.TG_EALIGN
     assert call(si=A + 4) == E.TG_EALIGN
     assert call(so=A + 8) == E.TG_EALIGN
+
+
+def test_kept_budget_semantics():
+    """The user budget is a maximum: K = min(max_kept, n); the never-pruned
+    question tokens must fit in it."""
+    assert binding.kept_budget(16384, 64, 2048) == 2048
+    assert binding.kept_budget(1000, 64, 2048) == 1000  # short prompt: everything kept
+    assert binding.kept_budget(1000, 64, 64) == 64       # exactly the forced tokens
+    assert binding.kept_budget(1000, 0, 1) == 1
+    for args in ((1000, 64, 63), (1000, 0, 0), (0, 0, 5), (1000, 1001, 2000), (1000, -1, 10)):
+        with pytest.raises(ValueError):
+            binding.kept_budget(*args)

@@ -5,6 +5,12 @@ size (the fp64 oracle would be too slow here).
   every key score adds the same constant to every logit of a row, so the
   output is unchanged and the score gradient sums to zero.  The GPU sum is
   held to 1e-3 of sum |ds| (fp32 terms of both signs, bf16 P and dU).
+  For the same reason (each row of dU sums to zero) the key gradients of a
+  kv head sum to zero, and since each row of P sums to one its value
+  gradients sum to its q heads' output gradients; both are held to 1e-3 of
+  the sum of the row norms.  dq of a query row depends on that row alone,
+  so sampled rows are compared with the oracle (1e-2 relative RMS, the
+  bound of the small-size parity tests).
 * Scorer backward at N = 16384, d = 2048, hd = 256 with eps_row = 0: a
   token's score depends on its residual only through h_i / |h_i|, so every
   row of the residual gradient is orthogonal to its row: |dh_i . h_i| is held
@@ -17,6 +23,7 @@ import torch
 
 import gpu_util as gu
 from learned_token_pruning_mlp_amd import binding as tg
+from oracle import attn_bwd
 
 pytestmark = pytest.mark.gpu
 
@@ -37,10 +44,35 @@ def test_attention_backward_score_gradient_sums_to_zero_at_8k():
     gu.say("attention backward K=8192 score-shift property")
     tg.tg_gated_attention_bwd(q, k, v, ks, gains, 0.1, pos, do, *o)
     torch.cuda.synchronize()
+    for t in o:
+        assert torch.isfinite(t).all()
     ds = o[3].double()
-    assert torch.isfinite(ds).all()
     assert abs(ds.sum().item()) <= 1e-3 * ds.abs().sum().item()
     assert ds.abs().sum().item() > 0
+    G = hq // hkv
+    dk, dv, dof = o[1].double(), o[2].double(), do.double()
+    for hk in range(hkv):
+        # each row of dU sums to zero, so the key gradients of a kv head sum to zero
+        sk = dk[:, hk, :].sum(dim=0).norm().item()
+        gu.say(f"  kv head {hk}: |sum dk| / sum |dk_j| = {sk / dk[:, hk, :].norm(dim=1).sum().item():.2e}")
+        assert sk <= 1e-3 * dk[:, hk, :].norm(dim=1).sum().item()
+        # each row of P sums to one, so the value gradients sum to the group's output gradients
+        want = dof[:, hk * G:(hk + 1) * G, :].sum(dim=(0, 1))
+        sv = (dv[:, hk, :].sum(dim=0) - want).norm().item()
+        gu.say(f"  kv head {hk}: |sum dv - sum dO| / sum |dv_j| = {sv / dv[:, hk, :].norm(dim=1).sum().item():.2e}")
+        assert sv <= 1e-3 * dv[:, hk, :].norm(dim=1).sum().item()
+    # dq of a query row depends on that row alone: sampled rows against the oracle
+    rows = np.unique(np.concatenate([np.arange(16), np.arange(K - 16, K),
+                                     np.random.default_rng(5).choice(K, size=48, replace=False)]))
+    gu.say(f"  dq of {rows.size} sampled rows against the oracle")
+    hb = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    ref = attn_bwd.gated_attention_dq_rows(hb(q), hb(k), hb(v), ks.cpu().numpy().astype(np.float64),
+                                           gains.cpu().numpy().astype(np.float64), 0.1, pos.cpu().numpy(),
+                                           hb(do), rows)
+    got = o[0].cpu().numpy()[rows].astype(np.float64)
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    gu.say(f"  dq rel-rms {rel:.2e}")
+    assert rel <= 1e-2
 
 
 def test_scorer_backward_rows_orthogonal_at_16k():

@@ -272,7 +272,10 @@ def test_attention(nk, hq, hkv, D):
     out32 = _run_attn(a, torch.float32)
     gu.check_attention(gu.host(out32), ref, "fp32 out")
     out16 = _run_attn(a, torch.bfloat16)
-    # the bf16 output is the nearest-even rounding of the fp32 result
+    # the bf16 output against the oracle: relative RMS, and one bf16 unit of
+    # the oracle's rounding (or the fp32 bound) per element
+    gu.check_attention_bf16(gu.bits(out16), ref, "bf16 out")
+    # and it is the nearest-even rounding of the fp32 result
     assert np.array_equal(gu.bits(out16), oracle.to_bf16(gu.host(out32).astype(np.float64)))
 
 

@@ -74,3 +74,30 @@ def test_value_gradients_sum_to_output_gradients():
     for hk in range(2):
         np.testing.assert_allclose(dv[:, hk, :].sum(axis=0), dout[:, hk * G:(hk + 1) * G, :].sum(axis=(0, 1)),
                                    rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed,c", [(7, 0.3), (8, -0.6)])
+def test_dq_rows_match_finite_differences(seed, c):
+    """The row-subset query gradient against central finite differences of
+    the C forward oracle, row by row (q_t moves only row t's output)."""
+    q, k, v, s, gains, c, pos, dout = _case(seed, K=9, c=c)
+    rows = np.array([0, 3, 8])
+    dq = attn_bwd.gated_attention_dq_rows(q, k, v, s, gains, c, pos, dout, rows)
+    eps = 1e-6
+    for i, t in enumerate(rows):
+        for idx in np.ndindex(q.shape[1:]):
+            a0 = q[(t,) + idx]
+            q[(t,) + idx] = a0 + eps
+            lp = _loss(q, k, v, s, gains, c, pos, dout)
+            q[(t,) + idx] = a0 - eps
+            lm = _loss(q, k, v, s, gains, c, pos, dout)
+            q[(t,) + idx] = a0
+            assert abs(dq[(i,) + idx] - (lp - lm) / (2 * eps)) <= 1e-6 * max(1.0, abs(dq[(i,) + idx]))
+
+
+def test_dq_rows_equal_dense_rows():
+    q, k, v, s, gains, c, pos, dout = _case(9, K=50, hq=6, hkv=3, D=8, c=0.2)
+    _, dq, _, _, _, _, _ = attn_bwd.gated_attention_grads(q, k, v, s, gains, c, pos, dout)
+    rows = np.array([0, 1, 17, 31, 49])
+    np.testing.assert_allclose(attn_bwd.gated_attention_dq_rows(q, k, v, s, gains, c, pos, dout, rows), dq[rows],
+                               rtol=1e-11, atol=1e-13)
