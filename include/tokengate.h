@@ -109,6 +109,24 @@ int tg_gate_score(const tg_bf16* resid, const tg_bf16* w1, const tg_bf16* b1, co
                   void* stream);
 
 /*
+ * tg_gate_score_noalloc -- tg_gate_score for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation): same arguments, results and checks, bit for bit,
+ * without the workspace.  Its scratch (the per-workgroup partial sums) is a
+ * fixed device array inside the library, one per device, located on the
+ * first call on each device (with that device current; the stream must
+ * belong to it).  Limit: n <= TG_NOALLOC_MAX_TOKENS, else TG_EUNSUPPORTED.
+ * Every call on one device shares that device's array: calls that overlap on
+ * one device (concurrent streams or threads) race and must not be issued;
+ * calls ordered on one stream are safe (each overwrites the array).  Returns
+ * TG_EDEVICE if the array's address cannot be obtained.
+ */
+#define TG_NOALLOC_MAX_TOKENS (1 << 22)
+int tg_gate_score_noalloc(const tg_bf16* resid, const tg_bf16* w1, const tg_bf16* b1, const tg_bf16* w2,
+                          float b2, int64_t n, int32_t d, int32_t hd, float eps_row, float eps_seq,
+                          float* score_norm, float* score_raw, void* stream);
+
+/*
  * tg_select_topk -- forced-keep top-K [P1 gate][P2 method][P3 how][P5 Fig 1(a)(b)].
  * Keeps every token with forced[i] != 0 and, among the others, the
  * k - F with the largest score (ties to the lower index; -0.0 equals +0.0;

@@ -26,7 +26,7 @@ TG_STATUS_FORCED_MISMATCH = 1
 TG_STATUS_FORCED_OVER_K = 2
 TG_MAX_GATHER = 16
 
-EXPORTS = ("tg_status_string", "tg_abi_version", "tg_workspace_bytes", "tg_gate_score",
+EXPORTS = ("tg_status_string", "tg_abi_version", "tg_workspace_bytes", "tg_gate_score", "tg_gate_score_noalloc",
            "tg_select_topk", "tg_compact", "tg_rope", "tg_rope_qk", "tg_gated_attention",
            "tg_rmsnorm", "tg_swiglu", "tg_blas_create", "tg_blas_destroy", "tg_linear",
            "tg_attention_bwd_workspace_bytes", "tg_gated_attention_bwd", "tg_gate_score_bwd_workspace_bytes",
@@ -64,6 +64,8 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
     L.tg_workspace_bytes.restype = ctypes.c_size_t
     L.tg_gate_score.argtypes = [P, P, P, P, F, I64, I32, I32, F, F, P, P, P, ctypes.c_size_t, P]
     L.tg_gate_score.restype = ctypes.c_int
+    L.tg_gate_score_noalloc.argtypes = [P, P, P, P, F, I64, I32, I32, F, F, P, P, P]
+    L.tg_gate_score_noalloc.restype = ctypes.c_int
     L.tg_select_topk.argtypes = [P, P, I64, I64, I64, P, P, P, ctypes.c_size_t, P]
     L.tg_select_topk.restype = ctypes.c_int
     L.tg_compact.argtypes = [P, I64, I64, P, P, I32, P, P, P, P, P, I32, P]
@@ -166,6 +168,23 @@ def tg_gate_score(resid: torch.Tensor, w1: torch.Tensor, b1: Optional[torch.Tens
     _check("tg_gate_score", load().tg_gate_score(
         _ptr(resid), _ptr(w1), _ptr(b1), _ptr(w2), float(b2), n, d, hd, float(eps_row), float(eps_seq),
         _ptr(score_norm), _ptr(score_raw), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def tg_gate_score_noalloc(resid: torch.Tensor, w1: torch.Tensor, b1: Optional[torch.Tensor], w2: torch.Tensor,
+                          b2: float, eps_row: float, eps_seq: float, score_norm: torch.Tensor,
+                          score_raw: Optional[torch.Tensor], stream=None) -> None:
+    """tg_gate_score without a workspace (the library's fixed scratch; see the header)."""
+    n, d = resid.shape
+    hd = w1.shape[0]
+    _need(resid, "resid", torch.bfloat16, (n, d))
+    _need(w1, "w1", torch.bfloat16, (hd, d))
+    _need(b1, "b1", torch.bfloat16, (hd,), optional=True)
+    _need(w2, "w2", torch.bfloat16, (hd,))
+    _need(score_norm, "score_norm", torch.float32, (n,))
+    _need(score_raw, "score_raw", torch.float32, (n,), optional=True)
+    _check("tg_gate_score_noalloc", load().tg_gate_score_noalloc(
+        _ptr(resid), _ptr(w1), _ptr(b1), _ptr(w2), float(b2), n, d, hd, float(eps_row), float(eps_seq),
+        _ptr(score_norm), _ptr(score_raw), _stream(stream)))
 
 
 def kept_budget(n: int, n_forced: int, max_kept: int) -> int:

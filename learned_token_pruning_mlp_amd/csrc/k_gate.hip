@@ -30,6 +30,8 @@
 // deterministic run to run.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "tg_device.h"
 #include "tg_internal.h"
 
@@ -390,7 +392,45 @@ int launch_gate_hd(const uint16_t* resid, const uint16_t* w1, const uint16_t* b1
 
 }  // namespace
 
+// Scratch of tg_gate_score_noalloc: the scorer's per-workgroup sums of
+// squared raw scores, for prompts of up to kNoAllocMaxTokens tokens (256 KB,
+// held on every device the library runs on until the process ends).  In host
+// code `scratch` names a host-side stand-in: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __align__(256) float scratch[tgi::kNoAllocMaxTokens / tgi::kGateRowsPerBlock];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_dev[kMaxDevices];  // per device: the address of its copy of `scratch`
+
+// The device address of `scratch` on the calling thread's current device
+// (looked up on the first call there), or nullptr on a runtime error.
+float* scratch_on_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_dev[dev] = static_cast<float*>(p);
+    }
+    return g_scratch_dev[dev];
+}
+
+}  // namespace
+
 namespace tgi {
+
+int launch_gate_score_noalloc(const uint16_t* resid, const uint16_t* w1, const uint16_t* b1, const uint16_t* w2,
+                              float b2, int64_t n, int d, int hd, float eps_row, float eps_seq, float* score_norm,
+                              float* score_raw, void* stream) {
+    float* ws = scratch_on_current_device();
+    if (!ws) return TG_EDEVICE;
+    // every workgroup overwrites its own partial: nothing to clear
+    return launch_gate_score(resid, w1, b1, w2, b2, n, d, hd, eps_row, eps_seq, score_norm, score_raw, ws, stream);
+}
 
 int launch_gate_score(const uint16_t* resid, const uint16_t* w1, const uint16_t* b1,
                       const uint16_t* w2, float b2, int64_t n, int d, int hd, float eps_row,

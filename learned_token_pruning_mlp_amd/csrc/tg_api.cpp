@@ -14,6 +14,7 @@ constexpr int kAbiVersion = 1;
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 inline bool finite_nonneg(float x) { return x >= 0.0f && x <= 3.4e38f; }
 constexpr int64_t kMaxRows = 0x7fffffffLL;
+static_assert(tgi::kNoAllocMaxTokens == TG_NOALLOC_MAX_TOKENS, "the header's limit is the scratch array's");
 
 }  // namespace
 
@@ -51,6 +52,23 @@ int tg_gate_score(const tg_bf16* resid, const tg_bf16* w1, const tg_bf16* b1, co
     if (!aligned(workspace, 16)) return TG_EALIGN;
     return tgi::launch_gate_score(resid, w1, b1, w2, b2, n, d, hd, eps_row, eps_seq, score_norm, score_raw,
                                   workspace, stream);
+}
+
+int tg_gate_score_noalloc(const tg_bf16* resid, const tg_bf16* w1, const tg_bf16* b1, const tg_bf16* w2, float b2,
+                          int64_t n, int32_t d, int32_t hd, float eps_row, float eps_seq, float* score_norm,
+                          float* score_raw, void* stream) {
+    if (n < 0 || n > kMaxRows) return TG_EINVAL;
+    if (!finite_nonneg(eps_row) || !finite_nonneg(eps_seq)) return TG_EINVAL;
+    if (d <= 0 || d % 64 != 0) return TG_EUNSUPPORTED;
+    if (hd != 64 && hd != 128 && hd != 256) return TG_EUNSUPPORTED;
+    if (n > tgi::kNoAllocMaxTokens) return TG_EUNSUPPORTED;  // beyond the fixed scratch
+    if (n == 0) return TG_OK;
+    if (!resid || !w1 || !w2 || !score_norm) return TG_EINVAL;
+    if (!aligned(resid, 16) || !aligned(w1, 16) || !aligned(score_norm, 4) ||
+        (score_raw && !aligned(score_raw, 4)) || (b1 && !aligned(b1, 2)) || !aligned(w2, 2))
+        return TG_EALIGN;
+    return tgi::launch_gate_score_noalloc(resid, w1, b1, w2, b2, n, d, hd, eps_row, eps_seq, score_norm, score_raw,
+                                          stream);
 }
 
 int tg_select_topk(const float* score, const uint8_t* forced, int64_t n, int64_t n_forced, int64_t k,

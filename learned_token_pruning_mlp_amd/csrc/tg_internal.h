@@ -30,7 +30,15 @@ inline size_t select_bytes(int64_t n) {
 }
 inline size_t workspace_bytes(int64_t n) { return gate_bytes(n) + select_bytes(n); }
 
+// Largest prompt tg_gate_score_noalloc takes: its per-workgroup partial sums
+// live in a fixed device array of kNoAllocMaxTokens / kGateRowsPerBlock floats.
+constexpr int64_t kNoAllocMaxTokens = int64_t(1) << 22;
+
 // Launchers: return 0 on success, TG_EDEVICE on a launch error.
+int launch_gate_score_noalloc(const uint16_t* resid, const uint16_t* w1, const uint16_t* b1, const uint16_t* w2,
+                              float b2, int64_t n, int d, int hd, float eps_row, float eps_seq, float* score_norm,
+                              float* score_raw, void* stream);
+
 int launch_gate_score(const uint16_t* resid, const uint16_t* w1, const uint16_t* b1,
                       const uint16_t* w2, float b2, int64_t n, int d, int hd, float eps_row,
                       float eps_seq, float* score_norm, float* score_raw, void* ws, void* stream);
