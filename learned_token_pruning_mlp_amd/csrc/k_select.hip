@@ -15,17 +15,21 @@
 // min(#ties before i, m).  Everything is integer arithmetic, so the result is
 // bit-exact and deterministic.
 //
-// One workgroup of 1024 threads does the whole selection (one launch, no
-// workspace traffic).  Up to 32768 tokens each thread keeps the keys of 16
-// (or 32) consecutive tokens in registers after one read of the scores, so
+// Up to 16384 tokens one workgroup of 1024 threads does the whole selection
+// (one launch, no workspace traffic); longer prompts, up to 524288 tokens,
+// take the many-workgroup form further below (three launches over chunks of
+// the prompt).  In the one-workgroup form each thread keeps the keys of 16
+// consecutive tokens in registers after one read of the scores, so
 // every later phase works on registers; the histogram copies are cleared
 // while that read is in flight, the first histogram goes into eight LDS
 // copies chosen by lane (float keys crowd into a few dozen top-11-bit bins,
 // so lanes of one wave would otherwise collide on the same words), and the
-// later rounds filter the keys by the prefix chosen so far.  Bin searches run in one wave with DPP scans; the emit pass takes one
-// block scan of packed counts and visits only the kept tokens.  Longer
-// prompts re-read the scores (L2-resident) in each sweep and gather the
-// first round's bucket into LDS when it fits.
+// later rounds filter the keys by the prefix chosen so far.  Bin searches
+// run in one wave with DPP scans; the emit pass takes one block scan of
+// packed counts and visits only the kept tokens.  Prompts too long for the
+// many-workgroup form take one workgroup that re-reads the scores
+// (L2-resident) in each sweep and gathers the first round's bucket into LDS
+// when it fits.
 #include <hip/hip_runtime.h>
 
 #include "tg_device.h"
@@ -556,19 +560,459 @@ __global__ __launch_bounds__(kThreads) void select_topk_block(const float* __res
     }
 }
 
+// ---------------------------------------------------------------------------
+// Many-workgroup select for long prompts.  The prompt is cut into chunks of
+// 256 * KPT consecutive tokens, one workgroup of 256 threads each (a thread
+// holds KPT consecutive keys in registers), and the selection takes three
+// launches over the same grid:
+//   selm_hist    each chunk's histogram of the keys' top 11 bits (u16) and
+//                its forced count;
+//   selm_gather  every workgroup adds up all chunks' counts of 64 groups of
+//                32 bins, picks the group, adds up all chunks' counts of that
+//                group's bins and picks the first round's bin b1 (the same
+//                sums and picks in every workgroup); it counts its chunk's
+//                prunable keys above b1 and stores its keys in b1 (the
+//                candidates) after those of the chunks before it, in index
+//                order;
+//   selm_emit    every workgroup reads all candidates (into LDS when they
+//                fit) and runs rounds 2 and 3 over them (identically), which
+//                fixes T and m, adds up the counts of the chunks before its
+//                own and writes its chunk's kept indices.
+// Integer arithmetic and no global atomics: bit-exact and deterministic, and
+// no workspace word needs clearing (every one is written before it is read).
+
+constexpr int kMT = tgi::kSelectThreads;
+constexpr int kMWaves = kMT / 64;
+
+// Exclusive scan over a 256-thread workgroup (one barrier); wsum has kMWaves
+// slots, alternated by the caller between consecutive scans.
+__device__ __forceinline__ uint32_t block_excl_scan_m(uint32_t x, uint32_t* wsum, uint32_t* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t incl = wave_incl_scan(x);
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    uint32_t below = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kMWaves; ++w) {
+        const uint32_t v = wsum[w];
+        all += v;
+        if (w < wave) below += v;
+    }
+    *total = all;
+    return below + incl - x;
+}
+
+// Keys of this thread's KPT consecutive tokens base .. base + KPT - 1
+// (kForcedMark for forced tokens; entries at or past n are unused).
+template <int KPT>
+__device__ __forceinline__ void chunk_keys(const float* __restrict__ score, const uint8_t* __restrict__ forced,
+                                           uint32_t base, uint32_t n, uint32_t (&key)[KPT]) {
+#pragma unroll
+    for (int v = 0; v < KPT / 4; ++v) {
+        const uint4 k4 = keys4_global(score, forced, base + 4 * v, n);
+        key[4 * v] = k4.x, key[4 * v + 1] = k4.y, key[4 * v + 2] = k4.z, key[4 * v + 3] = k4.w;
+    }
+}
+
+// The bin of `hist` (nbins, counted from the top) holding the remaining-th
+// largest key; one wave, two wave scans.  Sets ctl[0] = bin, ctl[1] = rank
+// inside it; ends with a barrier.
+__device__ __forceinline__ void pick_bin_m(const uint32_t* hist, uint32_t remaining, int nbins, uint32_t* ctl) {
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        const int per = nbins / 64;
+        const int hi = nbins - lane * per;
+        uint32_t sum = 0;
+        for (int i = 0; i < per; i += 4) {
+            const uint4 h4 = *reinterpret_cast<const uint4*>(&hist[hi - per + i]);
+            sum += h4.x + h4.y + h4.z + h4.w;
+        }
+        const uint32_t incl = wave_incl_scan(sum);
+        const int L = __builtin_ctzll(__builtin_amdgcn_ballot_w64(incl >= remaining));
+        const uint32_t before = __builtin_amdgcn_readlane(incl - sum, L);
+        const int hiL = nbins - L * per;
+        const uint32_t c = lane < per ? hist[hiL - 1 - lane] : 0u;
+        const uint32_t ci = wave_incl_scan(c) + before;
+        const int b = __builtin_ctzll(__builtin_amdgcn_ballot_w64(lane < per && ci >= remaining));
+        if (lane == b) {
+            ctl[0] = hiL - 1 - b;
+            ctl[1] = remaining - (ci - c);
+        }
+    }
+    __syncthreads();
+}
+
+// Sum over the 64 lanes of a wave, valid in lane 63 (the last lane of an
+// inclusive DPP scan: no LDS round trips).
+__device__ __forceinline__ uint32_t wave_sum_last(uint32_t x) { return wave_incl_scan(x); }
+
+// hist[bin] += 1 for every active lane; when all active lanes of the wave
+// share one bin (ties, or scores that crowd into one bin) a single lane adds
+// their count.
+__device__ __forceinline__ void hist_add_wave(uint32_t* hist, uint32_t bin, bool active) {
+    const uint64_t act = __builtin_amdgcn_ballot_w64(active);
+    if (act == 0) return;  // wave-uniform
+    const int first = __builtin_ctzll(act);
+    const uint32_t b0 = __builtin_amdgcn_readlane(bin, first);
+    if (__builtin_amdgcn_ballot_w64(active && bin == b0) == act) {
+        if ((int)(threadIdx.x & 63) == first) atomicAdd(&hist[b0], (uint32_t)__builtin_popcountll(act));
+    } else if (active) {
+        atomicAdd(&hist[bin], 1u);
+    }
+}
+
+template <int KPT>
+__global__ __launch_bounds__(kMT) void selm_hist(const float* __restrict__ score, const uint8_t* __restrict__ forced,
+                                                 uint32_t n, tgi::SelectWs w) {
+    constexpr int kCopies = 4;  // lane % 4 picks a copy: fewer lanes of a wave on one word
+    __shared__ __attribute__((aligned(16))) uint32_t h[kCopies][2048];
+    __shared__ uint32_t fw[kMWaves];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const uint32_t c = blockIdx.x;
+    const uint32_t base = c * (uint32_t)(kMT * KPT) + (uint32_t)tid * KPT;
+    uint32_t key[KPT];
+    chunk_keys<KPT>(score, forced, base, n, key);  // loads in flight while the copies are cleared
+#pragma unroll
+    for (int i = 0; i < kCopies * 2048 / (4 * kMT); ++i)
+        *reinterpret_cast<uint4*>(&h[0][0] + 4 * (i * kMT + tid)) = uint4{0u, 0u, 0u, 0u};
+    __syncthreads();
+    const int nvalid = base >= n ? 0 : (int)min((uint32_t)KPT, n - base);
+    uint32_t fcount = 0;
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+        const bool ok = e < nvalid;
+        const bool f = ok && key[e] == kForcedMark;
+        fcount += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(f));
+        if (ok && !f) atomicAdd(&h[lane % kCopies][key[e] >> 21], 1u);
+    }
+    if (lane == 0) fw[tid >> 6] = fcount;
+    __syncthreads();
+    // thread t merges bins 8t .. 8t+7 and stores them as u16 (a chunk holds
+    // at most 8192 keys); the four threads of a group of 32 bins add their
+    // sums into that group's coarse count
+    uint32_t sum[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sum[j] = 0;
+#pragma unroll
+    for (int cp = 0; cp < kCopies; ++cp) {
+        const uint4 a = *reinterpret_cast<const uint4*>(&h[cp][8 * tid]);
+        const uint4 b = *reinterpret_cast<const uint4*>(&h[cp][8 * tid + 4]);
+        sum[0] += a.x, sum[1] += a.y, sum[2] += a.z, sum[3] += a.w;
+        sum[4] += b.x, sum[5] += b.y, sum[6] += b.z, sum[7] += b.w;
+    }
+    *reinterpret_cast<uint4*>(w.hist + (size_t)c * 2048 + 8 * tid) =
+        uint4{sum[0] | (sum[1] << 16), sum[2] | (sum[3] << 16), sum[4] | (sum[5] << 16), sum[6] | (sum[7] << 16)};
+    uint32_t g = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) g += sum[j];
+    g += __shfl_xor(g, 1, 64);
+    g += __shfl_xor(g, 2, 64);
+    if ((tid & 3) == 0) w.coarse[(size_t)c * 64 + (tid >> 2)] = (uint16_t)g;
+    if (tid == 0) {
+        uint32_t f = 0;
+#pragma unroll
+        for (int i = 0; i < kMWaves; ++i) f += fw[i];
+        w.forced[c] = f;
+    }
+}
+
+// The bin holding the remaining-th largest count of a histogram of 64 bins
+// (one per lane of wave 0, lane l holding bin 63 - l, i.e. from the top):
+// returns (bin, rank inside it) to every lane of the wave.
+__device__ __forceinline__ void pick64(uint32_t cnt_from_top, uint32_t remaining, uint32_t* bin, uint32_t* rank) {
+    const uint32_t incl = wave_incl_scan(cnt_from_top);
+    const int L = __builtin_ctzll(__builtin_amdgcn_ballot_w64(incl >= remaining));
+    *bin = 63u - (uint32_t)L;
+    *rank = remaining - __builtin_amdgcn_readlane(incl - cnt_from_top, L);
+}
+
+template <int KPT>
+__global__ __launch_bounds__(kMT) void selm_gather(const float* __restrict__ score,
+                                                   const uint8_t* __restrict__ forced, uint32_t n, uint32_t chunks,
+                                                   uint32_t k, int64_t n_forced, int32_t* __restrict__ dev_status,
+                                                   tgi::SelectWs w) {
+    __shared__ uint32_t coarse[64], fine[32], ctl[8], fsum;
+    __shared__ uint32_t fall[tgi::kSelectMaxChunks][32];  // every chunk's counts in the chosen group of 32 bins
+    __shared__ uint32_t wsum[2][kMWaves];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const uint32_t c = blockIdx.x;
+    const uint32_t base = c * (uint32_t)(kMT * KPT) + (uint32_t)tid * KPT;
+    uint32_t key[KPT];
+    chunk_keys<KPT>(score, forced, base, n, key);
+    // Every chunk's coarse counts added up without atomics: lane l of each
+    // wave reads chunk l's counts of 16 groups (two 16-byte loads), and each
+    // group's sum over the 64 lanes is a wave reduction; wave v covers
+    // groups 16v .. 16v+15.  Wave 0 also adds up the forced counts.
+    const int wave = tid >> 6;
+    {
+        const bool ok = (uint32_t)lane < chunks;
+        const uint16_t* row = w.coarse + (size_t)lane * 64 + 16 * wave;
+        const uint4 v0 = ok ? *reinterpret_cast<const uint4*>(row) : uint4{0u, 0u, 0u, 0u};
+        const uint4 v1 = ok ? *reinterpret_cast<const uint4*>(row + 8) : uint4{0u, 0u, 0u, 0u};
+        const uint32_t f = (wave == 0 && ok) ? w.forced[lane] : 0u;
+        const uint32_t vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const uint32_t t = wave_sum_last((vv[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+            if (lane == 63) coarse[16 * wave + j] = t;
+        }
+        const uint32_t ft = wave_sum_last(f);
+        if (wave == 0 && lane == 63) fsum = ft;
+    }
+    __syncthreads();
+    const uint32_t F = fsum;
+    int64_t R = (int64_t)k - (int64_t)F;  // prunable tokens to choose
+    if (c == 0 && tid == 0 && dev_status) {
+        int32_t st = 0;
+        if ((int64_t)F != n_forced) st |= TG_STATUS_FORCED_MISMATCH;
+        if (R < 0) st |= TG_STATUS_FORCED_OVER_K;
+        *dev_status = st;
+    }
+    if (R < 0) R = 0;
+    uint32_t b1 = 0, r1 = 0, start = 0, total = 0;
+    if (R > 0) {
+        // the group of 32 bins, then the bin inside it: only that group's
+        // counts of every chunk are read (and kept, per chunk)
+        if (tid < 64) {
+            uint32_t grp, rank;
+            pick64(coarse[63 - lane], (uint32_t)R, &grp, &rank);
+            if (lane == 0) ctl[0] = grp, ctl[1] = rank;
+        }
+        __syncthreads();
+        const uint32_t grp = ctl[0], rank = ctl[1];
+        {
+            // lane l: chunk l's bins 8v .. 8v+7 of the group (wave v)
+            const bool ok = (uint32_t)lane < chunks;
+            const uint4 v = ok ? *reinterpret_cast<const uint4*>(w.hist + (size_t)lane * 2048 + 32 * grp + 8 * wave)
+                               : uint4{0u, 0u, 0u, 0u};
+            const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t x = (vv[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+                fall[lane][8 * wave + j] = x;
+                const uint32_t t = wave_sum_last(x);
+                if (lane == 63) fine[8 * wave + j] = t;
+            }
+        }
+        __syncthreads();
+        if (tid < 64) {
+            uint32_t bin, rk;  // lanes 0..31 hold bins 31..0 of the group; the rest hold 0
+            pick64(lane < 32 ? fine[31 - lane] : 0u, rank, &bin, &rk);
+            const uint32_t jb = bin - 32;  // bin inside the group
+            // the chunks' counts in that bin: where this chunk's candidates start
+            const uint32_t cnt = (uint32_t)lane < chunks ? fall[lane][jb] : 0u;
+            const uint32_t incl = wave_incl_scan(cnt);
+            const uint32_t st_c = __builtin_amdgcn_readlane(incl - cnt, (int)c);
+            if (lane == 63) ctl[2] = 32 * grp + jb, ctl[3] = rk, ctl[4] = st_c, ctl[5] = incl;
+        }
+        __syncthreads();
+        b1 = ctl[2], r1 = ctl[3], start = ctl[4], total = ctl[5];
+    }
+    // this chunk: prunable keys above bin b1, and its keys in b1 (stored in
+    // index order after a scan of the per-thread counts)
+    const int nvalid = base >= n ? 0 : (int)min((uint32_t)KPT, n - base);
+    uint32_t na = 0, nb = 0;
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+        const bool p = R > 0 && e < nvalid && key[e] != kForcedMark;
+        na += (p && (key[e] >> 21) > b1) ? 1u : 0u;
+        nb += (p && (key[e] >> 21) == b1) ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan_m((na << 16) | nb, wsum[0], &tot);
+    uint32_t* out = w.cand + start + (ex & 0xffffu);
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+        if (R > 0 && e < nvalid && key[e] != kForcedMark && (key[e] >> 21) == b1) *out++ = key[e];
+    }
+    if (tid == 0) {
+        w.above[c] = tot >> 16;
+        w.cstart[c] = start;
+        if (c == 0) {
+            w.ctl[0] = b1;
+            w.ctl[1] = r1;
+            w.ctl[2] = F;
+            w.ctl[3] = (uint32_t)R;
+            w.ctl[4] = total;
+        }
+    }
+}
+
+template <int KPT>
+__global__ __launch_bounds__(kMT) void selm_emit(const float* __restrict__ score, const uint8_t* __restrict__ forced,
+                                                 uint32_t n, uint32_t chunks, uint32_t k,
+                                                 int32_t* __restrict__ kept, tgi::SelectWs w) {
+    constexpr uint32_t CH = kMT * KPT;
+    constexpr uint32_t kCache = 16384;  // candidates held in LDS when they fit
+    __shared__ __attribute__((aligned(16))) uint32_t hist[2048];
+    __shared__ __attribute__((aligned(16))) uint32_t cache[kCache];
+    __shared__ uint32_t ctl[4];
+    __shared__ uint32_t wsum[2][kMWaves];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const uint32_t c = blockIdx.x;
+    const uint32_t base = c * CH + (uint32_t)tid * KPT;
+    uint32_t key[KPT];
+    chunk_keys<KPT>(score, forced, base, n, key);
+    // The first kSpec candidate words are read before their count is known
+    // (the array holds at least n words; words past the count are never used).
+    constexpr uint32_t kSpec = 4 * 4 * kMT;
+    uint4 spec[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const uint32_t i = 4 * (u * kMT + (uint32_t)tid);
+        spec[u] = i + 4 <= n ? *reinterpret_cast<const uint4*>(w.cand + i) : uint4{0u, 0u, 0u, 0u};
+    }
+    const uint32_t b1 = w.ctl[0], r1 = w.ctl[1], R = w.ctl[3], C = w.ctl[4];
+    const uint32_t c_end = w.cstart[c];  // candidates of the chunks before this one: [0, c_end)
+    const bool cached = C <= kCache;
+    if (R > 0 && cached) {
+        // all candidates into LDS: the speculative words, then the rest 16
+        // bytes a thread per trip (the array is 256-byte aligned; the last
+        // piece is read word by word)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) *reinterpret_cast<uint4*>(&cache[4 * (u * kMT + tid)]) = spec[u];
+        const uint32_t full = C / 4;
+        for (uint32_t i = kSpec / 4 + tid; i < full; i += kMT)
+            *reinterpret_cast<uint4*>(&cache[4 * i]) = *reinterpret_cast<const uint4*>(w.cand + 4 * i);
+        if ((uint32_t)tid < C - 4 * full) cache[4 * full + tid] = w.cand[4 * full + tid];
+    }
+    // the forced and above-b1 counts of the chunks before this one (wave 0)
+    uint32_t fa_before = 0;
+    if (tid < 64) {
+        const uint32_t fa = (uint32_t)lane < c ? w.forced[lane] + w.above[lane] : 0u;
+        fa_before = __builtin_amdgcn_readlane(wave_incl_scan(fa), 63);
+    }
+
+    uint32_t T = 0xffffffffu, m = 0;  // R == 0: no prunable token is taken
+    if (R > 0) {
+        // Rounds 2 and 3 (next 11 bits, last 10) over all candidates.
+        uint32_t prefix = b1 << 21, pmask = 0x7ffu << 21, remaining = r1;
+#pragma unroll
+        for (int round = 0; round < 2; ++round) {
+            const int shift = round == 0 ? 10 : 0;
+            const uint32_t dmask = round == 0 ? 0x7ffu : 0x3ffu;
+            for (int b = tid; b < 2048; b += kMT) hist[b] = 0;
+            __syncthreads();  // (also: the candidates are in LDS)
+            if (cached) {
+                // four keys a thread per trip (one 16-byte LDS read)
+                for (uint32_t f0 = 0; f0 < C; f0 += 4 * kMT) {  // whole-workgroup trips
+                    const uint32_t f = f0 + 4 * (uint32_t)tid;
+                    const uint4 k4 = f < C ? *reinterpret_cast<const uint4*>(&cache[f]) : uint4{0u, 0u, 0u, 0u};
+                    const uint32_t kq[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        hist_add_wave(hist, (kq[q] >> shift) & dmask, f + q < C && (kq[q] & pmask) == prefix);
+                }
+            } else {
+                for (uint32_t f0 = 0; f0 < C; f0 += kMT) {  // whole-workgroup trips
+                    const uint32_t f = f0 + (uint32_t)tid;
+                    const uint32_t key_f = f < C ? w.cand[f] : 0u;
+                    hist_add_wave(hist, (key_f >> shift) & dmask, f < C && (key_f & pmask) == prefix);
+                }
+            }
+            __syncthreads();
+            pick_bin_m(hist, remaining, (int)dmask + 1, ctl);
+            prefix |= ctl[0] << shift;
+            pmask |= dmask << shift;
+            remaining = ctl[1];
+            __syncthreads();
+        }
+        T = prefix;
+        m = remaining;
+    }
+
+    // Kept tokens and ties in the chunks before this one: forced and above
+    // b1 from the counts, above and equal to T from their candidates.
+    uint32_t a_pre = tid == 0 ? fa_before : 0u, b_pre = 0;  // (wave 0 holds fa_before in every lane)
+    if (cached) {
+        for (uint32_t f = 4 * (uint32_t)tid; f < c_end; f += 4 * kMT) {
+            const uint4 k4 = *reinterpret_cast<const uint4*>(&cache[f]);
+            const uint32_t kq[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                a_pre += (f + q < c_end && kq[q] > T) ? 1u : 0u;
+                b_pre += (f + q < c_end && kq[q] == T) ? 1u : 0u;
+            }
+        }
+    } else {
+        for (uint32_t f = tid; f < c_end; f += kMT) {
+            const uint32_t key_f = w.cand[f];
+            a_pre += key_f > T ? 1u : 0u;
+            b_pre += key_f == T ? 1u : 0u;
+        }
+    }
+    // workgroup totals (two scans: each total may exceed 16 bits)
+    uint32_t A0, B0;
+    block_excl_scan_m(a_pre, wsum[0], &A0);
+    block_excl_scan_m(b_pre, wsum[1], &B0);
+
+    // Emit this chunk in index order: slot = (#kind 1 before) + min(#ties before, m).
+    const int nvalid = base >= n ? 0 : (int)min((uint32_t)KPT, n - base);
+    uint32_t ka = 0, kb = 0;
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+        const uint32_t ok = e < nvalid ? 1u : 0u;
+        const uint32_t a = ok & ((key[e] == kForcedMark) | (key[e] > T));
+        const uint32_t b = ok & (a ^ 1u) & (key[e] == T);
+        ka |= a << e;
+        kb |= b << e;
+    }
+    const uint32_t ca = __builtin_popcount(ka), cb = __builtin_popcount(kb);
+    uint32_t tot;
+    // both counts in one word: each is at most KPT per thread and CH <= 8192 per chunk
+    const uint32_t ex = block_excl_scan_m((ca << 16) | cb, wsum[0], &tot);
+    const uint64_t A = (uint64_t)A0 + (ex >> 16), B = (uint64_t)B0 + (ex & 0xffffu);
+    uint32_t keep = ka;
+    if (B < m) {
+        uint32_t ties = kb;
+        if (m - B < (uint64_t)cb) {
+            uint32_t rest = kb;
+            for (uint32_t r = 0; r < (uint32_t)(m - B); ++r) rest &= rest - 1;
+            ties &= ~rest;
+        }
+        keep |= ties;
+    }
+    while (keep) {
+        const int e = __builtin_ctz(keep);
+        keep &= keep - 1;
+        const uint32_t below = (1u << e) - 1u;
+        const uint64_t a_before = A + __builtin_popcount(ka & below);
+        const uint64_t b_before = B + __builtin_popcount(kb & below);
+        const uint64_t slot = a_before + (b_before < m ? b_before : m);
+        if (slot < k) kept[slot] = (int32_t)(base + e);
+    }
+}
+
+template <int KPT>
+int launch_select_multi(const float* score, const uint8_t* forced, int64_t n, int64_t n_forced, int64_t k,
+                        int32_t* kept_idx, int32_t* dev_status, const tgi::SelectWs& w, hipStream_t s) {
+    const uint32_t chunks = (uint32_t)tgi::select_chunks(n);
+    hipLaunchKernelGGL(selm_hist<KPT>, dim3(chunks), dim3(kMT), 0, s, score, forced, (uint32_t)n, w);
+    hipLaunchKernelGGL(selm_gather<KPT>, dim3(chunks), dim3(kMT), 0, s, score, forced, (uint32_t)n, chunks,
+                       (uint32_t)k, n_forced, dev_status, w);
+    hipLaunchKernelGGL(selm_emit<KPT>, dim3(chunks), dim3(kMT), 0, s, score, forced, (uint32_t)n, chunks,
+                       (uint32_t)k, kept_idx, w);
+    return hipGetLastError() == hipSuccess ? TG_OK : TG_EDEVICE;
+}
+
 }  // namespace
 
 namespace tgi {
 
 int launch_select_topk(const float* score, const uint8_t* forced, int64_t n, int64_t n_forced,
                        int64_t k, int32_t* kept_idx, int32_t* dev_status, void* ws, void* stream) {
-    (void)ws;
     hipStream_t s = (hipStream_t)stream;
+    const int kpt = select_kpt(n);
+    if (kpt > 0) {
+        const SelectWs w = select_ws(static_cast<char*>(ws) + gate_bytes(n), n);
+        switch (kpt) {
+            case 8: return launch_select_multi<8>(score, forced, n, n_forced, k, kept_idx, dev_status, w, s);
+            case 16: return launch_select_multi<16>(score, forced, n, n_forced, k, kept_idx, dev_status, w, s);
+            default: return launch_select_multi<32>(score, forced, n, n_forced, k, kept_idx, dev_status, w, s);
+        }
+    }
     if (n <= kThreads * 16)
         hipLaunchKernelGGL(select_topk_regs<16>, dim3(1), dim3(kThreads), 0, s, score, forced, n, n_forced, k,
-                           kept_idx, dev_status);
-    else if (n <= kThreads * 32)
-        hipLaunchKernelGGL(select_topk_regs<32>, dim3(1), dim3(kThreads), 0, s, score, forced, n, n_forced, k,
                            kept_idx, dev_status);
     else
         hipLaunchKernelGGL(select_topk_block, dim3(1), dim3(kThreads), 0, s, score, forced, n, n_forced, k,

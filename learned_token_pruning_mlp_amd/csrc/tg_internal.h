@@ -21,12 +21,71 @@ constexpr int kGateRowsPerBlock = 64;
 inline int64_t gate_blocks(int64_t n) { return (n + kGateRowsPerBlock - 1) / kGateRowsPerBlock; }
 inline size_t gate_bytes(int64_t n) { return align_up(sizeof(float) * (size_t)(gate_blocks(n) > 0 ? gate_blocks(n) : 1)); }
 
-constexpr int kSelectChunk = 4096;  // keys per select workgroup
-inline int64_t select_chunks(int64_t n) { return (n + kSelectChunk - 1) / kSelectChunk; }
-// 4 radix rounds x 256 bins of u32, control words, then 2 x u32 per chunk.
+// The many-workgroup select (prompts of kSelectMultiMin tokens and more):
+// chunks of 256 * kpt consecutive tokens, one workgroup each, kpt the
+// smallest of 8, 16, 32 that keeps the chunk count at or below
+// kSelectMaxChunks (0: the prompt is too long for it, one workgroup selects).
+constexpr int kSelectThreads = 256;
+constexpr int kSelectMaxChunks = 64;
+constexpr int64_t kSelectMultiMin = 16385;
+inline int select_kpt(int64_t n) {
+    if (n < kSelectMultiMin) return 0;
+    for (int kpt = 8; kpt <= 32; kpt *= 2)
+        if ((n + (int64_t)kSelectThreads * kpt - 1) / ((int64_t)kSelectThreads * kpt) <= kSelectMaxChunks) return kpt;
+    return 0;
+}
+inline int64_t select_chunk_tokens(int64_t n) { return (int64_t)kSelectThreads * select_kpt(n); }
+inline int64_t select_chunks(int64_t n) {
+    const int64_t ch = select_chunk_tokens(n);
+    return ch > 0 ? (n + ch - 1) / ch : 0;
+}
+// Its workspace: per chunk a 2048-bin u16 histogram of the keys' top 11 bits
+// and its 64 sums of 32 consecutive bins, the forced count, the count of
+// prunable keys above the first round's bin and where its keys in that bin
+// start among all chunks' (the candidates, at most n keys), plus the control
+// words of the first round.
+struct SelectWs {
+    uint16_t* hist;    // [chunks][2048]
+    uint16_t* coarse;  // [chunks][64]: sums of 32 consecutive bins of hist
+    uint32_t* forced;  // [chunks]
+    uint32_t* above;   // [chunks]
+    uint32_t* cstart;  // [chunks]: where a chunk's candidates start in cand
+    uint32_t* ctl;     // [8]: first-round bin, rank left in it, forced total, prunable to choose, candidates
+    uint32_t* cand;    // the keys in the first round's bin, chunk after chunk, each chunk in index order
+};
+// Sized for kSelectMaxChunks chunks and for the candidates of min(n, the
+// largest prompt of the many-workgroup form) tokens rounded up to a chunk of
+// the largest size, so the size never shrinks as n grows (a workspace sized
+// for a prompt serves every shorter one).
+constexpr int64_t kSelectMultiMax = (int64_t)kSelectMaxChunks * kSelectThreads * 32;
 inline size_t select_bytes(int64_t n) {
-    return align_up(sizeof(uint32_t) * (4 * 256 + 64)) +
-           align_up(sizeof(uint32_t) * 2 * (size_t)(select_chunks(n) > 0 ? select_chunks(n) : 1));
+    if (n < kSelectMultiMin) return kAlign;
+    const int64_t m = n < kSelectMultiMax ? n : kSelectMultiMax;
+    const int64_t big = (int64_t)kSelectThreads * 32;
+    const size_t g = (size_t)kSelectMaxChunks;
+    return align_up(sizeof(uint16_t) * 2048 * g) + align_up(sizeof(uint16_t) * 64 * g) +
+           3 * align_up(sizeof(uint32_t) * g) + align_up(8 * sizeof(uint32_t)) +
+           align_up(sizeof(uint32_t) * (size_t)((m + big - 1) / big * big));
+}
+inline SelectWs select_ws(void* base, int64_t n) {
+    (void)n;
+    const size_t g = (size_t)kSelectMaxChunks;
+    char* p = (char*)base;
+    SelectWs w;
+    w.hist = (uint16_t*)p;
+    p += align_up(sizeof(uint16_t) * 2048 * g);
+    w.coarse = (uint16_t*)p;
+    p += align_up(sizeof(uint16_t) * 64 * g);
+    w.forced = (uint32_t*)p;
+    p += align_up(sizeof(uint32_t) * g);
+    w.above = (uint32_t*)p;
+    p += align_up(sizeof(uint32_t) * g);
+    w.cstart = (uint32_t*)p;
+    p += align_up(sizeof(uint32_t) * g);
+    w.ctl = (uint32_t*)p;
+    p += align_up(8 * sizeof(uint32_t));
+    w.cand = (uint32_t*)p;
+    return w;
 }
 inline size_t workspace_bytes(int64_t n) { return gate_bytes(n) + select_bytes(n); }
 

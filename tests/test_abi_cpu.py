@@ -44,7 +44,10 @@ def test_version_status_and_workspace(lib):
     for code in (0, -1, -2, -3, -4, -5):
         assert binding.tg_status_string(code) != "unknown status"
     assert binding.tg_status_string(12345) == "unknown status"
-    sizes = [binding.tg_workspace_bytes(n) for n in (0, 1, 512, 16384, 131072, 1 << 20)]
+    # a workspace sized for a prompt serves every shorter one, across the
+    # sizes where the select changes form or chunk size
+    ns = (0, 1, 512, 16384, 16385, 32768, 131072, 131073, 262144, 262145, 524288, 524289, 1 << 20)
+    sizes = [binding.tg_workspace_bytes(n) for n in ns]
     assert all(s > 0 and s % 256 == 0 for s in sizes)
     assert sizes == sorted(sizes)
 

@@ -140,6 +140,62 @@ def test_select_forced_count_status():
     assert np.array_equal(got, np.arange(n - 50, n - 5))
 
 
+@pytest.mark.parametrize("case", ["ragged_16385", "ragged_50001", "ragged_131071", "kpt16_262147",
+                                  "kpt32_524288", "one_wg_beyond_524289", "int_ties_100000", "student_t_65536",
+                                  "specials_40000", "k_equals_n_70000", "k_one_70000", "all_equal_131072"])
+def test_select_many_workgroups(case):
+    """Prompts past 16384 tokens: the select that runs over chunks of the
+    prompt in several workgroups (three launches), at ragged lengths, each
+    chunk size, heavy ties, heavy tails, special values, the budget
+    extremes and the all-equal closed form; one case past its largest size
+    (the one-workgroup fallback)."""
+    name, n = case.rsplit("_", 1)
+    n = int(n)
+    g = np.random.default_rng(n + len(name))
+    forced = np.zeros(n, np.uint8)
+    forced[g.choice(n, size=96, replace=False)] = 1
+    k = max(96, n // 16)
+    if name == "int_ties":
+        score = g.integers(-6, 7, size=n).astype(np.float32) * 0.5
+    elif name == "student_t":
+        score = synth.student_t_scores(n, seed=9)
+    elif name == "specials":
+        score = g.standard_normal(n).astype(np.float32)
+        sp = g.choice(n, size=4000, replace=False)
+        score[sp] = np.array([np.nan, np.inf, -np.inf, 0.0, -0.0], np.float32)[np.arange(4000) % 5]
+    elif name == "all_equal":
+        score = np.zeros(n, np.float32)
+    else:
+        score = g.standard_normal(n).astype(np.float32)
+    if name == "k_equals":
+        k = n
+    elif name == "k_one":
+        forced[:] = 0
+        k = 1
+    gu.say(f"select many workgroups: {case} k={k}")
+    got, st = _run_select(score, forced, k)
+    assert st == 0
+    if name == "all_equal":
+        fi = np.flatnonzero(forced)
+        want = np.sort(np.concatenate([np.setdiff1d(np.arange(n), fi)[:k - fi.size], fi]))
+        assert np.array_equal(got, want)
+    assert np.array_equal(got, oracle.select_topk(score, forced, k))
+
+
+def test_select_many_workgroups_status():
+    gu.say("select status, many workgroups")
+    n = 70000
+    score = np.random.default_rng(16).standard_normal(n).astype(np.float32)
+    forced = np.zeros(n, np.uint8)
+    forced[-500:] = 1
+    got, st = _run_select(score, forced, 3000, n_forced=400)  # caller's F is wrong
+    assert st == tg.TG_STATUS_FORCED_MISMATCH
+    assert np.array_equal(got, oracle.select_topk(score, forced, 3000))
+    got, st = _run_select(score, forced, 450, n_forced=450)  # 500 forced > k = 450
+    assert st == tg.TG_STATUS_FORCED_MISMATCH | tg.TG_STATUS_FORCED_OVER_K
+    assert np.array_equal(got, np.arange(n - 500, n - 50))
+
+
 # ------------------------------------------------------------- compaction
 
 @pytest.mark.parametrize("n,k,d", [(512, 128, 256), (16384, 2048, 2048), (3001, 1999, 64)])
