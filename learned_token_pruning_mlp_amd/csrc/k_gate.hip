@@ -6,9 +6,11 @@
 // gate sits; slinene.github.io digest, method key points; aiwillknow.com,
 // Figure 1(a)(b)).
 //
-// Kernel 1 (gate_mlp): one workgroup takes 64 residual rows (eight waves for
-// 256 hidden units, two per SIMD, so one wave's load latency hides behind the
-// other's products; four below).  The residual
+// Kernel 1 (gate_mlp): one workgroup takes 64 residual rows, or 128 once the
+// prompt still gives every CU a workgroup that way (each W1 tile read from L2
+// then serves twice the rows); eight waves for 256 hidden units, two per
+// SIMD, so one wave's load latency hides behind the other's products; four
+// below.  The residual
 // row norm is applied after the product, as a per-row scale (the product is
 // linear in the row), so the matrix cores see the exact bf16 residual:
 //     a_ij = r_i * (h_i . w1_j) + b1_j,  r_i = 1/sqrt(mean_k h_ik^2 + eps)
@@ -40,10 +42,12 @@ namespace {
 using tgd::f32x16;
 using tgd::u32x4;
 
-constexpr int kBT = tgi::kGateRowsPerBlock;  // 64 rows per workgroup
-constexpr int kKC = 64;                      // d-columns per LDS tile
+constexpr int kKC = 64;  // d-columns per LDS tile
 
-template <int HD>
+// HD hidden units, BT residual rows per workgroup (64, or 128 on prompts long
+// enough to give every CU a workgroup: each W1 tile read from L2 then serves
+// twice the rows).
+template <int HD, int BT>
 struct Cfg {
     // 256 hidden units: eight waves (two per SIMD, so one wave's LDS and
     // direct-load latency hides behind the other's products); fewer: four
@@ -52,7 +56,7 @@ struct Cfg {
     static constexpr int WAVES_H = HD >= 128 ? 4 : 2;  // waves along hidden units
     static constexpr int WAVES_T = WAVES / WAVES_H;     // waves along tokens
     static constexpr int WH = HD / WAVES_H;             // hidden units per wave
-    static constexpr int WT = kBT / WAVES_T;            // tokens per wave
+    static constexpr int WT = BT / WAVES_T;             // tokens per wave
     static constexpr int MB = WH / 32;                  // 32-row blocks of hidden units
     static constexpr int NB = WT / 32;                  // 32-column blocks of tokens
     static_assert(MB >= 1 && NB >= 1, "tile shape");
@@ -128,16 +132,17 @@ __device__ __forceinline__ void buffer_to_lds16(i32x4 rs, const TG_LDS uint8_t* 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
 #define TG_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
-template <int HD>
-__global__ __launch_bounds__(Cfg<HD>::THREADS) void gate_mlp(const uint16_t* __restrict__ resid,
+template <int HD, int BT>
+__global__ __launch_bounds__((Cfg<HD, BT>::THREADS)) void gate_mlp(const uint16_t* __restrict__ resid,
                                                      const uint16_t* __restrict__ w1,
                                                      const uint16_t* __restrict__ b1,
                                                      const uint16_t* __restrict__ w2, float b2,
                                                      int64_t n, int d, float eps_row,
                                                      float* __restrict__ s_out,
                                                      float* __restrict__ block_ss) {
-    using C = Cfg<HD>;
-    constexpr int H_BYTES = kBT * kKC * 2;            // residual tile: 64 rows x 128 bytes
+    using C = Cfg<HD, BT>;
+    constexpr int kBT = BT;
+    constexpr int H_BYTES = kBT * kKC * 2;            // residual tile: BT rows x 128 bytes
     constexpr int W_BYTES = HD * kKC * 2;             // W1 tile: HD rows x 128 bytes
     constexpr int STAGE = H_BYTES + W_BYTES;
     constexpr int H_LOADS = H_BYTES / 1024 / C::WAVES;  // 1 KB direct-load instructions per wave
@@ -340,7 +345,8 @@ __global__ __launch_bounds__(Cfg<HD>::THREADS) void gate_mlp(const uint16_t* __r
     }
     __syncthreads();
     if (wave == 0) {
-        float v = sS[lane];  // kBT == 64: one value per lane, fixed-order tree
+        float v = sS[lane];  // one or two values per lane, fixed-order tree
+        if constexpr (kBT == 128) v += sS[lane + 64];
         v = tgd::wave_sum(v);
         if (lane == 0) block_ss[blockIdx.x] = v;
     }
@@ -380,13 +386,20 @@ __global__ __launch_bounds__(kNormThreads) void gate_seqnorm(const float* s_raw,
     }
 }
 
+// Rows per scorer workgroup for a prompt of n tokens: 128 once that still
+// gives each of the 256 CUs a workgroup, else 64.
+inline int gate_rows_per_block(int64_t n) { return n >= (int64_t)256 * 128 ? 128 : 64; }
+
 template <int HD>
 int launch_gate_hd(const uint16_t* resid, const uint16_t* w1, const uint16_t* b1, const uint16_t* w2,
-                   float b2, int64_t n, int d, float eps_row, float* s_out, float* block_ss,
+                   float b2, int64_t n, int d, float eps_row, float* s_out, float* block_ss, int64_t nb,
                    hipStream_t s) {
-    const int64_t nb = tgi::gate_blocks(n);
-    hipLaunchKernelGGL(gate_mlp<HD>, dim3((unsigned)nb), dim3(Cfg<HD>::THREADS), 0, s, resid, w1, b1, w2, b2, n,
-                       d, eps_row, s_out, block_ss);
+    if (gate_rows_per_block(n) == 128)
+        hipLaunchKernelGGL((gate_mlp<HD, 128>), dim3((unsigned)nb), dim3(Cfg<HD, 128>::THREADS), 0, s, resid, w1, b1,
+                           w2, b2, n, d, eps_row, s_out, block_ss);
+    else
+        hipLaunchKernelGGL((gate_mlp<HD, 64>), dim3((unsigned)nb), dim3(Cfg<HD, 64>::THREADS), 0, s, resid, w1, b1,
+                           w2, b2, n, d, eps_row, s_out, block_ss);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_EDEVICE;
 }
 
@@ -438,17 +451,19 @@ int launch_gate_score(const uint16_t* resid, const uint16_t* w1, const uint16_t*
     hipStream_t s = (hipStream_t)stream;
     float* block_ss = reinterpret_cast<float*>(ws);
     float* s_out = score_raw ? score_raw : score_norm;
+    const int bt = gate_rows_per_block(n);
+    const int64_t nb = (n + bt - 1) / bt;  // (at most gate_blocks(n) partial sums)
     int rc;
     switch (hd) {
-        case 64: rc = launch_gate_hd<64>(resid, w1, b1, w2, b2, n, d, eps_row, s_out, block_ss, s); break;
-        case 128: rc = launch_gate_hd<128>(resid, w1, b1, w2, b2, n, d, eps_row, s_out, block_ss, s); break;
-        case 256: rc = launch_gate_hd<256>(resid, w1, b1, w2, b2, n, d, eps_row, s_out, block_ss, s); break;
+        case 64: rc = launch_gate_hd<64>(resid, w1, b1, w2, b2, n, d, eps_row, s_out, block_ss, nb, s); break;
+        case 128: rc = launch_gate_hd<128>(resid, w1, b1, w2, b2, n, d, eps_row, s_out, block_ss, nb, s); break;
+        case 256: rc = launch_gate_hd<256>(resid, w1, b1, w2, b2, n, d, eps_row, s_out, block_ss, nb, s); break;
         default: return TG_EUNSUPPORTED;
     }
     if (rc != TG_OK) return rc;
     const int64_t per = (int64_t)kNormThreads * kNormPerThread;
     hipLaunchKernelGGL(gate_seqnorm, dim3((unsigned)((n + per - 1) / per)), dim3(kNormThreads), 0, s, s_out,
-                       block_ss, gate_blocks(n), n, eps_seq, score_norm);
+                       block_ss, nb, n, eps_seq, score_norm);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_EDEVICE;
 }
 

@@ -51,6 +51,19 @@ def test_gate_score(n, d, hd, b1, b2):
     assert np.array_equal(again, got_norm)
 
 
+@pytest.mark.parametrize("n,d,hd,b1,b2", [(32768, 256, 64, True, 0.1), (40001, 512, 128, False, 0.0),
+                                          (32769, 2048, 256, True, -0.3)])
+def test_gate_score_long_prompt_tiles(n, d, hd, b1, b2):
+    """Prompts long enough for 128 residual rows per workgroup: every hidden
+    width, ragged tails (a last workgroup with 1 or 65 rows)."""
+    gu.say(f"gate_score long-prompt tiles n={n} d={d} hd={hd}")
+    inp = _gate_case(n, d, hd, seed=13, with_b1=b1, b2=b2)
+    ref_norm, ref_raw = oracle.gate_score(inp.resid, inp.w1, inp.b1, inp.w2, inp.b2)
+    got_norm, got_raw = _run_gate(inp)
+    assert np.max(np.abs(got_raw - ref_raw)) <= gu.SCORE_ABS
+    assert np.max(np.abs(got_norm - ref_norm)) <= gu.SCORE_ABS
+
+
 def test_gate_score_zero_weights_all_equal():
     gu.say("gate_score W1=0")
     inp = _gate_case(1000, 256, 64, seed=12, w1_zero=True)
