@@ -75,7 +75,8 @@ WORKLOADS = {
                 "qwen3-1.7b gate layer, N=16384, F=64, K=N (no pruning), 1 upper layer", 1, False),
 }
 N_LOWER_KV_LAYERS = 2   # layers below the gate whose full-length K/V the n128k step trims
-EV_STRIDE = 8           # the dominant kernel is bracketed by events on every 8th timed step
+EV_STRIDE = 6           # the dominant kernel is bracketed by events on every 6th timed step,
+EV_OFFSET = 3           # starting with the 4th (the first step after the synchronisation is left out)
 
 
 def attn_flops(shp):
@@ -248,8 +249,9 @@ def main():
     # Only the dominant stage's first launch is bracketed by events (on the
     # stream its kernel runs on), on every EV_STRIDE-th step whatever the
     # step count: each event record adds a barrier packet and a timestamp to
-    # the queue, which is instrumentation, not work of the path.
-    ev_steps = list(range(0, args.steps, EV_STRIDE))
+    # the queue, which is instrumentation, not work of the path.  The events
+    # also take in the dispatch gap before the kernel starts.
+    ev_steps = list(range(min(EV_OFFSET, args.steps - 1), args.steps, EV_STRIDE))
     dom_ev = {i: (Ev(), Ev()) for i in ev_steps}
 
     def timed_step(i):
