@@ -21,7 +21,10 @@
 //    to the diagonal: S^T = K.Q^T and dP^T = V.dO^T on the matrix cores (a
 //    lane owns a query column, so the row values are per-lane scalars), then
 //    dq^T += K^T.dU^T with K^T read from LDS by the transposing read, and the
-//    per-(head, query block) partials of dlambda and of sum_j dU s_j.
+//    per-(head, query block) partials of dlambda and of sum_j dU s_j.  The
+//    four waves of a workgroup (two q heads of a kv group x two adjacent
+//    query blocks) share one stream of K/V blocks, and two workgroups fit a
+//    CU (two waves a SIMD).
 //  * bwd_dkv: one wave per (kv head, 32-key block, share of the group's q
 //    heads) walks the query blocks from the diagonal on: S = Q.K^T and
 //    dP = dO.V^T (a lane owns a key column), then dv^T += dO^T.P and
@@ -31,9 +34,10 @@
 //  * bwd_reduce: the per-kv-head and per-block partials summed in a fixed
 //    order.
 // No atomics: results are deterministic.  P and dU enter the matrix cores as
-// bf16 (fp32 accumulation).  Each wave streams its blocks through two LDS
-// stages of its own, filled by direct loads one block ahead; rows past the
-// end read as zeros through the buffer bounds.
+// bf16 (fp32 accumulation).  Blocks stream through two LDS stages (per
+// workgroup in the dq pass, per wave in the dk/dv pass), filled by direct
+// loads one block ahead; rows past the end read as zeros through the buffer
+// bounds.
 #include <hip/hip_runtime.h>
 
 #include "tg_device.h"
@@ -190,32 +194,67 @@ __device__ __forceinline__ void load_block(const uint16_t* src, uint32_t bytes, 
     }
 }
 
-// ---- dq, and per-(head, query block) partials of dlambda and of sum dU s
-// Each wave streams its key blocks through two LDS stages of its own (K
-// block, V block, 64 key scores): the loads of block kb+1 fly while block kb
-// is multiplied.
+// The direct loads of load_block<D> numbered it0, it0 + step, ... (a share of
+// them, for a wave of a workgroup that loads a block together).
 template <int D>
-__global__ __launch_bounds__(64 * kWavesPerBlock) void bwd_dq(
+__device__ __forceinline__ void load_block_share(const uint16_t* src, uint32_t bytes, int heads, int hh, int row0,
+                                                 TG_LDS uint8_t* blk, int lane, int it0, int step) {
+    using G = Geo<D>;
+#pragma unroll
+    for (int it = 0; it < G::PIECES / 2; ++it) {
+        if ((it - it0) % step != 0 || it < it0) continue;
+        const int e = it * 64 + lane;
+        const int r = e / G::PIECES, c = (e % G::PIECES) ^ swz<G::PIECES>(r);
+        const uint32_t voff = ((uint32_t)(row0 + r) * (uint32_t)heads + (uint32_t)hh) * (uint32_t)G::ROW_BYTES + 16u * c;
+        lds_load<16>(src, bytes, blk + it * 1024, voff);
+    }
+}
+
+// Workgroup barrier that no LDS access moves across (the compiler sees a
+// memory clobber on both sides).
+__device__ __forceinline__ void lds_barrier() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
+// ---- dq, and per-(head, query block) partials of dlambda and of sum dU s
+// A workgroup's four waves take HPW q heads of one kv head x 4 / HPW
+// adjacent query blocks, so they all need the same key blocks: each K and V
+// block (and its 32 key scores) is streamed once into a two-stage LDS ring
+// that the four waves fill together and read together; the loads of block
+// kb+1 fly while block kb is multiplied.  A wave multiplies the key blocks up
+// to its own query block.
+template <int D, int HPW>
+__global__ __launch_bounds__(64 * kWavesPerBlock, 2) void bwd_dq(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ key_score, const float* __restrict__ gains, const int32_t* __restrict__ pos,
     const uint16_t* __restrict__ dO, const float4* __restrict__ rowv, int nk, int hq, int hkv, int kp,
     float* __restrict__ dq, float* __restrict__ dlamc, float* __restrict__ dgp) {
     using G = Geo<D>;
-    constexpr int STAGE = 2 * G::BLOCK_BYTES + 256;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[kWavesPerBlock * 2 * STAGE];
+    constexpr int QBW = kWavesPerBlock / HPW;         // query blocks per workgroup
+    constexpr int STAGE = 2 * G::BLOCK_BYTES + 256;   // K block, V block, 64 key scores (32 used)
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int l32 = lane & 31, g = lane >> 5;
+    const int grp = hq / hkv;
     const int nqb = (nk + 31) / 32;
-    const int item = blockIdx.x * kWavesPerBlock + w;
-    if (item >= hq * nqb) return;
-    // the longest walks (last query blocks) first
-    const int qb = nqb - 1 - item / hq, h = item % hq;
-    const int hk = h / (hq / hkv);
+    const int ngq = (nqb + QBW - 1) / QBW;            // query-block groups
+    const int nhg = grp / HPW;                        // head groups of a kv head
+    // work item: (query-block group, kv head, head group); the groups of the
+    // last query blocks (the longest walks) first
+    const int item = blockIdx.x;
+    const int gq = ngq - 1 - item / (hkv * nhg);
+    const int hk = (item / nhg) % hkv, hg = item % nhg;
+    const int h = hk * grp + hg * HPW + w % HPW;
+    const int qb = gq * QBW + w / HPW;                 // this wave's query block
+    const int qb_last = min(gq * QBW + QBW - 1, nqb - 1);
+    const bool live = qb < nqb;
     const int t = qb * 32 + l32;
-    const bool ok = t < nk;
+    const bool ok = live && t < nk;
     const float rs = 1.0f / sqrtf((float)D);
     const float sg = sqrtf((float)D) * gains[h];
-    TG_LDS uint8_t* st0 = (TG_LDS uint8_t*)smem + w * 2 * STAGE;
+    TG_LDS uint8_t* st0 = (TG_LDS uint8_t*)smem;
     TG_LDS uint8_t* st1 = st0 + STAGE;
     const uint32_t kv_bytes = (uint32_t)nk * (uint32_t)hkv * (uint32_t)G::ROW_BYTES;
 
@@ -225,7 +264,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void bwd_dq(
         qreg[s] = global_operand<D>(q, hq, h, t, nk, g, s);
         doreg[s] = global_operand<D>(dO, hq, h, t, nk, g, s);
     }
-    const float4 rv = rowv[(int64_t)h * kp + t];  // t < kp
+    const float4 rv = live ? rowv[(int64_t)h * kp + t] : float4{0.0f, 0.0f, 0.0f, 0.0f};  // t < kp
     const float a_t = rv.x, lse_t = rv.y, d_t = rv.z, lam_t = rv.w;
 
     f32x16 dqa[G::DB];
@@ -233,15 +272,19 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void bwd_dq(
     for (int db = 0; db < G::DB; ++db) dqa[db] = f32x16{};
     float dl = 0.0f, dgs = 0.0f;
 
+    // block kb into a stage: each wave issues its share of the K and V loads;
+    // wave 0 also the scores
     auto issue = [&](int kb, TG_LDS uint8_t* __restrict__ nb) {
         const int j0 = kb * 32;
-        load_block<D>(k, kv_bytes, hkv, hk, j0, nb, lane);
-        load_block<D>(v, kv_bytes, hkv, hk, j0, nb + G::BLOCK_BYTES, lane);
-        lds_load<4>(key_score, (uint32_t)nk * 4u, nb + 2 * G::BLOCK_BYTES, (uint32_t)(j0 + lane) * 4u);
+        load_block_share<D>(k, kv_bytes, hkv, hk, j0, nb, lane, w, kWavesPerBlock);
+        load_block_share<D>(v, kv_bytes, hkv, hk, j0, nb + G::BLOCK_BYTES, lane, w, kWavesPerBlock);
+        if (w == 0) lds_load<4>(key_score, (uint32_t)nk * 4u, nb + 2 * G::BLOCK_BYTES, (uint32_t)(j0 + lane) * 4u);
     };
     auto step = [&](int kb, TG_LDS uint8_t* __restrict__ cb, TG_LDS uint8_t* __restrict__ nb) {
-        TG_WAIT_VMCNT(0);  // this block is in LDS
-        if (kb < qb) issue(kb + 1, nb);
+        TG_WAIT_VMCNT(0);  // this wave's share of block kb is in LDS ...
+        lds_barrier();     // ... and every wave's; every wave is done with the other stage
+        if (kb < qb_last) issue(kb + 1, nb);
+        if (!live || kb > qb) return;  // (wave-uniform) this block is in this wave's future
         const int j0 = kb * 32;
         TG_LDS uint8_t* kblk = cb;
         TG_LDS uint8_t* vblk = cb + G::BLOCK_BYTES;
@@ -281,10 +324,11 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void bwd_dq(
                 dqa[db] = tgd::mfma32(tr_operand<D>(kblk, lane, db, s), pb[s], dqa[db]);
     };
     issue(0, st0);
-    for (int kb = 0; kb <= qb; kb += 2) {
+    for (int kb = 0; kb <= qb_last; kb += 2) {
         step(kb, st0, st1);
-        if (kb + 1 <= qb) step(kb + 1, st1, st0);
+        if (kb + 1 <= qb_last) step(kb + 1, st1, st0);
     }
+    if (!live) return;
     // dq_t[d]: accumulator unit u holds head_dim rows 32 (u/4) + 8 (u%4) + 4 g .. +3
     if (ok) {
 #pragma unroll
@@ -541,10 +585,18 @@ int launch_bwd_d(const uint16_t* q, const uint16_t* k, const uint16_t* v, const 
     hipLaunchKernelGGL(bwd_prep<D>, dim3((unsigned)(((int64_t)hq * kp + RPB - 1) / RPB)), dim3(256), 0, s, ws.out,
                        dout, ws.lse, pos, temp_coef, nk, hq, kp, rowv);
     const int nqb = (nk + 31) / 32;
-    hipLaunchKernelGGL(bwd_dq<D>, dim3((unsigned)((hq * nqb + kWavesPerBlock - 1) / kWavesPerBlock)),
-                       dim3(64 * kWavesPerBlock), 0, s, q, k, v, key_score, gains, pos, dout, rowv, nk, hq, hkv, kp,
-                       dq, ws.dlamc, ws.dgp);
     const int grp = hq / hkv;
+    // dq: two heads of a kv group x two query blocks per workgroup (one head x
+    // four query blocks when the group has one head)
+    if (grp % 2 == 0) {
+        const int items = hkv * (grp / 2) * ((nqb + 1) / 2);
+        hipLaunchKernelGGL((bwd_dq<D, 2>), dim3((unsigned)items), dim3(64 * kWavesPerBlock), 0, s, q, k, v, key_score,
+                           gains, pos, dout, rowv, nk, hq, hkv, kp, dq, ws.dlamc, ws.dgp);
+    } else {
+        const int items = hkv * grp * ((nqb + 3) / 4);
+        hipLaunchKernelGGL((bwd_dq<D, 1>), dim3((unsigned)items), dim3(64 * kWavesPerBlock), 0, s, q, k, v, key_score,
+                           gains, pos, dout, rowv, nk, hq, hkv, kp, dq, ws.dlamc, ws.dgp);
+    }
     const int wsplit = grp >= 4 ? 4 : (grp >= 2 ? 2 : 1);
     const int kbs = kWavesPerBlock / wsplit;
     hipLaunchKernelGGL(bwd_dkv<D>, dim3((unsigned)(hkv * ((nqb + kbs - 1) / kbs))), dim3(64 * kWavesPerBlock), 0, s,
