@@ -15,9 +15,10 @@
 // Rows of S evolve independently given the shared k, q and gates, so a wave
 // takes 2 rows of one head: lane (r, c) holds row r, columns c*dk/32 ..
 // +dk/32 in registers; the two row dot products reduce over the row's 32
-// lanes (four DPP steps and one cross-row swap).  Tokens are taken in order (the recurrence is sequential);
-// the loads of the next eight tokens' q, k, v and gates are in flight while
-// the current one is applied.  fp32 state and arithmetic; deterministic.
+// lanes (four DPP steps and one cross-row swap).  Tokens are taken in order (the recurrence is sequential),
+// in unrolled groups of eight: the group's LDS reads of q, k, v and the gates
+// go out together, and one token's output reduction overlaps the next one's
+// state chain.  fp32 state and arithmetic; deterministic.
 #include <hip/hip_runtime.h>
 
 #include "tg_device.h"
@@ -27,6 +28,7 @@ namespace {
 
 constexpr int kWaves = 4;   // waves per workgroup (consecutive row pairs of one head)
 constexpr int kChunk = 32;  // tokens per LDS stage
+constexpr int kGroup = 8;   // tokens per unrolled group
 
 #define TG_LDS __attribute__((address_space(3)))
 typedef unsigned int lu2 __attribute__((ext_vector_type(2)));  // LDS-side uint2
@@ -142,8 +144,9 @@ __global__ __launch_bounds__(64 * kWaves) void gdn_scan(const uint16_t* __restri
         const TG_LDS float* ac = (const TG_LDS float*)(cb + 2 * C::KQ + C::VB);
         const TG_LDS float* bc = ac + kChunk;
         float ov = 0.0f;  // lane c keeps the output of token t0 + c of its row
-#pragma unroll 8
-        for (int tt = 0; tt < tn; ++tt) {
+        // one token; `live` is false only past the last token of a short chunk
+        // (uniform over the workgroup), where the state is left as it is
+        auto token = [&](int tt, bool live) {
             float kf[CPL], qf[CPL];
             uint32_t kw[CPL / 2], qw[CPL / 2];
             if constexpr (CPL == 4) {
@@ -169,11 +172,25 @@ __global__ __launch_bounds__(64 * kWaves) void gdn_scan(const uint16_t* __restri
             float o = 0.0f;
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
-                S[i] = fmaf(a, S[i], wv * kf[i]);
+                const float si = fmaf(a, S[i], wv * kf[i]);
+                S[i] = live ? si : S[i];
                 o = fmaf(S[i], qf[i], o);
             }
             o = sum32(o);
             ov = c == tt ? o : ov;
+        };
+        // groups of kGroup tokens with a fixed trip count, so that the group's
+        // LDS reads are issued ahead of the chain of state updates
+        if (tn == kChunk) {
+            for (int g = 0; g < kChunk; g += kGroup) {
+#pragma unroll
+                for (int j = 0; j < kGroup; ++j) token(g + j, true);
+            }
+        } else {
+            for (int g = 0; g < tn; g += kGroup) {
+#pragma unroll
+                for (int j = 0; j < kGroup; ++j) token(g + j, g + j < tn);
+            }
         }
         if (c < tn) out[((t0 + c) * hv + h) * DV + row] = ov;
     };
