@@ -30,10 +30,11 @@
 //    key-bias scale change sign, which is exact, so every row has a positive
 //    exp2 scale and one code path serves all rows.
 //  * Per 32-key block a wave issues all its K-operand and score reads, then
-//    the eight S^T products with the transposing V reads between them, so
-//    LDS latency overlaps the matrix cores; it raises its issue priority
-//    while it issues the P.V products, so that the SIMD's other wave, in its
-//    softmax, does not hold them back.
+//    the eight S^T products, then (first block of a super-tile) the next
+//    super-tile's loads, then the transposing V reads, so LDS and memory-queue
+//    latency overlap the matrix cores; it raises its issue priority while it
+//    issues the P.V products, so that the SIMD's other wave, in its softmax,
+//    does not hold them back.
 //  * Work split: a workgroup owns one GQA kv head, HPW of its q heads and a
 //    pair of 32-row query blocks (b, last - b), so every workgroup carries the
 //    same causal work.  The keys of a query block are streamed as super-tiles
@@ -391,14 +392,15 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
     // precision).  This skips nearly every rescale of the accumulators.
     constexpr float kTau = 8.0f;
 
-    // ---- one 32-key block of this wave's slice: S^T, online softmax, P.V.
+    // ---- one 32-key block of this wave's slice: S^T, online softmax, P.V,
+    // in two parts: the front issues the K-operand and score reads and the
+    // S^T products, the back reads V and does the softmax and P.V.
     // Every row has a_t > 0, so the logits in the exp2 domain are a_t * S,
     // the block max is a_t * max(S) (rounding is monotonic) and
     // p = 2^(a_t * S - m) is one FMA and one exp2.
-    auto key_block = [&](int k0, int kb, const uint8_t* __restrict__ tK, const uint8_t* __restrict__ tV,
-                         const float* __restrict__ tS) __attribute__((always_inline)) {
+    auto block_front = [&](int kb, const uint8_t* __restrict__ tK,
+                           const float* __restrict__ tS) __attribute__((always_inline)) -> f32x16 {
         const uint8_t* bK = tK + kb * 32 * C::ROW_BYTES;
-        const uint8_t* bV = tV + kb * 32 * C::ROW_BYTES;
         const float* bS = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(tS) + soff) + 32 * kb;
         // all K-operand and score reads of the block go out together
         u32x4 ka[C::QS];
@@ -417,11 +419,14 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
             sacc[4 * i4 + 3] = sgl * sv[i4].w;
         }
         // Scheduling boundary: the operand reads and the bias products above
-        // are issued first; the products below then interleave with the V
-        // reads that follow (the order that measured fastest at 8K-16K keys).
+        // are issued first, then the products below.
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < C::QS; ++s) sacc = tgd::mfma32(ka[s], qreg[s], sacc);
+        return sacc;
+    };
+    auto block_back = [&](int k0, int kb, const uint8_t* __restrict__ tV, f32x16 sacc) __attribute__((always_inline)) {
+        const uint8_t* bV = tV + kb * 32 * C::ROW_BYTES;
         // V operands: the transposing read hands lane jj of each 16-lane group
         // four consecutive keys of one head_dim column; issued before the
         // softmax so they land while it runs.
@@ -482,13 +487,28 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
 
     // ---- this wave's slice of one super-tile: keys j0 + WKEYS*sp .. +WKEYS-1,
     // taken as KB blocks of 32 one after another.
+    // `mid` issues the next super-tile's loads.  It goes out right behind the
+    // first block's queued S^T products, so that a wave held up by a full
+    // memory queue waits while its matrix core is busy rather than before the
+    // block starts.  It has exactly one call site (a second copy of the load
+    // code costs registers), reached also by a wave whose slice lies entirely
+    // in its future.
     auto compute = [&](int j0, const uint8_t* __restrict__ tK, const uint8_t* __restrict__ tV,
-                       const float* __restrict__ tS) {
+                       const float* __restrict__ tS, auto&& mid) {
+        const int k00 = j0 + rb0;
+        const bool live = k00 <= wave_last;  // wave-uniform
+        f32x16 sacc;
+        if (live) sacc = block_front(0, tK, tS);
+        __builtin_amdgcn_sched_barrier(0);
+        mid();
+        __builtin_amdgcn_sched_barrier(0);
+        if (!live) return;
+        block_back(k00, 0, tV, sacc);
 #pragma unroll 1
-        for (int kb = 0; kb < KB; ++kb) {  // one block at a time keeps the register footprint of one
+        for (int kb = 1; kb < KB; ++kb) {  // one block at a time keeps the register footprint of one
             const int k0 = j0 + rb0 + 32 * kb;
             if (k0 > wave_last) break;  // the rest of the slice is in this wave's future
-            key_block(k0, kb, tK, tV, tS);
+            block_back(k0, kb, tV, block_front(kb, tK, tS));
         }
     };
 
@@ -504,8 +524,10 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
         if (st == 0) begin_block(inA ? qbA : qbB);
         TG_WAIT_VMCNT(0);
         __builtin_amdgcn_s_barrier();
-        if (it + 1 < ntot) issue(it + 1, nK, nV, nS);
-        compute(st * C::SKEYS, cK, cV, cS);
+        const bool more = it + 1 < ntot;
+        compute(st * C::SKEYS, cK, cV, cS, [&]() __attribute__((always_inline)) {
+            if (more) issue(it + 1, nK, nV, nS);
+        });
         const int last = inA ? nA - 1 : ntot - nA - 1;
         if (st == last) finish_block(cK, cV);  // K and V of this stage serve as merge scratch
     };
