@@ -38,7 +38,8 @@ def _run_gate(inp, eps_row=1e-6, eps_seq=1e-6, raw=True):
 
 @pytest.mark.parametrize("n,d,hd,b1,b2", [(512, 256, 64, False, 0.0), (1000, 256, 64, True, 0.3),
                                           (777, 512, 128, True, -0.2), (333, 2048, 256, False, 0.0),
-                                          (1, 128, 64, True, 0.0)])
+                                          (1, 128, 64, True, 0.0), (700, 192, 128, True, 0.1),
+                                          (300, 320, 256, False, 0.0)])
 def test_gate_score(n, d, hd, b1, b2):
     gu.say(f"gate_score n={n} d={d} hd={hd}")
     inp = _gate_case(n, d, hd, seed=11, with_b1=b1, b2=b2)
