@@ -184,11 +184,19 @@ class Path:
             if ev is not None and ev[j] is not None:
                 ev[j].record(self.stream)
         r = self.resid[i % len(self.resid)]
-        mark(0)
-        tg.tg_gate_score(r, self.w1, None, self.w2, 0.0, 1e-6, 1e-6, self.s_norm, None, self.ws)
-        mark(1)
         sc = self.s_norm if self.t_scores is None else self.t_scores
-        tg.tg_select_topk(sc, self.forced, shp.n_forced, shp.k, self.kept, None, self.ws)
+        # scorer and select in one call (the sequence norm inside the select
+        # up to 16384 tokens), unless they select on drawn scores or a mark
+        # between them is asked for (the per-stage pass)
+        fused = self.t_scores is None and (ev is None or (ev[1] is None and ev[2] is None))
+        mark(0)
+        if fused:
+            tg.tg_gate_score_select(r, self.w1, None, self.w2, 0.0, 1e-6, 1e-6, self.forced, shp.n_forced, shp.k,
+                                    self.s_norm, None, self.kept, None, self.ws)
+        else:
+            tg.tg_gate_score(r, self.w1, None, self.w2, 0.0, 1e-6, 1e-6, self.s_norm, None, self.ws)
+            mark(1)
+            tg.tg_select_topk(sc, self.forced, shp.n_forced, shp.k, self.kept, None, self.ws)
         mark(2)
         tg.tg_compact(self.kept, shp.n, r, self.resid_k, self.pos, self.pos_k, sc, self.score_k, extra=self.extra)
         mark(3)
@@ -326,6 +334,10 @@ def main():
         "median_step_ms": median_step_ms,
         "attn_mfma_pct": 100.0 * attn_tflops / PEAK_BF16_TFLOPS,
         "stage_us": {s: round(v * 1e3, 3) for s, v in per_stage.items()},
+        # the per-stage pass calls the scorer and the select separately; the
+        # timed and median steps call them as one tg_gate_score_select
+        # (unless the select takes drawn scores)
+        "stage_calls": "separate" if path.t_scores is not None else "separate in stage_us; fused when timed",
         "stage_event_sum_ms": sum(per_stage.values()),
         "attn_tflops": attn_tflops,
         "gate_hbm_gbs": gate_gbs,

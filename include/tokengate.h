@@ -4,7 +4,8 @@
  * The path runs at the gate layer L of a decoder and in the layers above it:
  *   tg_gate_score      -> a small MLP scores every token's normalised residual,
  *                         and the scores are RMS-normalised along the sequence;
- *   tg_select_topk     -> forced-keep top-K picks the tokens that continue;
+ *   tg_select_topk     -> forced-keep top-K picks the tokens that continue
+ *                         (tg_gate_score_select: scorer and select in one call);
  *   tg_compact         -> the kept rows, their original positions, their scores
  *                         and any extra per-token streams (KV rows) are gathered;
  *   tg_rope, tg_rope_qk -> (auxiliary) rotary embedding at the original positions;
@@ -143,6 +144,21 @@ int tg_gate_score_noalloc(const tg_bf16* resid, const tg_bf16* w1, const tg_bf16
 int tg_select_topk(const float* score, const uint8_t* forced, int64_t n, int64_t n_forced,
                    int64_t k, int32_t* kept_idx, int32_t* dev_status, void* workspace,
                    size_t workspace_bytes, void* stream);
+
+/*
+ * tg_gate_score_select -- tg_gate_score, then tg_select_topk on its
+ * normalised scores, in one call [P1 gate][P2 method][P3 how][P5 Fig 1(a)(b)]:
+ * the same score_norm, score_raw, kept_idx and dev_status as the two calls,
+ * bit for bit.  Up to 16384 tokens the sequence norm runs inside the
+ * one-workgroup select (one launch fewer); longer prompts take the two
+ * calls' kernels.  Arguments: those of tg_gate_score and tg_select_topk
+ * (score_norm must also be 16-byte aligned); checks: both calls' checks
+ * (n >= 1).  Workspace: tg_workspace_bytes(n).
+ */
+int tg_gate_score_select(const tg_bf16* resid, const tg_bf16* w1, const tg_bf16* b1, const tg_bf16* w2, float b2,
+                         int64_t n, int32_t d, int32_t hd, float eps_row, float eps_seq, const uint8_t* forced,
+                         int64_t n_forced, int64_t k, float* score_norm, float* score_raw, int32_t* kept_idx,
+                         int32_t* dev_status, void* workspace, size_t workspace_bytes, void* stream);
 
 /* One extra per-token row stream for tg_compact: dst row t = src row kept_idx[t]. */
 typedef struct tg_gather {

@@ -27,7 +27,7 @@ TG_STATUS_FORCED_OVER_K = 2
 TG_MAX_GATHER = 16
 
 EXPORTS = ("tg_status_string", "tg_abi_version", "tg_workspace_bytes", "tg_gate_score", "tg_gate_score_noalloc",
-           "tg_select_topk", "tg_compact", "tg_rope", "tg_rope_qk", "tg_gated_attention",
+           "tg_select_topk", "tg_gate_score_select", "tg_compact", "tg_rope", "tg_rope_qk", "tg_gated_attention",
            "tg_rmsnorm", "tg_swiglu", "tg_blas_create", "tg_blas_destroy", "tg_linear",
            "tg_attention_bwd_workspace_bytes", "tg_gated_attention_bwd", "tg_gate_score_bwd_workspace_bytes",
            "tg_gate_score_bwd", "tg_gated_delta_rule")
@@ -68,6 +68,9 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
     L.tg_gate_score_noalloc.restype = ctypes.c_int
     L.tg_select_topk.argtypes = [P, P, I64, I64, I64, P, P, P, ctypes.c_size_t, P]
     L.tg_select_topk.restype = ctypes.c_int
+    L.tg_gate_score_select.argtypes = [P, P, P, P, F, I64, I32, I32, F, F, P, I64, I64, P, P, P, P, P,
+                                       ctypes.c_size_t, P]
+    L.tg_gate_score_select.restype = ctypes.c_int
     L.tg_compact.argtypes = [P, I64, I64, P, P, I32, P, P, P, P, P, I32, P]
     L.tg_compact.restype = ctypes.c_int
     L.tg_rope.argtypes = [P, P, I64, I32, I32, ctypes.c_double, P]
@@ -217,6 +220,29 @@ def tg_select_topk(score: torch.Tensor, forced: Optional[torch.Tensor], n_forced
     _check("tg_select_topk", load().tg_select_topk(
         _ptr(score), _ptr(forced), n, int(n_forced), int(k), _ptr(kept_idx), _ptr(dev_status), _ptr(ws),
         ws.numel(), _stream(stream)))
+
+
+def tg_gate_score_select(resid: torch.Tensor, w1: torch.Tensor, b1: Optional[torch.Tensor], w2: torch.Tensor,
+                         b2: float, eps_row: float, eps_seq: float, forced: Optional[torch.Tensor], n_forced: int,
+                         k: int, score_norm: torch.Tensor, score_raw: Optional[torch.Tensor], kept_idx: torch.Tensor,
+                         dev_status: Optional[torch.Tensor], ws: torch.Tensor, stream=None) -> None:
+    """tg_gate_score then tg_select_topk on its normalised scores, in one call."""
+    n, d = resid.shape
+    hd = w1.shape[0]
+    _need(resid, "resid", torch.bfloat16, (n, d))
+    _need(w1, "w1", torch.bfloat16, (hd, d))
+    _need(b1, "b1", torch.bfloat16, (hd,), optional=True)
+    _need(w2, "w2", torch.bfloat16, (hd,))
+    _need(forced, "forced", torch.uint8, (n,), optional=True)
+    _need(score_norm, "score_norm", torch.float32, (n,))
+    _need(score_raw, "score_raw", torch.float32, (n,), optional=True)
+    _need(kept_idx, "kept_idx", torch.int32, (k,))
+    _need(dev_status, "dev_status", torch.int32, (1,), optional=True)
+    _need(ws, "ws", torch.uint8)
+    _check("tg_gate_score_select", load().tg_gate_score_select(
+        _ptr(resid), _ptr(w1), _ptr(b1), _ptr(w2), float(b2), n, d, hd, float(eps_row), float(eps_seq),
+        _ptr(forced), int(n_forced), int(k), _ptr(score_norm), _ptr(score_raw), _ptr(kept_idx), _ptr(dev_status),
+        _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def tg_compact(kept_idx: torch.Tensor, n: int, resid: Optional[torch.Tensor], resid_out: Optional[torch.Tensor],

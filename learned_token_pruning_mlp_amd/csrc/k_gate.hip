@@ -359,8 +359,9 @@ __global__ __launch_bounds__(kNormThreads) void gate_seqnorm(const float* s_raw,
                                                              const float* __restrict__ block_ss,
                                                              int64_t nblocks, int64_t n, float eps_seq,
                                                              float* s_norm) {
+    static_assert(kNormThreads == tgd::kSeqSumThreads, "every thread takes part in the fixed-order sum");
     __shared__ double red[kNormThreads / 64];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x;
     // this thread's raw scores first: their loads overlap the reduction
     const int64_t base = (int64_t)blockIdx.x * kNormThreads * kNormPerThread;
     float x[kNormPerThread];
@@ -369,32 +370,22 @@ __global__ __launch_bounds__(kNormThreads) void gate_seqnorm(const float* s_raw,
         const int64_t i = base + (int64_t)e * kNormThreads + tid;
         x[e] = i < n ? s_raw[i] : 0.0f;
     }
-    double acc = 0.0;
-    for (int64_t b = tid; b < nblocks; b += kNormThreads) acc += (double)block_ss[b];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-    if (lane == 0) red[wave] = acc;
+    tgd::seq_ss_partial(block_ss, nblocks, red);
     __syncthreads();
-    double tot = 0.0;
-#pragma unroll
-    for (int w = 0; w < kNormThreads / 64; ++w) tot += red[w];
-    const float rho = (float)sqrt(tot / (double)n + (double)eps_seq);
+    const float inv = tgd::seq_inv_rho(red, n, eps_seq);
 #pragma unroll
     for (int e = 0; e < kNormPerThread; ++e) {
         const int64_t i = base + (int64_t)e * kNormThreads + tid;
-        if (i < n) s_norm[i] = x[e] / rho;
+        if (i < n) s_norm[i] = x[e] * inv;
     }
 }
 
-// Rows per scorer workgroup for a prompt of n tokens: 128 once that still
-// gives each of the 256 CUs a workgroup, else 64.
-inline int gate_rows_per_block(int64_t n) { return n >= (int64_t)256 * 128 ? 128 : 64; }
 
 template <int HD>
 int launch_gate_hd(const uint16_t* resid, const uint16_t* w1, const uint16_t* b1, const uint16_t* w2,
                    float b2, int64_t n, int d, float eps_row, float* s_out, float* block_ss, int64_t nb,
                    hipStream_t s) {
-    if (gate_rows_per_block(n) == 128)
+    if (tgi::gate_rows_per_block(n) == 128)
         hipLaunchKernelGGL((gate_mlp<HD, 128>), dim3((unsigned)nb), dim3(Cfg<HD, 128>::THREADS), 0, s, resid, w1, b1,
                            w2, b2, n, d, eps_row, s_out, block_ss);
     else
@@ -445,26 +436,34 @@ int launch_gate_score_noalloc(const uint16_t* resid, const uint16_t* w1, const u
     return launch_gate_score(resid, w1, b1, w2, b2, n, d, hd, eps_row, eps_seq, score_norm, score_raw, ws, stream);
 }
 
+int launch_gate_mlp(const uint16_t* resid, const uint16_t* w1, const uint16_t* b1, const uint16_t* w2, float b2,
+                    int64_t n, int d, int hd, float eps_row, float* s_raw, float* block_ss, void* stream) {
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t nb = gate_partials(n);
+    switch (hd) {
+        case 64: return launch_gate_hd<64>(resid, w1, b1, w2, b2, n, d, eps_row, s_raw, block_ss, nb, s);
+        case 128: return launch_gate_hd<128>(resid, w1, b1, w2, b2, n, d, eps_row, s_raw, block_ss, nb, s);
+        case 256: return launch_gate_hd<256>(resid, w1, b1, w2, b2, n, d, eps_row, s_raw, block_ss, nb, s);
+        default: return TG_EUNSUPPORTED;
+    }
+}
+
+int launch_gate_seqnorm(const float* s_raw, const float* block_ss, int64_t n, float eps_seq, float* score_norm,
+                        void* stream) {
+    const int64_t per = (int64_t)kNormThreads * kNormPerThread;
+    hipLaunchKernelGGL(gate_seqnorm, dim3((unsigned)((n + per - 1) / per)), dim3(kNormThreads), 0,
+                       (hipStream_t)stream, s_raw, block_ss, gate_partials(n), n, eps_seq, score_norm);
+    return hipGetLastError() == hipSuccess ? TG_OK : TG_EDEVICE;
+}
+
 int launch_gate_score(const uint16_t* resid, const uint16_t* w1, const uint16_t* b1,
                       const uint16_t* w2, float b2, int64_t n, int d, int hd, float eps_row,
                       float eps_seq, float* score_norm, float* score_raw, void* ws, void* stream) {
-    hipStream_t s = (hipStream_t)stream;
     float* block_ss = reinterpret_cast<float*>(ws);
     float* s_out = score_raw ? score_raw : score_norm;
-    const int bt = gate_rows_per_block(n);
-    const int64_t nb = (n + bt - 1) / bt;  // (at most gate_blocks(n) partial sums)
-    int rc;
-    switch (hd) {
-        case 64: rc = launch_gate_hd<64>(resid, w1, b1, w2, b2, n, d, eps_row, s_out, block_ss, nb, s); break;
-        case 128: rc = launch_gate_hd<128>(resid, w1, b1, w2, b2, n, d, eps_row, s_out, block_ss, nb, s); break;
-        case 256: rc = launch_gate_hd<256>(resid, w1, b1, w2, b2, n, d, eps_row, s_out, block_ss, nb, s); break;
-        default: return TG_EUNSUPPORTED;
-    }
+    const int rc = launch_gate_mlp(resid, w1, b1, w2, b2, n, d, hd, eps_row, s_out, block_ss, stream);
     if (rc != TG_OK) return rc;
-    const int64_t per = (int64_t)kNormThreads * kNormPerThread;
-    hipLaunchKernelGGL(gate_seqnorm, dim3((unsigned)((n + per - 1) / per)), dim3(kNormThreads), 0, s, s_out,
-                       block_ss, nb, n, eps_seq, score_norm);
-    return hipGetLastError() == hipSuccess ? TG_OK : TG_EDEVICE;
+    return launch_gate_seqnorm(s_out, block_ss, n, eps_seq, score_norm, stream);
 }
 
 }  // namespace tgi

@@ -120,12 +120,20 @@ __device__ __forceinline__ uint4 keys4_global(const float* __restrict__ score, c
 // t*KPT .. t*KPT+KPT-1 in registers for the whole selection (one read of the
 // scores), so no phase touches LDS for keys.  Same rounds and emit as the
 // long-prompt kernel below.
-template <int KPT>
-__global__ __launch_bounds__(kThreads) void select_topk_regs(const float* __restrict__ score,
+// With SEQNORM the scores read are the scorer's raw ones: the first 256
+// threads form 1 / rho from its partial sums in the fixed order every
+// sequence-norm kernel uses, each thread scales its scores, writes them to
+// s_norm (which may be `score` itself: a thread reads its tokens before it
+// writes them) and selects on them, so the result equals the sequence norm
+// followed by the plain select, bit for bit, in one launch.
+template <int KPT, bool SEQNORM>
+__global__ __launch_bounds__(kThreads) void select_topk_regs(const float* score,
                                                              const uint8_t* __restrict__ forced,
                                                              int64_t n64, int64_t n_forced, int64_t k64,
                                                              int32_t* __restrict__ kept,
-                                                             int32_t* __restrict__ dev_status) {
+                                                             int32_t* __restrict__ dev_status,
+                                                             const float* __restrict__ block_ss, int64_t nblocks,
+                                                             float eps_seq, float* s_norm) {
     static_assert(KPT % 4 == 0 && KPT <= 32, "keys per thread");
     constexpr int kBins = 2048;
     // first-round histogram in eight copies (lane % 8 picks one), so lanes of
@@ -144,11 +152,25 @@ __global__ __launch_bounds__(kThreads) void select_topk_regs(const float* __rest
     const int nvalid = base >= n ? 0 : (int)min((uint32_t)KPT, n - base);  // this thread's tokens
 
     // Scores and forced flags of this thread's tokens are loaded first; the
-    // histogram copies are cleared while the loads are in flight.
+    // histogram copies are cleared while the loads are in flight.  A thread
+    // whose tokens are all in range issues its loads back to back with no
+    // branch between them (one round trip); only the thread with the ragged
+    // tail takes the per-token path.
     float4 sc[KPT / 4];
     uint32_t fm[KPT / 4];
+    if (base + KPT <= n) {
 #pragma unroll
-    for (int v = 0; v < KPT / 4; ++v) {
+        for (int v = 0; v < KPT / 4; ++v) sc[v] = *reinterpret_cast<const float4*>(score + base + 4 * v);
+        if (forced) {
+#pragma unroll
+            for (int v = 0; v < KPT / 4; ++v) fm[v] = *reinterpret_cast<const uint32_t*>(forced + base + 4 * v);
+        } else {
+#pragma unroll
+            for (int v = 0; v < KPT / 4; ++v) fm[v] = 0u;
+        }
+    } else {
+#pragma unroll
+      for (int v = 0; v < KPT / 4; ++v) {
         const uint32_t i = base + 4 * v;
         if (i + 4 <= n) {
             sc[v] = *reinterpret_cast<const float4*>(score + i);
@@ -164,6 +186,7 @@ __global__ __launch_bounds__(kThreads) void select_topk_regs(const float* __rest
             sc[v] = float4{t4[0], t4[1], t4[2], t4[3]};
             fm[v] = f;
         }
+      }
     }
 
     auto pick_bin = [&](const uint32_t* hist, uint32_t remaining, int nbins) {
@@ -189,6 +212,26 @@ __global__ __launch_bounds__(kThreads) void select_topk_regs(const float* __rest
         }
         __syncthreads();
     };
+
+    if constexpr (SEQNORM) {
+        __shared__ double red[tgd::kSeqSumThreads / 64];
+        if (tid < tgd::kSeqSumThreads) tgd::seq_ss_partial(block_ss, nblocks, red);
+        __syncthreads();
+        const float inv = tgd::seq_inv_rho(red, n64, eps_seq);
+#pragma unroll
+        for (int v = 0; v < KPT / 4; ++v) {
+            sc[v].x *= inv, sc[v].y *= inv, sc[v].z *= inv, sc[v].w *= inv;
+            const uint32_t i = base + 4 * v;
+            if (i + 4 <= n) {
+                *reinterpret_cast<float4*>(s_norm + i) = sc[v];
+            } else {
+                const float t4[4] = {sc[v].x, sc[v].y, sc[v].z, sc[v].w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (i + q < n) s_norm[i + q] = t4[q];
+            }
+        }
+    }
 
     // Radix pass 1: forced count and the histogram of the top 11 bits.
     for (int b = tid * 4; b < kCopies * kBins; b += kThreads * 4)
@@ -604,13 +647,31 @@ __device__ __forceinline__ uint32_t block_excl_scan_m(uint32_t x, uint32_t* wsum
 
 // Keys of this thread's KPT consecutive tokens base .. base + KPT - 1
 // (kForcedMark for forced tokens; entries at or past n are unused).
+// A thread whose tokens are all in range issues its loads back to back with no
+// branch between them (one round trip); the ragged tail takes keys4_global.
 template <int KPT>
 __device__ __forceinline__ void chunk_keys(const float* __restrict__ score, const uint8_t* __restrict__ forced,
                                            uint32_t base, uint32_t n, uint32_t (&key)[KPT]) {
+    if (base + KPT <= n) {
+        float4 s4[KPT / 4];
+        uint32_t f[KPT / 4];
 #pragma unroll
-    for (int v = 0; v < KPT / 4; ++v) {
-        const uint4 k4 = keys4_global(score, forced, base + 4 * v, n);
-        key[4 * v] = k4.x, key[4 * v + 1] = k4.y, key[4 * v + 2] = k4.z, key[4 * v + 3] = k4.w;
+        for (int v = 0; v < KPT / 4; ++v) s4[v] = *reinterpret_cast<const float4*>(score + base + 4 * v);
+#pragma unroll
+        for (int v = 0; v < KPT / 4; ++v) f[v] = forced ? *reinterpret_cast<const uint32_t*>(forced + base + 4 * v) : 0u;
+#pragma unroll
+        for (int v = 0; v < KPT / 4; ++v) {
+            key[4 * v] = (f[v] & 0x000000ffu) ? kForcedMark : order_key(s4[v].x);
+            key[4 * v + 1] = (f[v] & 0x0000ff00u) ? kForcedMark : order_key(s4[v].y);
+            key[4 * v + 2] = (f[v] & 0x00ff0000u) ? kForcedMark : order_key(s4[v].z);
+            key[4 * v + 3] = (f[v] & 0xff000000u) ? kForcedMark : order_key(s4[v].w);
+        }
+    } else {
+#pragma unroll
+        for (int v = 0; v < KPT / 4; ++v) {
+            const uint4 k4 = keys4_global(score, forced, base + 4 * v, n);
+            key[4 * v] = k4.x, key[4 * v + 1] = k4.y, key[4 * v + 2] = k4.z, key[4 * v + 3] = k4.w;
+        }
     }
 }
 
@@ -1012,11 +1073,21 @@ int launch_select_topk(const float* score, const uint8_t* forced, int64_t n, int
         }
     }
     if (n <= kThreads * 16)
-        hipLaunchKernelGGL(select_topk_regs<16>, dim3(1), dim3(kThreads), 0, s, score, forced, n, n_forced, k,
-                           kept_idx, dev_status);
+        hipLaunchKernelGGL((select_topk_regs<16, false>), dim3(1), dim3(kThreads), 0, s, score, forced, n, n_forced,
+                           k, kept_idx, dev_status, nullptr, 0, 0.0f, nullptr);
     else
         hipLaunchKernelGGL(select_topk_block, dim3(1), dim3(kThreads), 0, s, score, forced, n, n_forced, k,
                            kept_idx, dev_status);
+    return hipGetLastError() == hipSuccess ? TG_OK : TG_EDEVICE;
+}
+
+int launch_seqnorm_select(const float* s_raw, const float* block_ss, int64_t n, float eps_seq,
+                          float* score_norm, const uint8_t* forced, int64_t n_forced, int64_t k,
+                          int32_t* kept_idx, int32_t* dev_status, void* stream) {
+    static_assert(kSelectOneWgMax == kThreads * 16, "one workgroup of 16 keys a thread");
+    if (n > kSelectOneWgMax) return TG_EUNSUPPORTED;
+    hipLaunchKernelGGL((select_topk_regs<16, true>), dim3(1), dim3(kThreads), 0, (hipStream_t)stream, s_raw, forced,
+                       n, n_forced, k, kept_idx, dev_status, block_ss, gate_partials(n), eps_seq, score_norm);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_EDEVICE;
 }
 

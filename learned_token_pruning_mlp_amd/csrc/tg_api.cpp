@@ -85,6 +85,35 @@ int tg_select_topk(const float* score, const uint8_t* forced, int64_t n, int64_t
     return tgi::launch_select_topk(score, forced, n, n_forced, k, kept_idx, dev_status, workspace, stream);
 }
 
+int tg_gate_score_select(const tg_bf16* resid, const tg_bf16* w1, const tg_bf16* b1, const tg_bf16* w2, float b2,
+                         int64_t n, int32_t d, int32_t hd, float eps_row, float eps_seq, const uint8_t* forced,
+                         int64_t n_forced, int64_t k, float* score_norm, float* score_raw, int32_t* kept_idx,
+                         int32_t* dev_status, void* workspace, size_t workspace_bytes, void* stream) {
+    // the checks of tg_gate_score and of tg_select_topk together
+    if (n < 1 || n > kMaxRows || k < 1 || k > n || n_forced < 0 || n_forced > k) return TG_EINVAL;
+    if (!forced && n_forced != 0) return TG_EINVAL;
+    if (!finite_nonneg(eps_row) || !finite_nonneg(eps_seq)) return TG_EINVAL;
+    if (d <= 0 || d % 64 != 0) return TG_EUNSUPPORTED;
+    if (hd != 64 && hd != 128 && hd != 256) return TG_EUNSUPPORTED;
+    if (!resid || !w1 || !w2 || !score_norm || !kept_idx) return TG_EINVAL;
+    if (!aligned(resid, 16) || !aligned(w1, 16) || !aligned(score_norm, 16) ||
+        (score_raw && !aligned(score_raw, 4)) || (b1 && !aligned(b1, 2)) || !aligned(w2, 2) ||
+        (forced && !aligned(forced, 4)) || !aligned(kept_idx, 4) || (dev_status && !aligned(dev_status, 4)))
+        return TG_EALIGN;
+    if (!workspace || workspace_bytes < tgi::workspace_bytes(n)) return TG_EWORKSPACE;
+    if (!aligned(workspace, 16)) return TG_EALIGN;
+    float* block_ss = static_cast<float*>(workspace);
+    float* s_raw = score_raw ? score_raw : score_norm;
+    int rc = tgi::launch_gate_mlp(resid, w1, b1, w2, b2, n, d, hd, eps_row, s_raw, block_ss, stream);
+    if (rc != TG_OK) return rc;
+    if (n <= tgi::kSelectOneWgMax)
+        return tgi::launch_seqnorm_select(s_raw, block_ss, n, eps_seq, score_norm, forced, n_forced, k, kept_idx,
+                                          dev_status, stream);
+    rc = tgi::launch_gate_seqnorm(s_raw, block_ss, n, eps_seq, score_norm, stream);
+    if (rc != TG_OK) return rc;
+    return tgi::launch_select_topk(score_norm, forced, n, n_forced, k, kept_idx, dev_status, workspace, stream);
+}
+
 int tg_compact(const int32_t* kept_idx, int64_t k, int64_t n, const tg_bf16* resid, tg_bf16* resid_out,
                int32_t d, const int32_t* pos, int32_t* pos_out, const float* score, float* score_out,
                const tg_gather* extra, int32_t n_extra, void* stream) {

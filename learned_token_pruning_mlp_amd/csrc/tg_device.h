@@ -64,4 +64,27 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+// Sequence RMSNorm of the gate scores: 1 / rho, rho = sqrt(sum s^2 / n + eps),
+// from the scorer's per-workgroup partial sums of squared raw scores, in one
+// fixed order, so that every kernel that forms it gets the same value:
+// threads 0 .. 255 of a workgroup each add every 256-th partial in fp64
+// (seq_ss_partial), the four waves reduce by an xor butterfly whose lane-0
+// value is kept, and the four wave sums are added in wave order
+// (seq_inv_rho, after a barrier).  The scores are then s * (1 / rho).
+constexpr int kSeqSumThreads = 256;
+__device__ __forceinline__ void seq_ss_partial(const float* block_ss, int64_t nblocks, double* red) {
+    const int tid = threadIdx.x;  // < kSeqSumThreads
+    double acc = 0.0;
+    for (int64_t b = tid; b < nblocks; b += kSeqSumThreads) acc += (double)block_ss[b];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if ((tid & 63) == 0) red[tid >> 6] = acc;
+}
+__device__ __forceinline__ float seq_inv_rho(const double* red, int64_t n, float eps) {
+    double tot = 0.0;
+#pragma unroll
+    for (int w = 0; w < kSeqSumThreads / 64; ++w) tot += red[w];
+    return (float)(1.0 / sqrt(tot / (double)n + (double)eps));
+}
+
 }  // namespace tgd

@@ -19,6 +19,11 @@ constexpr int kGateRowsPerBlock = 64;
 //   [0, gate_bytes)        per-block sums of squared raw scores (fp32)
 //   [select_off, ...)      select: histograms, counters, per-chunk counts
 inline int64_t gate_blocks(int64_t n) { return (n + kGateRowsPerBlock - 1) / kGateRowsPerBlock; }
+// Rows per scorer workgroup actually used for a prompt of n tokens (128 once
+// that still gives each of the 256 CUs a workgroup, else 64), and the number
+// of per-workgroup partial sums the scorer writes (at most gate_blocks(n)).
+inline int gate_rows_per_block(int64_t n) { return n >= (int64_t)256 * 128 ? 128 : 64; }
+inline int64_t gate_partials(int64_t n) { return (n + gate_rows_per_block(n) - 1) / gate_rows_per_block(n); }
 inline size_t gate_bytes(int64_t n) { return align_up(sizeof(float) * (size_t)(gate_blocks(n) > 0 ? gate_blocks(n) : 1)); }
 
 // The many-workgroup select (prompts of kSelectMultiMin tokens and more):
@@ -101,6 +106,24 @@ int launch_gate_score_noalloc(const uint16_t* resid, const uint16_t* w1, const u
 int launch_gate_score(const uint16_t* resid, const uint16_t* w1, const uint16_t* b1,
                       const uint16_t* w2, float b2, int64_t n, int d, int hd, float eps_row,
                       float eps_seq, float* score_norm, float* score_raw, void* ws, void* stream);
+
+// The scorer's two launches on their own: the MLP (raw scores and the
+// per-workgroup partial sums of their squares, gate_partials(n) of them) and
+// the sequence norm.
+int launch_gate_mlp(const uint16_t* resid, const uint16_t* w1, const uint16_t* b1, const uint16_t* w2, float b2,
+                    int64_t n, int d, int hd, float eps_row, float* s_raw, float* block_ss, void* stream);
+int launch_gate_seqnorm(const float* s_raw, const float* block_ss, int64_t n, float eps_seq, float* score_norm,
+                        void* stream);
+
+// Largest prompt whose select runs in one workgroup; up to it the sequence
+// norm can run inside that workgroup (tg_gate_score_select).
+constexpr int64_t kSelectOneWgMax = 16384;
+
+// Sequence norm and select in one launch (n <= kSelectOneWgMax): from the raw
+// scores and their partial sums to the normalised scores and the kept set.
+int launch_seqnorm_select(const float* s_raw, const float* block_ss, int64_t n, float eps_seq,
+                          float* score_norm, const uint8_t* forced, int64_t n_forced, int64_t k,
+                          int32_t* kept_idx, int32_t* dev_status, void* stream);
 
 int launch_select_topk(const float* score, const uint8_t* forced, int64_t n, int64_t n_forced,
                        int64_t k, int32_t* kept_idx, int32_t* dev_status, void* ws, void* stream);

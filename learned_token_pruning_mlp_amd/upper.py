@@ -190,9 +190,9 @@ class Prefill:
         gl = self.gl
         attention_block(self.blas, s, self.W[gl], src, self.arange, self.zeros_n, self.zero_gains, 0.0,
                         self.buf, self.h2_gate, self.k_low[gl], self.v_low[gl])
-        tg.tg_gate_score(self.h2_gate, self.w1, None, self.w2, 0.0, s.eps, s.eps, self.s_norm, None, self.ws)
         kept = torch.empty(k, dtype=torch.int32, device=dev)
-        tg.tg_select_topk(self.s_norm, forced, n_forced, k, kept, None, self.ws)
+        tg.tg_gate_score_select(self.h2_gate, self.w1, None, self.w2, 0.0, s.eps, s.eps, forced, n_forced, k,
+                                self.s_norm, None, kept, None, self.ws)
         bf = dict(dtype=torch.bfloat16, device=dev)
         h2k = torch.empty(k, s.d, **bf)
         pos_k = torch.empty(k, dtype=torch.int32, device=dev)

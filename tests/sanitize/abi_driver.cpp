@@ -48,6 +48,17 @@ int main() {
     EXPECT(tg_select_topk(F, U, 200000, 5000, 4000, I, nullptr, W, wsl, nullptr), TG_EINVAL);
     EXPECT(tg_select_topk(F, nullptr, 200000, 10, 4000, I, nullptr, W, wsl, nullptr), TG_EINVAL);
     EXPECT(tg_select_topk(F, U, 200000, 10, 4000, I, nullptr, W, wsl - 1, nullptr), TG_EWORKSPACE);
+    // scorer and select in one call
+    EXPECT(tg_gate_score_select(A, A, nullptr, A, 0.f, 200000, 256, 64, 1e-6f, 1e-6f, U, 10, 4000, F, nullptr, I,
+                                nullptr, W, wsl, nullptr), R);
+    EXPECT(tg_gate_score_select(A, A, nullptr, A, 0.f, 200000, 256, 64, 1e-6f, 1e-6f, U, 10, 0, F, nullptr, I,
+                                nullptr, W, wsl, nullptr), TG_EINVAL);
+    EXPECT(tg_gate_score_select(A, A, nullptr, A, 0.f, 200000, 200, 64, 1e-6f, 1e-6f, U, 10, 4000, F, nullptr, I,
+                                nullptr, W, wsl, nullptr), TG_EUNSUPPORTED);
+    EXPECT(tg_gate_score_select(A, A, nullptr, A, 0.f, 200000, 256, 64, 1e-6f, 1e-6f, U, 10, 4000, F + 1, nullptr, I,
+                                nullptr, W, wsl, nullptr), TG_EALIGN);
+    EXPECT(tg_gate_score_select(A, A, nullptr, A, 0.f, 200000, 256, 64, 1e-6f, 1e-6f, U, 10, 4000, F, nullptr, I,
+                                nullptr, W, wsl - 1, nullptr), TG_EWORKSPACE);
     // compaction
     tg_gather g{A, A, 64, 64, 64};
     EXPECT(tg_compact(I, 64, 512, A, A, 256, nullptr, I, F, F, &g, 1, nullptr), R);

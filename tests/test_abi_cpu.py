@@ -100,6 +100,35 @@ def test_select_checks(lib):
     assert _sel(lib, ws_bytes=16) == E.TG_EWORKSPACE
 
 
+def _gsel(lib, **kw):
+    a = dict(resid=A, w1=A, b1=None, w2=A, b2=0.0, n=1000, d=256, hd=64, eps_row=1e-6, eps_seq=1e-6, forced=A,
+             nf=10, k=100, score_norm=A, score_raw=None, kept=A, st=None, ws=A, ws_bytes=WS, stream=None)
+    a.update(kw)
+    return lib.tg_gate_score_select(a["resid"], a["w1"], a["b1"], a["w2"], a["b2"], a["n"], a["d"], a["hd"],
+                                    a["eps_row"], a["eps_seq"], a["forced"], a["nf"], a["k"], a["score_norm"],
+                                    a["score_raw"], a["kept"], a["st"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_gate_score_select_checks(lib):
+    """Both calls' checks: the scorer's shapes and the select's budget."""
+    E = binding
+    assert _gsel(lib, n=0, k=0) == E.TG_EINVAL  # the select needs a token
+    assert _gsel(lib, k=0) == E.TG_EINVAL
+    assert _gsel(lib, k=1001) == E.TG_EINVAL
+    assert _gsel(lib, nf=101) == E.TG_EINVAL
+    assert _gsel(lib, forced=None) == E.TG_EINVAL
+    assert _gsel(lib, d=200) == E.TG_EUNSUPPORTED
+    assert _gsel(lib, hd=96) == E.TG_EUNSUPPORTED
+    assert _gsel(lib, eps_seq=-1.0) == E.TG_EINVAL
+    assert _gsel(lib, resid=None) == E.TG_EINVAL
+    assert _gsel(lib, kept=None) == E.TG_EINVAL
+    assert _gsel(lib, score_norm=A + 4) == E.TG_EALIGN  # the select reads it in 16-byte pieces
+    assert _gsel(lib, w1=M) == E.TG_EALIGN
+    assert _gsel(lib, forced=A + 2) == E.TG_EALIGN
+    assert _gsel(lib, ws=None) == E.TG_EWORKSPACE
+    assert _gsel(lib, ws_bytes=binding.tg_workspace_bytes(1000) - 1) == E.TG_EWORKSPACE
+
+
 def _cmp(lib, **kw):
     a = dict(idx=A, k=64, n=512, resid=A, resid_out=A, d=256, pos=None, pos_out=A, score=A, score_out=A,
              extra=None, n_extra=0, stream=None)

@@ -1,0 +1,75 @@
+"""tg_gate_score_select against its two calls, tg_gate_score then
+tg_select_topk on the normalised scores: the same normalised and raw scores,
+kept indices and status word, bit for bit.  Up to 16384 tokens the sequence
+norm runs inside the one-workgroup select; longer prompts take the two calls'
+kernels.  (The two calls themselves are pinned to the oracle in
+test_gpu_steps.py and test_gpu_workloads.py.)"""
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as gu
+from learned_token_pruning_mlp_amd import binding as tg
+from learned_token_pruning_mlp_amd import synth
+from oracle import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(n, d, hd, f, k, seed, layout, with_raw, with_forced, fused):
+    shp = synth.GateShape(n=n, d=d, hd=hd, n_forced=f, k=k, hq=1, hkv=1, head_dim=64, forced_layout=layout)
+    inp = synth.gate_inputs(shp, seed, with_b1=True)
+    resid, w1, b1, w2 = gu.bf16(inp.resid), gu.bf16(inp.w1), gu.bf16(inp.b1), gu.bf16(inp.w2)
+    forced = gu.u8(inp.forced) if with_forced else None
+    nf = int(inp.forced.sum()) if with_forced else 0
+    s_norm = torch.full((n,), float("nan"), dtype=torch.float32, device=gu.dev())
+    s_raw = torch.full((n,), float("nan"), dtype=torch.float32, device=gu.dev()) if with_raw else None
+    kept = torch.full((k,), -1, dtype=torch.int32, device=gu.dev())
+    st = torch.full((1,), -7, dtype=torch.int32, device=gu.dev())
+    ws = tg.workspace(n)
+    if fused:
+        tg.tg_gate_score_select(resid, w1, b1, w2, 0.25, 1e-6, 1e-6, forced, nf, k, s_norm, s_raw, kept, st, ws)
+    else:
+        tg.tg_gate_score(resid, w1, b1, w2, 0.25, 1e-6, 1e-6, s_norm, s_raw, ws)
+        tg.tg_select_topk(s_norm, forced, nf, k, kept, st, ws)
+    torch.cuda.synchronize()
+    return (gu.host(s_norm), None if s_raw is None else gu.host(s_raw), gu.host(kept), int(gu.host(st)[0]),
+            inp)
+
+
+@pytest.mark.parametrize("n,d,hd,f,k,layout,with_raw,with_forced", [
+    (512, 256, 64, 32, 128, "tail", True, True),
+    (1000, 256, 64, 50, 300, "scatter_tail", False, True),
+    (333, 2048, 256, 0, 50, "tail", True, False),
+    (1, 128, 64, 0, 1, "tail", False, False),
+    (16384, 2048, 256, 64, 2048, "tail", False, True),
+    (16383, 512, 128, 64, 4000, "tail", True, True),
+    (16385, 512, 128, 64, 2048, "tail", True, True),
+])
+def test_gate_score_select_matches_two_calls(n, d, hd, f, k, layout, with_raw, with_forced):
+    gu.say(f"gate_score_select n={n} d={d} hd={hd} k={k}")
+    a = _run(n, d, hd, f, k, 21, layout, with_raw, with_forced, fused=True)
+    b = _run(n, d, hd, f, k, 21, layout, with_raw, with_forced, fused=False)
+    assert np.array_equal(a[0], b[0])  # normalised scores
+    if with_raw:
+        assert np.array_equal(a[1], b[1])
+    assert np.array_equal(a[2], b[2])  # kept indices
+    assert a[3] == b[3] == 0
+    # and the kept set is the oracle's select over these scores
+    forced = a[4].forced if with_forced else np.zeros(n, np.uint8)
+    assert np.array_equal(a[2], oracle.select_topk(a[0], forced, k))
+
+
+def test_gate_score_select_status_word():
+    """A forced count that disagrees with the mask is reported, as by the select."""
+    n, d, hd, f, k = 2000, 256, 64, 40, 200
+    gu.say("gate_score_select status word")
+    shp = synth.GateShape(n=n, d=d, hd=hd, n_forced=f, k=k, hq=1, hkv=1, head_dim=64)
+    inp = synth.gate_inputs(shp, 3)
+    s_norm = torch.empty(n, dtype=torch.float32, device=gu.dev())
+    kept = torch.empty(k, dtype=torch.int32, device=gu.dev())
+    st = torch.full((1,), -7, dtype=torch.int32, device=gu.dev())
+    tg.tg_gate_score_select(gu.bf16(inp.resid), gu.bf16(inp.w1), None, gu.bf16(inp.w2), 0.0, 1e-6, 1e-6,
+                            gu.u8(inp.forced), f - 1, k, s_norm, None, kept, st, tg.workspace(n))
+    torch.cuda.synchronize()
+    assert int(gu.host(st)[0]) == tg.TG_STATUS_FORCED_MISMATCH
