@@ -362,21 +362,35 @@ __global__ __launch_bounds__(kNormThreads) void gate_seqnorm(const float* s_raw,
     static_assert(kNormThreads == tgd::kSeqSumThreads, "every thread takes part in the fixed-order sum");
     __shared__ double red[kNormThreads / 64];
     const int tid = threadIdx.x;
-    // this thread's raw scores first: their loads overlap the reduction
+    // this thread's raw scores first: their loads overlap the reduction.  A
+    // workgroup whose slice is all in range loads and stores with no branch
+    // between the accesses (a branch per access made the compiler wait for
+    // each store before the next); only the last one takes the guarded path.
     const int64_t base = (int64_t)blockIdx.x * kNormThreads * kNormPerThread;
+    const bool full = base + kNormThreads * kNormPerThread <= n;
     float x[kNormPerThread];
+    if (full) {
 #pragma unroll
-    for (int e = 0; e < kNormPerThread; ++e) {
-        const int64_t i = base + (int64_t)e * kNormThreads + tid;
-        x[e] = i < n ? s_raw[i] : 0.0f;
+        for (int e = 0; e < kNormPerThread; ++e) x[e] = s_raw[base + e * kNormThreads + tid];
+    } else {
+#pragma unroll
+        for (int e = 0; e < kNormPerThread; ++e) {
+            const int64_t i = base + (int64_t)e * kNormThreads + tid;
+            x[e] = i < n ? s_raw[i] : 0.0f;
+        }
     }
     tgd::seq_ss_partial(block_ss, nblocks, red);
     __syncthreads();
     const float inv = tgd::seq_inv_rho(red, n, eps_seq);
+    if (full) {
 #pragma unroll
-    for (int e = 0; e < kNormPerThread; ++e) {
-        const int64_t i = base + (int64_t)e * kNormThreads + tid;
-        if (i < n) s_norm[i] = x[e] * inv;
+        for (int e = 0; e < kNormPerThread; ++e) s_norm[base + e * kNormThreads + tid] = x[e] * inv;
+    } else {
+#pragma unroll
+        for (int e = 0; e < kNormPerThread; ++e) {
+            const int64_t i = base + (int64_t)e * kNormThreads + tid;
+            if (i < n) s_norm[i] = x[e] * inv;
+        }
     }
 }
 

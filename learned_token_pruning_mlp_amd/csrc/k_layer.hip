@@ -46,12 +46,28 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_rows(const uint16_t* x,
     const int64_t row = (int64_t)blockIdx.x * RPB + tid / LANES;
     const bool ok = row < rows;
     const int pieces = dim / 8;
-    u32x4 v[PER];
+    // A lane whose pieces are all in range loads them (and its weights) with
+    // no branch between the accesses, so they go out together; the guarded
+    // path (short rows, rows past the end) waits per access.
+    const bool all = ok && (PER - 1) * LANES + sub < pieces;
+    u32x4 v[PER], wv[PER];
+    if (all) {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) v[p] = *reinterpret_cast<const u32x4*>(x + row * dim + 8 * (p * LANES + sub));
+#pragma unroll
+        for (int p = 0; p < PER; ++p) wv[p] = *reinterpret_cast<const u32x4*>(w + 8 * (p * LANES + sub));
+    } else {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int c = p * LANES + sub;
+            const bool in = ok && c < pieces;
+            v[p] = in ? *reinterpret_cast<const u32x4*>(x + row * dim + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+            wv[p] = in ? *reinterpret_cast<const u32x4*>(w + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
     float ss = 0.0f;
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-        const int c = p * LANES + sub;
-        v[p] = (ok && c < pieces) ? *reinterpret_cast<const u32x4*>(x + row * dim + 8 * c) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float a = lo16(v[p][e]), b = hi16(v[p][e]);
@@ -67,11 +83,10 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_rows(const uint16_t* x,
     for (int p = 0; p < PER; ++p) {
         const int c = p * LANES + sub;
         if (c >= pieces) continue;
-        const u32x4 wv = *reinterpret_cast<const u32x4*>(w + 8 * c);
         u32x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            o[e] = tgd::cvt_pk_bf16(lo16(v[p][e]) * r * lo16(wv[e]), hi16(v[p][e]) * r * hi16(wv[e]));
+            o[e] = tgd::cvt_pk_bf16(lo16(v[p][e]) * r * lo16(wv[p][e]), hi16(v[p][e]) * r * hi16(wv[p][e]));
         *reinterpret_cast<u32x4*>(y + row * dim + 8 * c) = o;
     }
 }
