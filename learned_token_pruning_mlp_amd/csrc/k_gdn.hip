@@ -133,9 +133,20 @@ __global__ __launch_bounds__(64 * kWaves) void gdn_scan(const uint16_t* __restri
     };
     auto step = [&](int64_t ch, const TG_LDS uint8_t* __restrict__ cb, TG_LDS uint8_t* __restrict__ nb,
                     int64_t nch) {
-        TG_WAIT_VMCNT(0);  // this wave's share of the chunk is in LDS (and its stores are done)
-        __syncthreads();   // ... and every wave's; the other stage is free again
+        // This wave's share of the chunk is in LDS.  Loads complete in issue
+        // order and the one memory operation issued after them is the
+        // previous chunk's output store, which may stay in flight.
+        if (ch == 0) {
+            TG_WAIT_VMCNT(0);
+        } else {
+            TG_WAIT_VMCNT(1);
+        }
+        // ... and every wave's; the other stage is free again.  A bare barrier
+        // (with a compiler memory fence, so no LDS read moves above it): a
+        // workgroup fence here would also wait for the output store.
+        asm volatile("s_barrier" ::: "memory");
         if (ch + 1 < nch) issue(ch + 1, nb);
+        asm volatile("" ::: "memory");  // the chunk's output store stays behind these loads
         const int64_t t0 = ch * kChunk;
         const int tn = n - t0 < kChunk ? (int)(n - t0) : kChunk;
         const TG_LDS uint16_t* kc = (const TG_LDS uint16_t*)cb;
