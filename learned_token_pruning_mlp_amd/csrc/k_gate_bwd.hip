@@ -26,6 +26,8 @@
 // No float atomics anywhere (the rocBLAS handle has atomics disabled).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "tg_device.h"
 #include "tg_internal.h"
 
@@ -97,14 +99,13 @@ __global__ __launch_bounds__(1024) void gbw_scalars(const float* __restrict__ s,
 
 // kRowsPerWave rows per wave.  Lane L holds hidden units L*UPL .. +UPL-1 and
 // the 16-byte pieces L, L+64, ... of the residual row.
-template <int HD>
+template <int HD, int PPL>
 __global__ __launch_bounds__(64 * kWaves) void gbw_rows(
     const uint16_t* __restrict__ h, const float* __restrict__ Z, const uint16_t* __restrict__ b1,
     const uint16_t* __restrict__ w2, const float* __restrict__ s, const float* __restrict__ dsh,
     const float* __restrict__ sc, int64_t n, int d, float eps_row, uint16_t* __restrict__ dz,
     float* __restrict__ dh, float* __restrict__ dw2p, float* __restrict__ db1p, float* __restrict__ db2p) {
-    constexpr int UPL = HD / 64;
-    constexpr int PPL = 8;  // pieces per lane at most (d <= 4096)
+    constexpr int UPL = HD / 64;  // (PPL: 16-byte pieces of a row per lane, 64-lane passes; d <= 512 * PPL)
     const int lane = threadIdx.x & 63;
     const int64_t wg = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
     const int64_t row0 = wg * kRowsPerWave;
@@ -121,39 +122,63 @@ __global__ __launch_bounds__(64 * kWaves) void gbw_rows(
     }
     float ab2 = 0.0f;
     const int64_t rows = n - row0 < kRowsPerWave ? n - row0 : kRowsPerWave;
-    for (int rr = 0; rr < (int)rows; ++rr) {
-        const int64_t i = row0 + rr;
+    // A row's operands: its residual pieces, Z row, dshat and raw score.  The
+    // next row's are loaded (its index clamped to the wave's last row, so the
+    // loads are unconditional) before this row's outputs are stored; loads
+    // and stores complete in issue order, so waiting for them never waits for
+    // the previous row's stores.  When the pieces fill PPL 64-lane passes
+    // exactly, the piece loads are unconditional too.
+    struct RowIn {
         u32x4 hv[PPL];
+        float zv[UPL];
+        float dsh, s;
+    };
+    // the row loop, with FULL = (the pieces fill the PPL passes exactly) fixed
+    auto run = [&](auto FULL) {
+    constexpr bool full = decltype(FULL)::value;
+    auto load_row = [&](int64_t i, RowIn& in) {
+        if constexpr (full) {
+#pragma unroll
+            for (int q = 0; q < PPL; ++q) in.hv[q] = *reinterpret_cast<const u32x4*>(h + i * d + 8 * (lane + 64 * q));
+        } else {
+#pragma unroll
+            for (int q = 0; q < PPL; ++q) {
+                const int p = lane + 64 * q;
+                in.hv[q] = p < pieces ? *reinterpret_cast<const u32x4*>(h + i * d + 8 * p) : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UPL; ++u) in.zv[u] = Z[i * HD + lane * UPL + u];
+        in.dsh = dsh[i];
+        in.s = s[i];
+    };
+    auto row_step = [&](int rr, const RowIn& cur, RowIn& nxt) {
+        const int64_t i = row0 + rr;
+        load_row(row0 + (rr + 1 < rows ? rr + 1 : rr), nxt);
         float ss = 0.0f;
 #pragma unroll
         for (int q = 0; q < PPL; ++q) {
-            const int p = lane + 64 * q;
-            hv[q] = u32x4{0u, 0u, 0u, 0u};
-            if (p < pieces) hv[q] = *reinterpret_cast<const u32x4*>(h + i * d + 8 * p);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float lo = tgd::bf16lo(hv[q][e]), hi = tgd::bf16hi(hv[q][e]);
+                const float lo = tgd::bf16lo(cur.hv[q][e]), hi = tgd::bf16hi(cur.hv[q][e]);
                 ss = fmaf(lo, lo, ss);
                 ss = fmaf(hi, hi, ss);
             }
         }
         ss = tgd::wave_sum(ss);
         const float r = 1.0f / sqrtf(ss / (float)d + eps_row);
-        float zv[UPL];
-#pragma unroll
-        for (int u = 0; u < UPL; ++u) zv[u] = Z[i * HD + lane * UPL + u];
-        const float dsi = dsh[i] * inv_rho - s[i] * coef;
+        const float dsi = cur.dsh * inv_rho - cur.s * coef;
         float dr = 0.0f;
         float dzv[UPL];
 #pragma unroll
         for (int u = 0; u < UPL; ++u) {
-            const float a = fmaf(r, zv[u], b1v[u]);
+            const float a = fmaf(r, cur.zv[u], b1v[u]);
             const float Phi = 0.5f * (1.0f + erf_as(a * kInvSqrt2));
             const float phi = kInvSqrt2Pi * __builtin_amdgcn_exp2f(-0.5f * a * a * kLog2e);
             const float da = dsi * w2v[u] * fmaf(a, phi, Phi);
             aw2[u] = fmaf(dsi, a * Phi, aw2[u]);
             ab1[u] += da;
-            dr = fmaf(da, zv[u], dr);
+            dr = fmaf(da, cur.zv[u], dr);
             dzv[u] = r * da;
         }
         if constexpr (UPL == 4) {
@@ -169,16 +194,27 @@ __global__ __launch_bounds__(64 * kWaves) void gbw_rows(
 #pragma unroll
         for (int q = 0; q < PPL; ++q) {
             const int p = lane + 64 * q;
-            if (p < pieces) {
+            if (full || p < pieces) {
                 float4* o = reinterpret_cast<float4*>(dh + i * d + 8 * p);
-                o[0] = float4{e * tgd::bf16lo(hv[q][0]), e * tgd::bf16hi(hv[q][0]), e * tgd::bf16lo(hv[q][1]),
-                              e * tgd::bf16hi(hv[q][1])};
-                o[1] = float4{e * tgd::bf16lo(hv[q][2]), e * tgd::bf16hi(hv[q][2]), e * tgd::bf16lo(hv[q][3]),
-                              e * tgd::bf16hi(hv[q][3])};
+                o[0] = float4{e * tgd::bf16lo(cur.hv[q][0]), e * tgd::bf16hi(cur.hv[q][0]),
+                              e * tgd::bf16lo(cur.hv[q][1]), e * tgd::bf16hi(cur.hv[q][1])};
+                o[1] = float4{e * tgd::bf16lo(cur.hv[q][2]), e * tgd::bf16hi(cur.hv[q][2]),
+                              e * tgd::bf16lo(cur.hv[q][3]), e * tgd::bf16hi(cur.hv[q][3])};
             }
         }
         ab2 += dsi;
+    };
+    RowIn ra, rb;
+    load_row(row0, ra);
+    for (int rr = 0; rr < (int)rows; rr += 2) {
+        row_step(rr, ra, rb);
+        if (rr + 1 < (int)rows) row_step(rr + 1, rb, ra);
     }
+    };
+    if (pieces == PPL * 64)
+        run(std::true_type{});
+    else
+        run(std::false_type{});
 #pragma unroll
     for (int u = 0; u < UPL; ++u) {
         dw2p[wg * HD + lane * UPL + u] = aw2[u];
@@ -236,8 +272,21 @@ template <int HD>
 int launch_rows(const uint16_t* resid, const uint16_t* b1, const uint16_t* w2, const float* s_raw, int64_t n, int d,
                 float eps_row, const tgi::GateBwdWs& ws, float* dresid, hipStream_t st) {
     const int64_t nw = tgi::gate_bwd_waves(n);
-    hipLaunchKernelGGL(gbw_rows<HD>, dim3((unsigned)((nw + kWaves - 1) / kWaves)), dim3(64 * kWaves), 0, st, resid,
-                       ws.z, b1, w2, s_raw, ws.dsh, ws.sc, n, d, eps_row, ws.dz, dresid, ws.dw2p, ws.db1p, ws.db2p);
+    const dim3 grid((unsigned)((nw + kWaves - 1) / kWaves)), block(64 * kWaves);
+    // 16-byte pieces of a row per lane: d <= 512 * PPL (the C ABI takes d <= 4096)
+    const int pieces = d / 8, ppl = (pieces + 63) / 64;
+    if (ppl <= 1)
+        hipLaunchKernelGGL((gbw_rows<HD, 1>), grid, block, 0, st, resid, ws.z, b1, w2, s_raw, ws.dsh, ws.sc, n, d,
+                           eps_row, ws.dz, dresid, ws.dw2p, ws.db1p, ws.db2p);
+    else if (ppl <= 2)
+        hipLaunchKernelGGL((gbw_rows<HD, 2>), grid, block, 0, st, resid, ws.z, b1, w2, s_raw, ws.dsh, ws.sc, n, d,
+                           eps_row, ws.dz, dresid, ws.dw2p, ws.db1p, ws.db2p);
+    else if (ppl <= 4)
+        hipLaunchKernelGGL((gbw_rows<HD, 4>), grid, block, 0, st, resid, ws.z, b1, w2, s_raw, ws.dsh, ws.sc, n, d,
+                           eps_row, ws.dz, dresid, ws.dw2p, ws.db1p, ws.db2p);
+    else
+        hipLaunchKernelGGL((gbw_rows<HD, 8>), grid, block, 0, st, resid, ws.z, b1, w2, s_raw, ws.dsh, ws.sc, n, d,
+                           eps_row, ws.dz, dresid, ws.dw2p, ws.db1p, ws.db2p);
     return TG_OK;
 }
 
