@@ -149,9 +149,11 @@ int tg_select_topk(const float* score, const uint8_t* forced, int64_t n, int64_t
  * tg_gate_score_select -- tg_gate_score, then tg_select_topk on its
  * normalised scores, in one call [P1 gate][P2 method][P3 how][P5 Fig 1(a)(b)]:
  * the same score_norm, score_raw, kept_idx and dev_status as the two calls,
- * bit for bit.  Up to 16384 tokens the sequence norm runs inside the
- * one-workgroup select (one launch fewer); longer prompts take the two
- * calls' kernels.  Arguments: those of tg_gate_score and tg_select_topk
+ * bit for bit.  Up to 524288 tokens the sequence norm runs inside the
+ * select's first launch (one launch fewer: the one-workgroup select up to
+ * 16384 tokens, the first of the many-workgroup select's three launches
+ * above); longer prompts take the two calls' kernels.  Arguments: those of
+ * tg_gate_score and tg_select_topk
  * (score_norm must also be 16-byte aligned); checks: both calls' checks
  * (n >= 1).  Workspace: tg_workspace_bytes(n).
  */

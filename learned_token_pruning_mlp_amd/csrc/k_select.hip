@@ -675,6 +675,34 @@ __device__ __forceinline__ void chunk_keys(const float* __restrict__ score, cons
     }
 }
 
+// Scores and forced-flag words of this thread's KPT consecutive tokens, for
+// the fused sequence norm (the keys are formed after the scaling); entries
+// at or past n read as 0.  Same load pattern as chunk_keys.
+template <int KPT>
+__device__ __forceinline__ void chunk_vals(const float* score, const uint8_t* __restrict__ forced, uint32_t base,
+                                           uint32_t n, float4 (&sc)[KPT / 4], uint32_t (&fm)[KPT / 4]) {
+    if (base + KPT <= n) {
+#pragma unroll
+        for (int v = 0; v < KPT / 4; ++v) sc[v] = *reinterpret_cast<const float4*>(score + base + 4 * v);
+#pragma unroll
+        for (int v = 0; v < KPT / 4; ++v) fm[v] = forced ? *reinterpret_cast<const uint32_t*>(forced + base + 4 * v) : 0u;
+    } else {
+#pragma unroll
+        for (int v = 0; v < KPT / 4; ++v) {
+            float t4[4];
+            uint32_t f = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t i = base + 4 * v + q;
+                t4[q] = i < n ? score[i] : 0.0f;
+                if (forced && i < n && forced[i]) f |= 1u << (8 * q);
+            }
+            sc[v] = float4{t4[0], t4[1], t4[2], t4[3]};
+            fm[v] = f;
+        }
+    }
+}
+
 // The bin of `hist` (nbins, counted from the top) holding the remaining-th
 // largest key; one wave, two wave scans.  Sets ctl[0] = bin, ctl[1] = rank
 // inside it; ends with a barrier.
@@ -722,9 +750,18 @@ __device__ __forceinline__ void hist_add_wave(uint32_t* hist, uint32_t bin, bool
     }
 }
 
-template <int KPT>
-__global__ __launch_bounds__(kMT) void selm_hist(const float* __restrict__ score, const uint8_t* __restrict__ forced,
-                                                 uint32_t n, tgi::SelectWs w) {
+// With SEQNORM the scores read are the scorer's raw ones: every workgroup
+// forms 1 / rho from all the partial sums in the fixed order of every
+// sequence-norm kernel (so all get the same value), scales its chunk's scores,
+// writes them to s_norm (which may be `score` itself: a thread reads its
+// tokens before it writes them, and no other workgroup reads them in this
+// launch) and histograms their keys.  The two later launches read s_norm, so
+// the result equals the sequence norm followed by the plain select, bit for
+// bit, with one launch fewer.
+template <int KPT, bool SEQNORM>
+__global__ __launch_bounds__(kMT) void selm_hist(const float* score, const uint8_t* __restrict__ forced,
+                                                 uint32_t n, tgi::SelectWs w, const float* __restrict__ block_ss,
+                                                 int64_t nblocks, float eps_seq, float* s_norm) {
     constexpr int kCopies = 4;  // lane % 4 picks a copy: fewer lanes of a wave on one word
     __shared__ __attribute__((aligned(16))) uint32_t h[kCopies][2048];
     __shared__ uint32_t fw[kMWaves];
@@ -732,11 +769,46 @@ __global__ __launch_bounds__(kMT) void selm_hist(const float* __restrict__ score
     const uint32_t c = blockIdx.x;
     const uint32_t base = c * (uint32_t)(kMT * KPT) + (uint32_t)tid * KPT;
     uint32_t key[KPT];
-    chunk_keys<KPT>(score, forced, base, n, key);  // loads in flight while the copies are cleared
+    if constexpr (SEQNORM) {
+        static_assert(kMT == tgd::kSeqSumThreads, "every thread adds partials");
+        __shared__ double red[tgd::kSeqSumThreads / 64];
+        float4 sc[KPT / 4];
+        uint32_t fm[KPT / 4];
+        chunk_vals<KPT>(score, forced, base, n, sc, fm);
 #pragma unroll
-    for (int i = 0; i < kCopies * 2048 / (4 * kMT); ++i)
-        *reinterpret_cast<uint4*>(&h[0][0] + 4 * (i * kMT + tid)) = uint4{0u, 0u, 0u, 0u};
-    __syncthreads();
+        for (int i = 0; i < kCopies * 2048 / (4 * kMT); ++i)
+            *reinterpret_cast<uint4*>(&h[0][0] + 4 * (i * kMT + tid)) = uint4{0u, 0u, 0u, 0u};
+        tgd::seq_ss_partial(block_ss, nblocks, red);
+        __syncthreads();
+        const float inv = tgd::seq_inv_rho(red, (int64_t)n, eps_seq);
+#pragma unroll
+        for (int v = 0; v < KPT / 4; ++v) sc[v].x *= inv, sc[v].y *= inv, sc[v].z *= inv, sc[v].w *= inv;
+        if (base + KPT <= n) {
+#pragma unroll
+            for (int v = 0; v < KPT / 4; ++v) *reinterpret_cast<float4*>(s_norm + base + 4 * v) = sc[v];
+        } else {
+#pragma unroll
+            for (int v = 0; v < KPT / 4; ++v) {
+                const float t4[4] = {sc[v].x, sc[v].y, sc[v].z, sc[v].w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (base + 4 * v + q < n) s_norm[base + 4 * v + q] = t4[q];
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < KPT / 4; ++v) {
+            const float x[4] = {sc[v].x, sc[v].y, sc[v].z, sc[v].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                key[4 * v + q] = (fm[v] >> (8 * q)) & 0xffu ? kForcedMark : order_key(x[q]);
+        }
+    } else {
+        chunk_keys<KPT>(score, forced, base, n, key);  // loads in flight while the copies are cleared
+#pragma unroll
+        for (int i = 0; i < kCopies * 2048 / (4 * kMT); ++i)
+            *reinterpret_cast<uint4*>(&h[0][0] + 4 * (i * kMT + tid)) = uint4{0u, 0u, 0u, 0u};
+        __syncthreads();
+    }
     const int nvalid = base >= n ? 0 : (int)min((uint32_t)KPT, n - base);
     uint32_t fcount = 0;
 #pragma unroll
@@ -1044,11 +1116,21 @@ __global__ __launch_bounds__(kMT) void selm_emit(const float* __restrict__ score
     }
 }
 
+// With block_ss set, `score` holds the raw scores and the first launch forms
+// the normalised ones into s_norm, which the other two read.
 template <int KPT>
 int launch_select_multi(const float* score, const uint8_t* forced, int64_t n, int64_t n_forced, int64_t k,
-                        int32_t* kept_idx, int32_t* dev_status, const tgi::SelectWs& w, hipStream_t s) {
+                        int32_t* kept_idx, int32_t* dev_status, const tgi::SelectWs& w, hipStream_t s,
+                        const float* block_ss = nullptr, float eps_seq = 0.0f, float* s_norm = nullptr) {
     const uint32_t chunks = (uint32_t)tgi::select_chunks(n);
-    hipLaunchKernelGGL(selm_hist<KPT>, dim3(chunks), dim3(kMT), 0, s, score, forced, (uint32_t)n, w);
+    if (block_ss) {
+        hipLaunchKernelGGL((selm_hist<KPT, true>), dim3(chunks), dim3(kMT), 0, s, score, forced, (uint32_t)n, w,
+                           block_ss, tgi::gate_partials(n), eps_seq, s_norm);
+        score = s_norm;
+    } else {
+        hipLaunchKernelGGL((selm_hist<KPT, false>), dim3(chunks), dim3(kMT), 0, s, score, forced, (uint32_t)n, w,
+                           nullptr, (int64_t)0, 0.0f, nullptr);
+    }
     hipLaunchKernelGGL(selm_gather<KPT>, dim3(chunks), dim3(kMT), 0, s, score, forced, (uint32_t)n, chunks,
                        (uint32_t)k, n_forced, dev_status, w);
     hipLaunchKernelGGL(selm_emit<KPT>, dim3(chunks), dim3(kMT), 0, s, score, forced, (uint32_t)n, chunks,
@@ -1083,8 +1165,25 @@ int launch_select_topk(const float* score, const uint8_t* forced, int64_t n, int
 
 int launch_seqnorm_select(const float* s_raw, const float* block_ss, int64_t n, float eps_seq,
                           float* score_norm, const uint8_t* forced, int64_t n_forced, int64_t k,
-                          int32_t* kept_idx, int32_t* dev_status, void* stream) {
+                          int32_t* kept_idx, int32_t* dev_status, void* ws, void* stream) {
     static_assert(kSelectOneWgMax == kThreads * 16, "one workgroup of 16 keys a thread");
+    static_assert(kSelectMultiMin == kSelectOneWgMax + 1, "the two forms meet");
+    const int kpt = select_kpt(n);
+    if (kpt > 0) {
+        hipStream_t s = (hipStream_t)stream;
+        const SelectWs w = select_ws(static_cast<char*>(ws) + gate_bytes(n), n);
+        switch (kpt) {
+            case 8:
+                return launch_select_multi<8>(s_raw, forced, n, n_forced, k, kept_idx, dev_status, w, s, block_ss,
+                                              eps_seq, score_norm);
+            case 16:
+                return launch_select_multi<16>(s_raw, forced, n, n_forced, k, kept_idx, dev_status, w, s, block_ss,
+                                               eps_seq, score_norm);
+            default:
+                return launch_select_multi<32>(s_raw, forced, n, n_forced, k, kept_idx, dev_status, w, s, block_ss,
+                                               eps_seq, score_norm);
+        }
+    }
     if (n > kSelectOneWgMax) return TG_EUNSUPPORTED;
     hipLaunchKernelGGL((select_topk_regs<16, true>), dim3(1), dim3(kThreads), 0, (hipStream_t)stream, s_raw, forced,
                        n, n_forced, k, kept_idx, dev_status, block_ss, gate_partials(n), eps_seq, score_norm);

@@ -106,9 +106,9 @@ int tg_gate_score_select(const tg_bf16* resid, const tg_bf16* w1, const tg_bf16*
     float* s_raw = score_raw ? score_raw : score_norm;
     int rc = tgi::launch_gate_mlp(resid, w1, b1, w2, b2, n, d, hd, eps_row, s_raw, block_ss, stream);
     if (rc != TG_OK) return rc;
-    if (n <= tgi::kSelectOneWgMax)
+    if (n <= tgi::kSelectOneWgMax || tgi::select_kpt(n) > 0)
         return tgi::launch_seqnorm_select(s_raw, block_ss, n, eps_seq, score_norm, forced, n_forced, k, kept_idx,
-                                          dev_status, stream);
+                                          dev_status, workspace, stream);
     rc = tgi::launch_gate_seqnorm(s_raw, block_ss, n, eps_seq, score_norm, stream);
     if (rc != TG_OK) return rc;
     return tgi::launch_select_topk(score_norm, forced, n, n_forced, k, kept_idx, dev_status, workspace, stream);

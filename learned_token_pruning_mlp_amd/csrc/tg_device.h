@@ -71,11 +71,24 @@ __device__ __forceinline__ float wave_sum(float x) {
 // (seq_ss_partial), the four waves reduce by an xor butterfly whose lane-0
 // value is kept, and the four wave sums are added in wave order
 // (seq_inv_rho, after a barrier).  The scores are then s * (1 / rho).
+// A thread's partials are loaded four at a time from clamped indices, with no
+// branch between the loads (one round trip per four, not one per partial);
+// the ones past the end count as +0.0, which leaves the sum of non-negative
+// terms unchanged, so the order of the additions is the one stated above.
 constexpr int kSeqSumThreads = 256;
 __device__ __forceinline__ void seq_ss_partial(const float* block_ss, int64_t nblocks, double* red) {
     const int tid = threadIdx.x;  // < kSeqSumThreads
     double acc = 0.0;
-    for (int64_t b = tid; b < nblocks; b += kSeqSumThreads) acc += (double)block_ss[b];
+    for (int64_t b0 = tid; b0 < nblocks; b0 += 4 * kSeqSumThreads) {
+        float x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t b = b0 + (int64_t)j * kSeqSumThreads;
+            x[j] = block_ss[b < nblocks ? b : nblocks - 1];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc += b0 + (int64_t)j * kSeqSumThreads < nblocks ? (double)x[j] : 0.0;
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
     if ((tid & 63) == 0) red[tid >> 6] = acc;

@@ -119,11 +119,14 @@ int launch_gate_seqnorm(const float* s_raw, const float* block_ss, int64_t n, fl
 // norm can run inside that workgroup (tg_gate_score_select).
 constexpr int64_t kSelectOneWgMax = 16384;
 
-// Sequence norm and select in one launch (n <= kSelectOneWgMax): from the raw
-// scores and their partial sums to the normalised scores and the kept set.
+// Sequence norm and select together, from the raw scores and their partial
+// sums to the normalised scores and the kept set: one launch up to
+// kSelectOneWgMax tokens, the norm inside the first of the many-workgroup
+// select's launches from there up to its limit (ws: the whole workspace, as
+// for launch_select_topk); TG_EUNSUPPORTED beyond.
 int launch_seqnorm_select(const float* s_raw, const float* block_ss, int64_t n, float eps_seq,
                           float* score_norm, const uint8_t* forced, int64_t n_forced, int64_t k,
-                          int32_t* kept_idx, int32_t* dev_status, void* stream);
+                          int32_t* kept_idx, int32_t* dev_status, void* ws, void* stream);
 
 int launch_select_topk(const float* score, const uint8_t* forced, int64_t n, int64_t n_forced,
                        int64_t k, int32_t* kept_idx, int32_t* dev_status, void* ws, void* stream);

@@ -17,7 +17,7 @@ int launch_gate_mlp(const uint16_t*, const uint16_t*, const uint16_t*, const uin
                     float*, float*, void*) { return kReached; }
 int launch_gate_seqnorm(const float*, const float*, int64_t, float, float*, void*) { return kReached; }
 int launch_seqnorm_select(const float*, const float*, int64_t, float, float*, const uint8_t*, int64_t, int64_t,
-                          int32_t*, int32_t*, void*) { return kReached; }
+                          int32_t*, int32_t*, void*, void*) { return kReached; }
 int launch_compact(const int32_t*, int64_t, int64_t, const uint16_t*, uint16_t*, int, const int32_t*, int32_t*,
                    const float*, float*, const tg_gather*, int, void*) { return kReached; }
 int launch_rope(uint16_t*, const int32_t*, int64_t, int, int, double, void*) { return kReached; }

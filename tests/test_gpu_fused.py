@@ -1,9 +1,10 @@
 """tg_gate_score_select against its two calls, tg_gate_score then
 tg_select_topk on the normalised scores: the same normalised and raw scores,
 kept indices and status word, bit for bit.  Up to 16384 tokens the sequence
-norm runs inside the one-workgroup select; longer prompts take the two calls'
-kernels.  (The two calls themselves are pinned to the oracle in
-test_gpu_steps.py and test_gpu_workloads.py.)"""
+norm runs inside the one-workgroup select, up to 524288 inside the first
+launch of the many-workgroup select (8, 16 and 32 keys a thread); longer
+prompts take the two calls' kernels.  (The two calls themselves are pinned to
+the oracle in test_gpu_steps.py and test_gpu_workloads.py.)"""
 import numpy as np
 import pytest
 import torch
@@ -45,6 +46,12 @@ def _run(n, d, hd, f, k, seed, layout, with_raw, with_forced, fused):
     (16384, 2048, 256, 64, 2048, "tail", False, True),
     (16383, 512, 128, 64, 4000, "tail", True, True),
     (16385, 512, 128, 64, 2048, "tail", True, True),
+    (32768, 512, 128, 64, 1024, "scatter_tail", False, True),
+    (50001, 256, 64, 64, 5000, "tail", True, True),
+    (131072, 512, 64, 0, 8192, "tail", True, False),
+    (262147, 128, 64, 64, 20000, "scatter_tail", False, True),
+    (524288, 128, 64, 64, 4096, "tail", True, True),
+    (524289, 128, 64, 64, 4096, "tail", False, True),
 ])
 def test_gate_score_select_matches_two_calls(n, d, hd, f, k, layout, with_raw, with_forced):
     gu.say(f"gate_score_select n={n} d={d} hd={hd} k={k}")
@@ -60,10 +67,11 @@ def test_gate_score_select_matches_two_calls(n, d, hd, f, k, layout, with_raw, w
     assert np.array_equal(a[2], oracle.select_topk(a[0], forced, k))
 
 
-def test_gate_score_select_status_word():
+@pytest.mark.parametrize("n", [2000, 40000])
+def test_gate_score_select_status_word(n):
     """A forced count that disagrees with the mask is reported, as by the select."""
-    n, d, hd, f, k = 2000, 256, 64, 40, 200
-    gu.say("gate_score_select status word")
+    d, hd, f, k = 256, 64, 40, 200
+    gu.say(f"gate_score_select status word n={n}")
     shp = synth.GateShape(n=n, d=d, hd=hd, n_forced=f, k=k, hq=1, hkv=1, head_dim=64)
     inp = synth.gate_inputs(shp, 3)
     s_norm = torch.empty(n, dtype=torch.float32, device=gu.dev())
