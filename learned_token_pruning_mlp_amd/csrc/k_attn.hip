@@ -138,6 +138,11 @@ __device__ __forceinline__ int swz(int r) {
     return ((x & 1) << 2) | (x >> 1);
 }
 
+// Workgroup barrier that waits only for this wave's LDS accesses: memory
+// loads in flight (the next query block's rows, the next super-tile) stay in
+// flight across it.  The memory clobber keeps LDS accesses on their side.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // acc + lo + hi of a packed bf16 pair, in fp32.
 __device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -251,21 +256,31 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
 
     // ---- per query-block state of this wave (head h, rows q0 .. q0+31)
     u32x4 qreg[C::QS];
+    int qpos = 0;
     f32x16 o[C::DB];
     float m_run = -INFINITY, l_run = 0.0f, a_t = 0.0f, sgl = 0.0f;
     int q0 = 0, t = 0, wave_last = 0;
 
-    auto begin_block = [&](int qb) {
+    // Query rows and original position of this lane's row of block qb.
+    auto fetch_q = [&](int qb) {
+        const int tq = C::QROWS * qb + 32 * rb + l32;
+        const bool ok = tq < nk;
+        const uint16_t* qp = q + ((int64_t)tq * hq + h) * D;
+#pragma unroll
+        for (int s = 0; s < C::QS; ++s)
+            qreg[s] = ok ? *reinterpret_cast<const u32x4*>(qp + s * 16 + g * 8) : u32x4{0, 0, 0, 0};
+        qpos = ok ? pos[tq] : 0;
+    };
+    // fetched: fetch_q(qb) was issued already (the second block's rows go
+    // out before the first block's merge, so their latency hides behind it)
+    auto begin_block = [&](int qb, bool fetched) {
         q0 = C::QROWS * qb + 32 * rb;
         t = q0 + l32;
         wave_last = min(nk - 1, q0 + 31);
         const bool ok = t < nk;
-        const uint16_t* qp = q + ((int64_t)t * hq + h) * D;
-#pragma unroll
-        for (int s = 0; s < C::QS; ++s)
-            qreg[s] = ok ? *reinterpret_cast<const u32x4*>(qp + s * 16 + g * 8) : u32x4{0, 0, 0, 0};
+        if (!fetched) fetch_q(qb);
         float lam = 1.0f;
-        if (ok) lam = 1.0f + temp_coef * logf((float)(t + 1) / ((float)pos[t] + 1.0f));
+        if (ok) lam = 1.0f + temp_coef * logf((float)(t + 1) / ((float)qpos + 1.0f));
         // A row with lambda < 0 takes z = |lambda| * (-S): its query and its
         // key-bias scale change sign (exact), so every row has a positive exp2
         // scale; lambda = 0 (all logits 0) takes a tiny positive one.
@@ -303,7 +318,7 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
                 const int off = (hr * NS + slot) * C::SLOT_BYTES;
                 return reinterpret_cast<float*>(off < C::TILE_BYTES ? scK + off : scV + (off - C::TILE_BYTES));
             };
-            __syncthreads();  // every wave is done with this stage's K/V
+            lds_barrier();  // every wave is done with this stage's K/V
             // One round with split stride S while holding units LO .. LO+2*half-1;
             // x = XOR of the strides of the earlier rounds.  The branch on this
             // wave's split bit is wave-uniform; every wave meets one barrier.
@@ -326,7 +341,7 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
                         mbuf[hr][ws][l32] = m_run;
                         lbuf[hr][ws][l32] = l;
                     }
-                    __syncthreads();
+                    lds_barrier();
                     const float mp = mbuf[hr][rs][l32], lp = lbuf[hr][rs][l32];
                     const float mn = fmaxf(m_run, mp);
                     const float fs = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - mn);
@@ -521,7 +536,7 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
                        uint8_t* __restrict__ nK, uint8_t* __restrict__ nV, float* __restrict__ nS) {
         const bool inA = it < nA;
         const int st = inA ? it : it - nA;
-        if (st == 0) begin_block(inA ? qbA : qbB);
+        if (st == 0) begin_block(inA ? qbA : qbB, !inA);
         TG_WAIT_VMCNT(0);
         __builtin_amdgcn_s_barrier();
         const bool more = it + 1 < ntot;
@@ -529,7 +544,10 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
             if (more) issue(it + 1, nK, nV, nS);
         });
         const int last = inA ? nA - 1 : ntot - nA - 1;
-        if (st == last) finish_block(cK, cV);  // K and V of this stage serve as merge scratch
+        if (st == last) {
+            if (inA && ntot > nA) fetch_q(qbB);  // this block's rows are no longer read
+            finish_block(cK, cV);  // K and V of this stage serve as merge scratch
+        }
     };
 
     issue(0, sK0, sV0, sS0);
