@@ -156,13 +156,16 @@ def test_select_forced_count_status():
 
 @pytest.mark.parametrize("case", ["ragged_16385", "ragged_50001", "ragged_131071", "kpt16_262147",
                                   "kpt32_524288", "one_wg_beyond_524289", "int_ties_100000", "student_t_65536",
-                                  "specials_40000", "k_equals_n_70000", "k_one_70000", "all_equal_131072"])
+                                  "specials_40000", "k_equals_n_70000", "k_one_70000", "all_equal_131072",
+                                  "few_ties_131072", "no_forced_50001", "whole_chunks_98304"])
 def test_select_many_workgroups(case):
     """Prompts past 16384 tokens: the select that runs over chunks of the
-    prompt in several workgroups (three launches), at ragged lengths, each
-    chunk size, heavy ties, heavy tails, special values, the budget
-    extremes and the all-equal closed form; one case past its largest size
-    (the one-workgroup fallback)."""
+    prompt in several workgroups (three launches), at ragged lengths and
+    whole chunks, each chunk size, heavy ties (five values at 131072 tokens:
+    the first round's bin holds more keys than the last launch keeps in
+    LDS, so it reads them from memory), heavy tails, special values, no
+    forced mask, the budget extremes and the all-equal closed form; one case
+    past its largest size (the one-workgroup fallback)."""
     name, n = case.rsplit("_", 1)
     n = int(n)
     g = np.random.default_rng(n + len(name))
@@ -171,6 +174,8 @@ def test_select_many_workgroups(case):
     k = max(96, n // 16)
     if name == "int_ties":
         score = g.integers(-6, 7, size=n).astype(np.float32) * 0.5
+    elif name == "few_ties":
+        score = g.integers(-2, 3, size=n).astype(np.float32)
     elif name == "student_t":
         score = synth.student_t_scores(n, seed=9)
     elif name == "specials":
@@ -186,6 +191,8 @@ def test_select_many_workgroups(case):
     elif name == "k_one":
         forced[:] = 0
         k = 1
+    if name == "no_forced":
+        forced = None
     gu.say(f"select many workgroups: {case} k={k}")
     got, st = _run_select(score, forced, k)
     assert st == 0
