@@ -174,10 +174,12 @@ class Path:
     def extra_row_bytes(self):
         return sum(s[0].numel() * s.element_size() for s, _ in self.extra)
 
-    def step(self, i, ev=None):
+    def step(self, i, ev=None, attn_ev=None):
         """One pass of the path.  ev: optional list of 6 events (or None
         entries) recorded between the stages; the rope / attention marks go
-        around the first upper layer's launches."""
+        around the first upper layer's launches.  attn_ev: optional pair of
+        events that the first upper layer's attention launch records at the
+        kernel's own start and end (tg_gated_attention_timed)."""
         tg, shp = self.tg, self.shp
 
         def mark(j):
@@ -204,8 +206,12 @@ class Path:
             tg.tg_rope_qk(self.q[L], self.kk[L], self.pos_k, shp.rope_theta)
             if L == 0:
                 mark(4)
-            tg.tg_gated_attention(self.q[L], self.kk[L], self.vv[L], self.score_k, self.gains, shp.temp_coef,
-                                  self.pos_k, self.out)
+            if L == 0 and attn_ev is not None:
+                tg.tg_gated_attention_timed(self.q[L], self.kk[L], self.vv[L], self.score_k, self.gains,
+                                            shp.temp_coef, self.pos_k, self.out, attn_ev[0], attn_ev[1])
+            else:
+                tg.tg_gated_attention(self.q[L], self.kk[L], self.vv[L], self.score_k, self.gains, shp.temp_coef,
+                                      self.pos_k, self.out)
             if L == 0:
                 mark(5)
 
@@ -254,20 +260,30 @@ def main():
     median_step_ms = step_ms[n_diag // 2] if n_diag % 2 else 0.5 * (step_ms[n_diag // 2 - 1] + step_ms[n_diag // 2])
 
     # ---- timed region: exactly `steps` steps, synchronised on both sides.
-    # Only the dominant stage's first launch is bracketed by events (on the
-    # stream its kernel runs on), on every EV_STRIDE-th step whatever the
-    # step count: each event record adds a barrier packet and a timestamp to
-    # the queue, which is instrumentation, not work of the path.  The events
-    # also take in the dispatch gap before the kernel starts.
+    # Only the dominant stage's first launch is timed, on every EV_STRIDE-th
+    # step whatever the step count.  Attention records a pair of events at
+    # its kernel's own start and end (tg_gated_attention_timed, on the stream
+    # the kernel runs on); another dominant stage is bracketed by events
+    # recorded around its call, which also take in the dispatch gap before
+    # the kernel starts.  Each timed launch adds queue work (timestamps),
+    # which is instrumentation, not work of the path.
     ev_steps = list(range(min(EV_OFFSET, args.steps - 1), args.steps, EV_STRIDE))
     dom_ev = {i: (Ev(), Ev()) for i in ev_steps}
+    kernel_events = dom == "gated_attention"
+    if kernel_events:
+        for a, b in dom_ev.values():  # torch creates an event's handle at its first record
+            a.record(stream)
+            b.record(stream)
 
     def timed_step(i):
-        marks = None
-        if i in dom_ev:
+        if i not in dom_ev:
+            path.step(i)
+        elif kernel_events:
+            path.step(i, attn_ev=dom_ev[i])
+        else:
             marks = [None] * 6
             marks[dom_j], marks[dom_j + 1] = dom_ev[i]
-        path.step(i, marks)
+            path.step(i, marks)
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -295,6 +311,8 @@ def main():
                 "frac": achieved / PEAK_HBM_GBS, "traffic": None}
     roof["launch_us"] = dom_ms * 1e3
     roof["timed_launches"] = len(dom_ev)
+    roof["timing"] = ("events recorded at the kernel's start and end (extended launch)" if kernel_events
+                      else "events recorded around the call (dispatch gap included)")
     attn_tflops = attn_flops(shp) / (per_stage["gated_attention"] * 1e-3) / 1e12
     gate_gbs = gate_bytes(shp) / (per_stage["gate_score"] * 1e-3) / 1e9
     compact_gbs = compact_bytes(shp, path.extra_row_bytes()) / (per_stage["compact"] * 1e-3) / 1e9

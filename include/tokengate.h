@@ -230,6 +230,21 @@ int tg_gated_attention(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v,
                        int32_t head_dim, void* out, int32_t out_dtype, void* stream);
 
 /*
+ * tg_gated_attention_timed -- tg_gated_attention (same arguments, checks and
+ * results, bit for bit) for measuring the attention kernel alone: the launch
+ * also records start_event and stop_event (hipEvent_t, created by the caller
+ * with timing enabled, owned by the caller; either may be NULL) at the
+ * kernel's own start and end, so hipEventElapsedTime(start, stop) leaves out
+ * the queue's dispatch gap that events recorded around the call take in.
+ * Nothing is recorded when n_kept == 0 or a check fails.
+ */
+int tg_gated_attention_timed(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v,
+                             const float* key_score, const float* gains, float temp_coef,
+                             const int32_t* pos, int64_t n_kept, int32_t hq, int32_t hkv,
+                             int32_t head_dim, void* out, int32_t out_dtype, void* stream,
+                             void* start_event, void* stop_event);
+
+/*
  * tg_attention_bwd_workspace_bytes -- device workspace of tg_gated_attention_bwd
  * (256-byte aligned): about 4 * n_kept * hq * head_dim bytes plus per-row
  * arrays.

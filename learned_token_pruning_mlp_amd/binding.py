@@ -28,6 +28,7 @@ TG_MAX_GATHER = 16
 
 EXPORTS = ("tg_status_string", "tg_abi_version", "tg_workspace_bytes", "tg_gate_score", "tg_gate_score_noalloc",
            "tg_select_topk", "tg_gate_score_select", "tg_compact", "tg_rope", "tg_rope_qk", "tg_gated_attention",
+           "tg_gated_attention_timed",
            "tg_rmsnorm", "tg_swiglu", "tg_blas_create", "tg_blas_destroy", "tg_linear",
            "tg_attention_bwd_workspace_bytes", "tg_gated_attention_bwd", "tg_gate_score_bwd_workspace_bytes",
            "tg_gate_score_bwd", "tg_gated_delta_rule")
@@ -79,6 +80,8 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
     L.tg_rope_qk.restype = ctypes.c_int
     L.tg_gated_attention.argtypes = [P, P, P, P, P, F, P, I64, I32, I32, I32, P, I32, P]
     L.tg_gated_attention.restype = ctypes.c_int
+    L.tg_gated_attention_timed.argtypes = [P, P, P, P, P, F, P, I64, I32, I32, I32, P, I32, P, P, P]
+    L.tg_gated_attention_timed.restype = ctypes.c_int
     L.tg_rmsnorm.argtypes = [P, P, P, I64, I32, F, P]
     L.tg_rmsnorm.restype = ctypes.c_int
     L.tg_swiglu.argtypes = [P, P, I64, I32, P]
@@ -293,9 +296,7 @@ def tg_rope_qk(q: torch.Tensor, k: torch.Tensor, pos: torch.Tensor, theta: float
                                            _stream(stream)))
 
 
-def tg_gated_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_score: torch.Tensor,
-                       gains: torch.Tensor, temp_coef: float, pos: torch.Tensor, out: torch.Tensor,
-                       stream=None) -> None:
+def _attention_args(q, k, v, key_score, gains, temp_coef, pos, out, stream):
     nk, hq, D = q.shape
     hkv = k.shape[1]
     _need(q, "q", torch.bfloat16, (nk, hq, D))
@@ -311,9 +312,30 @@ def tg_gated_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_sc
     else:
         raise ValueError("out must be bfloat16 or float32")
     _need(out, "out", out.dtype, (nk, hq, D))
+    return (_ptr(q), _ptr(k), _ptr(v), _ptr(key_score), _ptr(gains), float(temp_coef), _ptr(pos), nk, hq, hkv, D,
+            _ptr(out), od, _stream(stream))
+
+
+def tg_gated_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_score: torch.Tensor,
+                       gains: torch.Tensor, temp_coef: float, pos: torch.Tensor, out: torch.Tensor,
+                       stream=None) -> None:
     _check("tg_gated_attention", load().tg_gated_attention(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(key_score), _ptr(gains), float(temp_coef), _ptr(pos), nk, hq, hkv, D,
-        _ptr(out), od, _stream(stream)))
+        *_attention_args(q, k, v, key_score, gains, temp_coef, pos, out, stream)))
+
+
+def tg_gated_attention_timed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_score: torch.Tensor,
+                             gains: torch.Tensor, temp_coef: float, pos: torch.Tensor, out: torch.Tensor,
+                             start, stop, stream=None) -> None:
+    """tg_gated_attention whose launch also records two torch.cuda.Event
+    objects (timing enabled) at the attention kernel's own start and end.
+    torch creates an event's HIP handle at its first record, so each must
+    have been recorded once before."""
+    for e in (start, stop):
+        if not e.cuda_event:
+            raise ValueError("record each event once before passing it (its HIP handle is created then)")
+    _check("tg_gated_attention_timed", load().tg_gated_attention_timed(
+        *_attention_args(q, k, v, key_score, gains, temp_coef, pos, out, stream), start.cuda_event,
+        stop.cuda_event))
 
 
 def tg_rmsnorm(x: torch.Tensor, weight: torch.Tensor, y: torch.Tensor, eps: float, stream=None) -> None:

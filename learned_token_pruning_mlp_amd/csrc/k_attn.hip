@@ -52,6 +52,7 @@
 //  * Work items are laid out so all workgroups of one kv head run on the same
 //    XCD (workgroups go round-robin over the 8 XCDs), keeping that head's K/V
 //    in one L2.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -557,10 +558,25 @@ __global__ __launch_bounds__(64 * HPW * RB * NS, 1) void gated_attn(const uint16
     }
 }
 
+// The stream of a launch and, optionally, two events that record the
+// kernel's own start and end (an extended launch; null: a plain launch).
+struct Launch {
+    hipStream_t s;
+    hipEvent_t start, stop;
+};
+
+template <typename... A, typename... P>
+void launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, const Launch& L, A... args) {
+    if (L.start || L.stop)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, L.s, L.start, L.stop, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, L.s, args...);
+}
+
 template <int D, int HPW, int RB, int NS, int KB>
 int launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* ks, const float* gains,
                 float c, const int32_t* pos, int64_t nk, int hq, int hkv, void* out, int out_dtype,
-                float* lse, int lse_ld, hipStream_t s) {
+                float* lse, int lse_ld, const Launch& L) {
     using C = AttnCfg<D, HPW, RB, NS, KB>;
     const int nqb = (int)((nk + C::QROWS - 1) / C::QROWS);
     const int npairs = (nqb + 1) / 2;
@@ -568,11 +584,11 @@ int launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const f
     const int per_xcd = (n_items + kXcds - 1) / kXcds;
     const dim3 grid((unsigned)(per_xcd * kXcds));
     if (out_dtype == 1)
-        hipLaunchKernelGGL((gated_attn<D, HPW, RB, NS, KB, true>), grid, dim3(C::THREADS), 0, s, q, k, v, ks, gains,
-                           c, pos, (int)nk, hq, hkv, npairs, per_xcd, n_items, out, lse, lse_ld);
+        launch_kernel(gated_attn<D, HPW, RB, NS, KB, true>, grid, dim3(C::THREADS), L, q, k, v, ks, gains, c, pos,
+                      (int)nk, hq, hkv, npairs, per_xcd, n_items, out, lse, lse_ld);
     else
-        hipLaunchKernelGGL((gated_attn<D, HPW, RB, NS, KB, false>), grid, dim3(C::THREADS), 0, s, q, k, v, ks, gains,
-                           c, pos, (int)nk, hq, hkv, npairs, per_xcd, n_items, out, lse, lse_ld);
+        launch_kernel(gated_attn<D, HPW, RB, NS, KB, false>, grid, dim3(C::THREADS), L, q, k, v, ks, gains, c, pos,
+                      (int)nk, hq, hkv, npairs, per_xcd, n_items, out, lse, lse_ld);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_EDEVICE;
 }
 
@@ -590,28 +606,28 @@ inline int64_t attn_items(int64_t nk, int hq, int hkv, int hpw, int rb) {
 template <int D, int HPW>
 int launch_attn_h(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* ks, const float* gains,
                   float c, const int32_t* pos, int64_t nk, int hq, int hkv, void* out, int out_dtype,
-                  float* lse, int lse_ld, hipStream_t s) {
+                  float* lse, int lse_ld, const Launch& L) {
     constexpr int kCUs = 256;
     constexpr int W = HPW == 1 ? 4 : 8 / HPW;  // row blocks x splits
     if constexpr (W >= 4) {
         if (attn_items(nk, hq, hkv, HPW, 4) >= kCUs)
-            return launch_attn<D, HPW, 4, W / 4, 2>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, lse, lse_ld, s);
+            return launch_attn<D, HPW, 4, W / 4, 2>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, lse, lse_ld, L);
     }
     if constexpr (W >= 2) {
         if (attn_items(nk, hq, hkv, HPW, 2) >= kCUs)
-            return launch_attn<D, HPW, 2, W / 2, 2>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, lse, lse_ld, s);
+            return launch_attn<D, HPW, 2, W / 2, 2>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, lse, lse_ld, L);
     }
-    return launch_attn<D, HPW, 1, W, (W >= 4 ? 1 : 2)>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, lse, lse_ld, s);
+    return launch_attn<D, HPW, 1, W, (W >= 4 ? 1 : 2)>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, lse, lse_ld, L);
 }
 
 template <int D>
 int launch_attn_d(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* ks, const float* gains,
                   float c, const int32_t* pos, int64_t nk, int hq, int hkv, void* out, int out_dtype,
-                  float* lse, int lse_ld, hipStream_t s) {
+                  float* lse, int lse_ld, const Launch& L) {
     const int G = hq / hkv;
-    if (G % 4 == 0) return launch_attn_h<D, 4>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, lse, lse_ld, s);
-    if (G % 2 == 0) return launch_attn_h<D, 2>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, lse, lse_ld, s);
-    return launch_attn_h<D, 1>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, lse, lse_ld, s);
+    if (G % 4 == 0) return launch_attn_h<D, 4>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, lse, lse_ld, L);
+    if (G % 2 == 0) return launch_attn_h<D, 2>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, lse, lse_ld, L);
+    return launch_attn_h<D, 1>(q, k, v, ks, gains, c, pos, nk, hq, hkv, out, out_dtype, lse, lse_ld, L);
 }
 
 }  // namespace
@@ -621,13 +637,14 @@ namespace tgi {
 int launch_gated_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                            const float* key_score, const float* gains, float temp_coef,
                            const int32_t* pos, int64_t n_kept, int hq, int hkv, int head_dim,
-                           void* out, int out_dtype, float* lse, int lse_ld, void* stream) {
-    hipStream_t s = (hipStream_t)stream;
+                           void* out, int out_dtype, float* lse, int lse_ld, void* stream, void* start_event,
+                           void* stop_event) {
+    const Launch L{(hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event};
     switch (head_dim) {
         case 64:
-            return launch_attn_d<64>(q, k, v, key_score, gains, temp_coef, pos, n_kept, hq, hkv, out, out_dtype, lse, lse_ld, s);
+            return launch_attn_d<64>(q, k, v, key_score, gains, temp_coef, pos, n_kept, hq, hkv, out, out_dtype, lse, lse_ld, L);
         case 128:
-            return launch_attn_d<128>(q, k, v, key_score, gains, temp_coef, pos, n_kept, hq, hkv, out, out_dtype, lse, lse_ld, s);
+            return launch_attn_d<128>(q, k, v, key_score, gains, temp_coef, pos, n_kept, hq, hkv, out, out_dtype, lse, lse_ld, L);
         default:
             return TG_EUNSUPPORTED;
     }

@@ -168,6 +168,14 @@ int tg_rope_qk(tg_bf16* q, tg_bf16* k, const int32_t* pos, int64_t rows, int32_t
 int tg_gated_attention(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, const float* key_score,
                        const float* gains, float temp_coef, const int32_t* pos, int64_t n_kept, int32_t hq,
                        int32_t hkv, int32_t head_dim, void* out, int32_t out_dtype, void* stream) {
+    return tg_gated_attention_timed(q, k, v, key_score, gains, temp_coef, pos, n_kept, hq, hkv, head_dim, out,
+                                    out_dtype, stream, nullptr, nullptr);
+}
+
+int tg_gated_attention_timed(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, const float* key_score,
+                             const float* gains, float temp_coef, const int32_t* pos, int64_t n_kept, int32_t hq,
+                             int32_t hkv, int32_t head_dim, void* out, int32_t out_dtype, void* stream,
+                             void* start_event, void* stop_event) {
     if (n_kept < 0 || n_kept > kMaxRows || hq < 1 || hkv < 1 || hq % hkv != 0) return TG_EINVAL;
     if (out_dtype != 0 && out_dtype != 1) return TG_EINVAL;
     if (!(temp_coef == temp_coef) || temp_coef > 3.4e38f || temp_coef < -3.4e38f) return TG_EINVAL;
@@ -180,7 +188,7 @@ int tg_gated_attention(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, con
         !aligned(gains, 4) || !aligned(pos, 4))
         return TG_EALIGN;
     return tgi::launch_gated_attention(q, k, v, key_score, gains, temp_coef, pos, n_kept, hq, hkv, head_dim, out,
-                                       out_dtype, nullptr, 0, stream);
+                                       out_dtype, nullptr, 0, stream, start_event, stop_event);
 }
 
 size_t tg_attention_bwd_workspace_bytes(int64_t n_kept, int32_t hq, int32_t hkv, int32_t head_dim) {

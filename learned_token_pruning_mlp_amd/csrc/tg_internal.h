@@ -142,10 +142,13 @@ int launch_rope(uint16_t* x, const int32_t* pos, int64_t rows, int heads, int he
 int launch_rope_qk(uint16_t* q, uint16_t* k, const int32_t* pos, int64_t rows, int hq, int hk, int head_dim,
                    double theta, void* stream);
 
+// start_event / stop_event (hipEvent_t, may be null): recorded at the
+// attention kernel's own start and end (an extended launch).
 int launch_gated_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                            const float* key_score, const float* gains, float temp_coef,
                            const int32_t* pos, int64_t n_kept, int hq, int hkv, int head_dim,
-                           void* out, int out_dtype, float* lse, int lse_ld, void* stream);
+                           void* out, int out_dtype, float* lse, int lse_ld, void* stream,
+                           void* start_event = nullptr, void* stop_event = nullptr);
 
 // Workspace of the attention backward (fp32 arrays; row arrays padded to kp =
 // n_kept rounded up to 32 rows): the recomputed forward output [n, hq, D], the

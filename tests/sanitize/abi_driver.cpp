@@ -75,6 +75,8 @@ int main() {
     EXPECT(tg_gated_attention(A, A, A, F, F, 0.1f, I, 128, 4, 2, 64, A, 0, nullptr), R);
     EXPECT(tg_gated_attention(A, A, A, F, F, 0.1f, I, 128, 6, 4, 64, A, 0, nullptr), TG_EINVAL);
     EXPECT(tg_gated_attention(A, A, A, F, F, 0.1f, I, 1 << 20, 16, 8, 128, A, 0, nullptr), TG_EUNSUPPORTED);
+    EXPECT(tg_gated_attention_timed(A, A, A, F, F, 0.1f, I, 128, 4, 2, 64, A, 0, nullptr, A, A), R);
+    EXPECT(tg_gated_attention_timed(A, A, A, F, F, 0.1f, I, 128, 4, 2, 64, A + 1, 0, nullptr, A, A), TG_EALIGN);
     const size_t wsb = tg_attention_bwd_workspace_bytes(64, 4, 2, 64);
     EXPECT(tg_gated_attention_bwd(A, A, A, F, F, 0.1f, I, 64, 4, 2, 64, A, F, F, F, F, F, F, W, wsb, nullptr), R);
     EXPECT(tg_gated_attention_bwd(A, A, A, F, F, 0.1f, I, 131072, 64, 8, 128, A, F, F, F, F, F, F, W, wsb, nullptr),

@@ -23,7 +23,9 @@ int launch_compact(const int32_t*, int64_t, int64_t, const uint16_t*, uint16_t*,
 int launch_rope(uint16_t*, const int32_t*, int64_t, int, int, double, void*) { return kReached; }
 int launch_rope_qk(uint16_t*, uint16_t*, const int32_t*, int64_t, int, int, int, double, void*) { return kReached; }
 int launch_gated_attention(const uint16_t*, const uint16_t*, const uint16_t*, const float*, const float*, float,
-                           const int32_t*, int64_t, int, int, int, void*, int, float*, int, void*) { return kReached; }
+                           const int32_t*, int64_t, int, int, int, void*, int, float*, int, void*, void*, void*) {
+    return kReached;
+}
 int launch_gated_attention_bwd(const uint16_t*, const uint16_t*, const uint16_t*, const float*, const float*, float,
                                const int32_t*, int64_t, int, int, int, const uint16_t*, float*, float*, float*, float*,
                                float*, float*, void*, void*) { return kReached; }

@@ -370,6 +370,38 @@ def test_attention_large_temperature_and_bias():
     gu.check_attention(gu.host(_run_attn(a)), ref, "heavy tails")
 
 
+@pytest.mark.parametrize("nk", [1000, 2048])
+def test_attention_timed_matches_plain(nk):
+    """tg_gated_attention_timed: the same output bit for bit (fp32 and bf16),
+    and its events hold a positive interval no longer than that of events
+    recorded around the call on the same stream."""
+    gu.say(f"attention timed variant nk={nk}")
+    a = synth.attn_inputs(nk, 16, 8, 128, seed=nk)
+    args = (gu.bf16(a.q), gu.bf16(a.k), gu.bf16(a.v), gu.f32(a.key_score), gu.f32(a.gains), a.temp_coef,
+            gu.i32(a.pos))
+    stream = torch.cuda.current_stream()
+    Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    for dt in (torch.float32, torch.bfloat16):
+        plain = torch.empty((nk, 16, 128), dtype=dt, device=gu.dev())
+        timed = torch.full((nk, 16, 128), float("nan"), dtype=dt, device=gu.dev())
+        tg.tg_gated_attention(*args, plain)
+        s0, s1, o0, o1 = Ev(), Ev(), Ev(), Ev()
+        for e in (s0, s1):
+            e.record(stream)  # creates the event's handle
+        torch.cuda.synchronize()
+        o0.record(stream)
+        tg.tg_gated_attention_timed(*args, timed, s0, s1)
+        o1.record(stream)
+        torch.cuda.synchronize()
+        assert torch.equal(plain.view(torch.int16 if dt == torch.bfloat16 else torch.int32),
+                           timed.view(torch.int16 if dt == torch.bfloat16 else torch.int32))
+        inner, outer = s0.elapsed_time(s1), o0.elapsed_time(o1)
+        gu.say(f"  {dt}: kernel events {inner * 1e3:.1f} us, events around the call {outer * 1e3:.1f} us")
+        assert 0.0 < inner <= outer + 1e-3
+    with pytest.raises(ValueError):
+        tg.tg_gated_attention_timed(*args, plain, Ev(), Ev())  # events never recorded: no handle yet
+
+
 def test_attention_deterministic():
     gu.say("attention determinism")
     a = synth.attn_inputs(1500, 16, 8, 128, seed=3)
