@@ -12,7 +12,9 @@
  *   tg_gated_attention -> causal attention over the kept tokens only, with a
  *                         per-key importance bias and a per-query temperature.
  * Training-side gradients: tg_gated_attention_bwd, tg_gate_score_bwd.  The
- * hybrid backbone's recurrent mixer over the kept tokens: tg_gated_delta_rule.
+ * hybrid backbone's recurrent mixer over the kept tokens: tg_gated_delta_rule
+ * (a scan over the tokens) and tg_gated_delta_rule_chunked (in chunks on the
+ * matrix cores, with a workspace).
  * The rest of an upper decoder layer on the kept rows (see the section at the
  * end): tg_rmsnorm, tg_swiglu, and tg_linear (a rocBLAS GEMM through a handle
  * from tg_blas_create).
@@ -346,6 +348,27 @@ int tg_gate_score_bwd(void* blas, const tg_bf16* resid, const tg_bf16* w1, const
 int tg_gated_delta_rule(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, const float* alpha, const float* beta,
                         const float* state_in, int64_t n, int32_t hk, int32_t hv, int32_t dk, int32_t dv, float* out,
                         float* state_out, void* stream);
+
+/*
+ * tg_gated_delta_rule_chunked -- tg_gated_delta_rule in chunks of 32 tokens on
+ * the matrix cores (the chunkwise WY / UT form of the Gated Delta Networks
+ * paper): the same arguments, checks and definition, plus a workspace.  A
+ * pre-pass forms every chunk's state-independent transform at once (Gram
+ * products, decay table, the inverse of the chunk's unit lower-triangular
+ * system) and writes it to the workspace, one 16 KB record per (v head,
+ * chunk); then the state walks the chunks, one workgroup per 16 rows of a
+ * head's state.  fp32 operands enter the bf16 matrix cores split into three
+ * parts (fp32-level products); the results agree with tg_gated_delta_rule to
+ * rounding, not bit for bit.  Deterministic.  A run split at a multiple of 32
+ * tokens with the state carried over equals one run bit for bit.
+ * workspace: tg_gated_delta_rule_workspace_bytes(n, hv) bytes, 16-byte
+ * aligned, overwritten (no contents need clearing); not needed when n == 0.
+ */
+size_t tg_gated_delta_rule_workspace_bytes(int64_t n, int32_t hv);
+int tg_gated_delta_rule_chunked(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, const float* alpha,
+                                const float* beta, const float* state_in, int64_t n, int32_t hk, int32_t hv,
+                                int32_t dk, int32_t dv, float* out, float* state_out, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /*
  * ---- Upper decoder layer on the kept rows ----

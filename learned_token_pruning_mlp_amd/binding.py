@@ -31,7 +31,8 @@ EXPORTS = ("tg_status_string", "tg_abi_version", "tg_workspace_bytes", "tg_gate_
            "tg_gated_attention_timed",
            "tg_rmsnorm", "tg_swiglu", "tg_blas_create", "tg_blas_destroy", "tg_linear",
            "tg_attention_bwd_workspace_bytes", "tg_gated_attention_bwd", "tg_gate_score_bwd_workspace_bytes",
-           "tg_gate_score_bwd", "tg_gated_delta_rule")
+           "tg_gate_score_bwd", "tg_gated_delta_rule", "tg_gated_delta_rule_workspace_bytes",
+           "tg_gated_delta_rule_chunked")
 
 
 class TgGather(ctypes.Structure):
@@ -104,6 +105,10 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
     L.tg_gate_score_bwd.restype = ctypes.c_int
     L.tg_gated_delta_rule.argtypes = [P, P, P, P, P, P, I64, I32, I32, I32, I32, P, P, P]
     L.tg_gated_delta_rule.restype = ctypes.c_int
+    L.tg_gated_delta_rule_workspace_bytes.argtypes = [I64, I32]
+    L.tg_gated_delta_rule_workspace_bytes.restype = ctypes.c_size_t
+    L.tg_gated_delta_rule_chunked.argtypes = [P, P, P, P, P, P, I64, I32, I32, I32, I32, P, P, P, ctypes.c_size_t, P]
+    L.tg_gated_delta_rule_chunked.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -459,10 +464,7 @@ def tg_gate_score_bwd(handle: BlasHandle, resid: torch.Tensor, w1: torch.Tensor,
         _ptr(db2), _ptr(ws), ws.numel(), _stream(stream)))
 
 
-def tg_gated_delta_rule(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
-                        out: torch.Tensor, state_in: Optional[torch.Tensor] = None,
-                        state_out: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Gated delta rule over the token sequence (fp32 out and state)."""
+def _gdn_args(q, k, v, alpha, beta, out, state_in, state_out):
     n, hk, dk = q.shape
     hv, dv = v.shape[1], v.shape[2]
     _need(q, "q", torch.bfloat16, (n, hk, dk))
@@ -473,6 +475,33 @@ def tg_gated_delta_rule(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha
     _need(out, "out", torch.float32, (n, hv, dv))
     _need(state_in, "state_in", torch.float32, (hv, dv, dk), optional=True)
     _need(state_out, "state_out", torch.float32, (hv, dv, dk), optional=True)
+    return (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in), n, hk, hv, dk, dv, _ptr(out),
+            _ptr(state_out))
+
+
+def tg_gated_delta_rule(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
+                        out: torch.Tensor, state_in: Optional[torch.Tensor] = None,
+                        state_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Gated delta rule over the token sequence (fp32 out and state), as a scan."""
     _check("tg_gated_delta_rule", load().tg_gated_delta_rule(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in), n, hk, hv, dk, dv, _ptr(out),
-        _ptr(state_out), _stream(stream)))
+        *_gdn_args(q, k, v, alpha, beta, out, state_in, state_out), _stream(stream)))
+
+
+def tg_gated_delta_rule_workspace_bytes(n: int, hv: int) -> int:
+    return int(load().tg_gated_delta_rule_workspace_bytes(int(n), int(hv)))
+
+
+def gdn_workspace(n: int, hv: int, device=None) -> torch.Tensor:
+    """A workspace for tg_gated_delta_rule_chunked (uint8; no contents need clearing)."""
+    return torch.empty(tg_gated_delta_rule_workspace_bytes(n, hv), dtype=torch.uint8,
+                       device=device if device is not None else "cuda")
+
+
+def tg_gated_delta_rule_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+                                beta: torch.Tensor, out: torch.Tensor, ws: torch.Tensor,
+                                state_in: Optional[torch.Tensor] = None, state_out: Optional[torch.Tensor] = None,
+                                stream=None) -> None:
+    """The gated delta rule in chunks on the matrix cores (same results to rounding)."""
+    _need(ws, "ws", torch.uint8)
+    _check("tg_gated_delta_rule_chunked", load().tg_gated_delta_rule_chunked(
+        *_gdn_args(q, k, v, alpha, beta, out, state_in, state_out), _ptr(ws), ws.numel(), _stream(stream)))

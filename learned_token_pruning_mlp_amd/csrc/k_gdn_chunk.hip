@@ -1,0 +1,666 @@
+// k_gdn_chunk.hip -- the gated delta rule over the kept tokens in chunks on
+// the matrix cores, the chunks' state-independent transforms formed first by
+// a parallel pre-pass.
+//
+// The recurrent mixer of the hybrid backbone runs above the gate on the kept
+// tokens only (fluxbbs.com TokenGate article, section on the hybrid
+// architecture; aiwillknow.com, section on the two kinds of state in hybrid
+// models).  Its core is the gated delta rule (Yang, Kautz and Hatamizadeh,
+// "Gated Delta Networks", 2024): per v head, with S in R^{dv x dk},
+//   S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,  o_t = S_t q_t.
+// With w_t = beta_t (v_t - alpha_t S_{t-1} k_t) the rule reads
+// S_t = alpha_t S_{t-1} + w_t k_t^T, and over a chunk of C tokens from the
+// state S0, with R(t, i) = prod_{i<j<=t} alpha_j and gamma_t = prod_{j<=t}
+// alpha_j (the chunkwise WY / UT form of the same paper),
+//   (I + L) W = diag(beta) (V - diag(gamma) K S0^T),  L_ti = beta_t R(t,i) k_t.k_i  (i < t)
+//   O   = diag(gamma) Q S0^T + M W,                    M_ti = R(t,i) q_t.k_i        (i <= t)
+//   S_C = gamma_{C-1} S0 + W^T diag(R(C-1, .)) K.
+// Everything but the products with S0 and W is independent of the state:
+//  * gdn_prep, one workgroup per (v head, chunk), all chunks at once: the
+//    Gram products K K^T and Q K^T, the decay table, L, M and
+//    T = (I + L)^{-1} (16 x 16 diagonal blocks by forward substitution, then
+//    T10 = -T11 L10 T00); it writes T and M as the matrix-core operands of
+//    the two products that use them, already split, and gamma, beta and
+//    R(C-1, .), into one record of the workspace per (v head, chunk);
+//  * gdn_seq, one workgroup per 16 rows of a head's state, walks the chunks
+//    in order: K S0^T and Q S0^T (each of DK/32 waves owns a 32-column band
+//    of the rows, held in registers), U = diag(beta)(V - diag(gamma) K S0^T),
+//    W = T U, the outputs and the state update.  Each chunk's k, q and v rows
+//    and its record go through LDS by direct loads, two stages, the next
+//    chunk's in flight while this one is applied.
+// The products run on 16x16x32 bf16 MFMA with fp32 accumulation.  k, q and v
+// are bf16 already; every fp32 operand (the state, T, U, M, W) is split into
+// three bf16 parts (hi + mid + lo, each the nearest bf16 to what the ones
+// before it leave), a state product takes three MFMAs and an fp32 x fp32
+// product the six terms above 2^-24 (the bf16x3 scheme of Henry, Tang and
+// Heinecke, "Leveraging the bfloat16 Artificial Intelligence Datatype For
+// Higher-Precision Computations", 2019).  Tokens past the last take
+// alpha = 1, beta = 0 and zero rows, which leaves the state unchanged.
+// Deterministic.
+#include <hip/hip_runtime.h>
+
+#include "tg_device.h"
+#include "tg_internal.h"
+
+namespace {
+
+using tgd::f32x4;
+using tgd::u32x2;
+using tgd::u32x4;
+
+#define TG_LDS __attribute__((address_space(3)))
+typedef float lf4 __attribute__((ext_vector_type(4)));  // LDS-side float4
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+
+constexpr int kCC = 32;  // tokens per chunk
+constexpr int kRS = 16;  // state rows per workgroup of the sequential pass
+
+// One record per (v head, chunk), in bytes: the A operands of W = T U and of
+// M W (per 16-token row block tb, per part hi / mid / lo, per lane: 16 bytes),
+// then gamma, beta (0 past the last token) and R(C-1, i), 32 floats each.
+constexpr int kRecT = 0;
+constexpr int kRecM = 2 * 3 * 64 * 16;
+constexpr int kRecGam = 2 * kRecM;
+constexpr int kRecBet = kRecGam + kCC * 4;
+constexpr int kRecRl = kRecBet + kCC * 4;
+constexpr int kRecBytes = 16384;  // four 4 KB rounds of direct loads
+static_assert(kRecRl + kCC * 4 <= kRecBytes, "record layout");
+
+constexpr int kBufferWord3 = 0x00020000;
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Direct load of SIZE bytes per lane from base + voff into LDS at
+// lds + SIZE * lane (lds wave-uniform), through a raw buffer resource over
+// `bytes` bytes (offsets at or past the end read as zero).  Issued from
+// inline assembly so the compiler does not track these LDS writes: it would
+// otherwise make the reads of one stage (and other LDS writes) wait for the
+// loads in flight into the other.  The instruction writes no register; the
+// kernels order it with explicit vector-memory waits and barriers written as
+// inline assembly with a memory clobber.  (m0 is set right before each use.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <int SIZE>
+__device__ __forceinline__ void lds_load(const void* base, uint32_t bytes, TG_LDS uint8_t* lds, uint32_t voff) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    const i32x4 rs = i32x4{(int32_t)(uint32_t)a, (int32_t)((uint32_t)(a >> 32) & 0xffffu), (int32_t)bytes,
+                           kBufferWord3};
+    const uint32_t m = (uint32_t)(uintptr_t)lds;
+    if constexpr (SIZE == 16)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :
+                     : "s"(m), "v"(voff), "s"(rs)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                     :
+                     : "s"(m), "v"(voff), "s"(rs)
+                     : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+#define TG_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+
+// Workgroup barrier that waits only for this wave's LDS accesses (the phases
+// of a chunk talk through LDS): the next chunk's loads and this chunk's
+// output stores stay in flight across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(tgd::as_bf16x8(a), tgd::as_bf16x8(b), c, 0, 0, 0);
+}
+
+// eight fp32 values into three packed bf16 parts: x = hi + mid + lo
+__device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& mid, u32x4& lo) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t h = tgd::cvt_pk_bf16(x[2 * p], x[2 * p + 1]);
+        const float r0 = x[2 * p] - tgd::bf16lo(h), r1 = x[2 * p + 1] - tgd::bf16hi(h);
+        const uint32_t m = tgd::cvt_pk_bf16(r0, r1);
+        const uint32_t l = tgd::cvt_pk_bf16(r0 - tgd::bf16lo(m), r1 - tgd::bf16hi(m));
+        hi[p] = h, mid[p] = m, lo[p] = l;
+    }
+}
+
+// fp32 x fp32 product of 8-wide operands on a 16x16x32 tile, the A operand
+// already split: the six cross terms above 2^-24, smallest first
+__device__ __forceinline__ f32x4 mfma16_x6s(u32x4 ah, u32x4 am, u32x4 al, const float* b, f32x4 acc) {
+    u32x4 bh, bm, bl;
+    split8(b, bh, bm, bl);
+    acc = mfma16(am, bm, acc);
+    acc = mfma16(al, bh, acc);
+    acc = mfma16(ah, bl, acc);
+    acc = mfma16(am, bh, acc);
+    acc = mfma16(ah, bm, acc);
+    return mfma16(ah, bh, acc);
+}
+
+__device__ __forceinline__ f32x4 mfma16_x6(const float* a, const float* b, f32x4 acc) {
+    u32x4 ah, am, al;
+    split8(a, ah, am, al);
+    return mfma16_x6s(ah, am, al, b, acc);
+}
+
+// k and q rows of a chunk in LDS: the 16-byte pieces of row t at slot
+// t * NP + (piece ^ t % NP), so the rows a tile's lanes read hit distinct banks.
+template <int DK>
+struct Rows {
+    static constexpr int NP = DK / 8;
+    static constexpr int KQ = kCC * DK * 2;  // bytes of the chunk's k (or q) rows
+    static_assert(KQ % 4096 == 0, "k/q chunk in whole rounds of direct loads");
+    __device__ static int boff(int row, int col) { return 16 * (row * NP + ((col >> 3) ^ (row % NP))) + 2 * (col & 7); }
+    // k and q rows of tokens t0 .. t0 + kCC - 1 of q/k head hq into kb, qb
+    __device__ static void issue(const uint16_t* k, const uint16_t* q, uint32_t qk_bytes, int64_t t0, int hk, int hq,
+                                 TG_LDS uint8_t* kb, TG_LDS uint8_t* qb) {
+        const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+#pragma unroll
+        for (int it = 0; it < KQ / 4096; ++it) {
+            const int e = it * 256 + tid;  // piece slot
+            const int t = e / NP, p = (e % NP) ^ (t % NP);
+            const uint32_t go = ((uint32_t)(t0 + t) * (uint32_t)hk + (uint32_t)hq) * (DK * 2u) + 16u * p;
+            lds_load<16>(k, qk_bytes, kb + it * 4096 + w * 1024, go);
+            lds_load<16>(q, qk_bytes, qb + it * 4096 + w * 1024, go);
+        }
+    }
+    // 16-byte operand piece of k-step s (32 columns) for this lane's k-group
+    __device__ static u32x4 rowop(const TG_LDS uint8_t* base, int row, int s, int g4) {
+        return *(const TG_LDS u32x4*)(base + boff(row, 32 * s + 8 * g4));
+    }
+};
+
+// ---- the pre-pass: one workgroup (4 waves) per (v head, chunk)
+template <int DK>
+__global__ __launch_bounds__(256) void gdn_prep(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                const float* __restrict__ alpha, const float* __restrict__ beta,
+                                                int64_t n, int hk, int hv, int64_t nch, uint8_t* __restrict__ rec) {
+    using RW = Rows<DK>;
+    __shared__ __attribute__((aligned(1024))) uint8_t stg[2 * RW::KQ + 2 * kCC * 4];
+    __shared__ __attribute__((aligned(16))) float gkk[kCC][36];  // k_t . k_i
+    __shared__ __attribute__((aligned(16))) float gqk[kCC][36];  // q_t . k_i
+    __shared__ __attribute__((aligned(16))) float lm[kCC][36];   // L
+    __shared__ __attribute__((aligned(16))) float mm[kCC][36];   // M
+    __shared__ __attribute__((aligned(16))) float tm[kCC][36];   // T = (I + L)^{-1}
+    __shared__ __attribute__((aligned(16))) float xx[16][20];    // L10 T00
+    __shared__ __attribute__((aligned(16))) float gam[kCC], bet[kCC], rl[kCC];
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int i16 = lane & 15, g4 = lane >> 4;
+    const int h = (int)(blockIdx.x / nch);
+    const int64_t ch = blockIdx.x % nch;
+    const int hq = h / (hv / hk);
+    const int64_t t0 = ch * kCC;
+    const int tn = n - t0 < kCC ? (int)(n - t0) : kCC;
+    TG_LDS uint8_t* kb = (TG_LDS uint8_t*)stg;
+    TG_LDS uint8_t* qb = kb + RW::KQ;
+    TG_LDS float* ab = (TG_LDS float*)(kb + 2 * RW::KQ);
+    TG_LDS float* bb = ab + kCC;
+
+    RW::issue(k, q, (uint32_t)n * (uint32_t)hk * DK * 2u, t0, hk, hq, kb, qb);
+    if (w == 0 && lane < kCC) {
+        const uint32_t g_bytes = (uint32_t)n * (uint32_t)hv * 4u;
+        const uint32_t go = ((uint32_t)(t0 + lane) * (uint32_t)hv + (uint32_t)h) * 4u;
+        lds_load<4>(alpha, g_bytes, (TG_LDS uint8_t*)ab, go);
+        lds_load<4>(beta, g_bytes, (TG_LDS uint8_t*)bb, go);
+    }
+    TG_WAIT_VMCNT(0);
+    lds_barrier();
+
+    // Gram products, two 16 x 16 tiles a wave: K K^T blocks (0,0), (1,0),
+    // (1,1), then Q K^T's (the blocks L and M need)
+    if (w < 3) {
+        const int ga = 2 * w, gb = 2 * w + 1;
+        const int ra0 = ga % 3 == 0 ? 0 : 1, rb0 = ga % 3 == 2 ? 1 : 0;
+        const int ra1 = gb % 3 == 0 ? 0 : 1, rb1 = gb % 3 == 2 ? 1 : 0;
+        const TG_LDS uint8_t* xa = ga >= 3 ? qb : kb;
+        const TG_LDS uint8_t* xg = gb >= 3 ? qb : kb;
+        f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int sk = 0; sk < DK / 32; ++sk) {
+            acc0 = mfma16(RW::rowop(xa, 16 * ra0 + i16, sk, g4), RW::rowop(kb, 16 * rb0 + i16, sk, g4), acc0);
+            acc1 = mfma16(RW::rowop(xg, 16 * ra1 + i16, sk, g4), RW::rowop(kb, 16 * rb1 + i16, sk, g4), acc1);
+        }
+        float(*g0)[36] = ga >= 3 ? gqk : gkk;
+        float(*g1)[36] = gb >= 3 ? gqk : gkk;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            g0[16 * ra0 + 4 * g4 + j][16 * rb0 + i16] = acc0[j];
+            g1[16 * ra1 + 4 * g4 + j][16 * rb1 + i16] = acc1[j];
+        }
+    }
+    // decay table, a row quad a thread: R(t, i) = alpha_t alpha_{t-1} ...
+    // alpha_{i+1} (1 at i = t, 0 above); gates past the last token are
+    // alpha = 1, beta = 0.  Thread (t, c4) forms R(t, c4 + 3) from t down,
+    // then the three below it.
+    const int rt_t = tid >> 3, rt_c = 4 * (tid & 7);
+    float rq[4];
+    {
+        float al[kCC];
+#pragma unroll
+        for (int m4 = 0; m4 < kCC / 4; ++m4) {
+            const lf4 a4 = *(const TG_LDS lf4*)(ab + 4 * m4);
+            al[4 * m4] = a4.x, al[4 * m4 + 1] = a4.y, al[4 * m4 + 2] = a4.z, al[4 * m4 + 3] = a4.w;
+        }
+#pragma unroll
+        for (int i = 0; i < kCC; ++i) al[i] = i < tn ? al[i] : 1.0f;
+        float acc = 1.0f;
+#pragma unroll
+        for (int jj = kCC - 1; jj >= 4; --jj)
+            if (jj <= rt_t && jj > rt_c + 3) acc *= al[jj];
+        // acc = R(t, c4 + 3) when c4 + 3 < t (and is 1 otherwise)
+#pragma unroll
+        for (int e = 3; e >= 0; --e) {
+            const int i = rt_c + e;
+            rq[e] = i <= rt_t ? acc : 0.0f;
+            if (i >= 1 && i <= rt_t) acc *= al[i];  // R(t, i - 1) = R(t, i) alpha_i
+        }
+        if (rt_t == kCC - 1) *(float4*)&rl[rt_c] = float4{rq[0], rq[1], rq[2], rq[3]};
+        if (rt_c == 0) {
+            gam[rt_t] = rq[0] * al[0];
+            bet[rt_t] = rt_t < tn ? bb[rt_t] : 0.0f;
+        }
+    }
+    __syncthreads();
+
+    // L and M, a row quad a thread
+    {
+        const int t = rt_t, c4 = rt_c;
+        const float4 k4 = *(const float4*)&gkk[t][c4];
+        const float4 q4 = *(const float4*)&gqk[t][c4];
+        const float bt = bet[t];
+        float4 l4, m4;
+        l4.x = c4 + 0 < t ? bt * rq[0] * k4.x : 0.0f;
+        l4.y = c4 + 1 < t ? bt * rq[1] * k4.y : 0.0f;
+        l4.z = c4 + 2 < t ? bt * rq[2] * k4.z : 0.0f;
+        l4.w = c4 + 3 < t ? bt * rq[3] * k4.w : 0.0f;
+        m4.x = c4 + 0 <= t ? rq[0] * q4.x : 0.0f;
+        m4.y = c4 + 1 <= t ? rq[1] * q4.y : 0.0f;
+        m4.z = c4 + 2 <= t ? rq[2] * q4.z : 0.0f;
+        m4.w = c4 + 3 <= t ? rq[3] * q4.w : 0.0f;
+        *(float4*)&lm[t][c4] = l4;
+        *(float4*)&mm[t][c4] = m4;
+    }
+    __syncthreads();
+
+    // T = (I + L)^{-1}: the diagonal 16 x 16 blocks by forward substitution
+    // (wave 0: T00, wave 1: T11; lane (p, j) = (lane / 16, lane % 16) keeps
+    // rows 4 p .. 4 p + 3 of column j and sums that slice of each row's dot
+    // product, the four slices added by two lane swaps, which leave the same
+    // bits in all four lanes), then T10 = -T11 (L10 T00) on the matrix cores
+    if (w < 2) {
+        const int o = 16 * w, j = i16, pp = g4;
+        lf4 lrow[16];
+#pragma unroll
+        for (int u = 1; u < 16; ++u) lrow[u] = *(const lf4*)&lm[o + u][o + 4 * pp];
+        float cbk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cbk[e] = 4 * pp + e == j ? 1.0f : 0.0f;
+#pragma unroll
+        for (int u = 1; u < 16; ++u) {
+            float part = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) part = fmaf(4 * pp + e < u ? lrow[u][e] : 0.0f, cbk[e], part);
+            const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+            float sum = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+            const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum), __float_as_uint(sum), false, false);
+            sum = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+            const float val = u > j ? -sum : (u == j ? 1.0f : 0.0f);
+            if (pp == (u >> 2)) cbk[u & 3] = val;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            tm[o + 4 * pp + e][o + j] = cbk[e];
+            if (w == 0) tm[4 * pp + e][16 + j] = 0.0f;  // T01 = 0
+        }
+    }
+    __syncthreads();
+    if (w == 0) {
+        // X = L10 T00 (k = 0..15; k-groups 2 and 3 are zero)
+        float a8[8], b8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            a8[e] = g4 < 2 ? lm[16 + i16][8 * g4 + e] : 0.0f;
+            b8[e] = g4 < 2 ? tm[8 * g4 + e][i16] : 0.0f;
+        }
+        f32x4 x = mfma16_x6(a8, b8, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) xx[4 * g4 + jj][i16] = x[jj];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        // T10 = -T11 X
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            a8[e] = g4 < 2 ? tm[16 + i16][16 + 8 * g4 + e] : 0.0f;
+            b8[e] = g4 < 2 ? xx[8 * g4 + e][i16] : 0.0f;
+        }
+        x = mfma16_x6(a8, b8, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) tm[16 + 4 * g4 + jj][i16] = -x[jj];
+    }
+    __syncthreads();
+
+    // The record: waves 0, 1 split T's 16-token row block w, waves 2, 3 M's
+    // block w - 2, as the A operands (row 16 tb + i16, k = 8 g4 .. 8 g4 + 7)
+    uint8_t* r = rec + ((int64_t)h * nch + ch) * kRecBytes;
+    {
+        const int tb = w & 1;
+        float(*src)[36] = w < 2 ? tm : mm;
+        float a8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a8[e] = src[16 * tb + i16][8 * g4 + e];
+        u32x4 parts[3];
+        split8(a8, parts[0], parts[1], parts[2]);
+        uint8_t* dst = r + (w < 2 ? kRecT : kRecM);
+#pragma unroll
+        for (int p = 0; p < 3; ++p) *reinterpret_cast<u32x4*>(dst + ((tb * 3 + p) * 64 + lane) * 16) = parts[p];
+    }
+    if (tid < kCC) {
+        reinterpret_cast<float*>(r + kRecGam)[tid] = gam[tid];
+        reinterpret_cast<float*>(r + kRecBet)[tid] = bet[tid];
+        reinterpret_cast<float*>(r + kRecRl)[tid] = rl[tid];
+    }
+}
+
+// ---- the sequential pass: one workgroup (4 waves) per kRS rows of a head's state
+template <int DK, int DV>
+struct Seq {
+    static constexpr int DW = DK / 32;           // waves that own a 32-column band of the state
+    static constexpr int VB = kCC * kRS * 2;     // bytes of the workgroup's v values of a chunk
+    static constexpr int STAGE = 2 * Rows<DK>::KQ + VB + kRecBytes;
+    static_assert(VB == 1024, "v chunk in one 4-byte load per thread");
+    static_assert(DV % kRS == 0 && DW >= 1 && DW <= 4, "state slices");
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void gdn_seq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                               const uint16_t* __restrict__ v, const float* state_in, int64_t n,
+                                               int hk, int hv, int64_t nch, const uint8_t* __restrict__ rec,
+                                               float* __restrict__ out,
+                                               float* state_out) {  // state_out may be state_in
+    using RW = Rows<DK>;
+    using C = Seq<DK, DV>;
+    constexpr int DW = C::DW, KQ = RW::KQ;
+    // one LDS object per stage, so the compiler can see that reads of one
+    // stage never alias the loads in flight into the other
+    __shared__ __attribute__((aligned(1024))) uint8_t stg0[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t stg1[C::STAGE];
+    __shared__ __attribute__((aligned(16))) float ppk[DW][kCC][20];     // per band: K S0^T
+    __shared__ __attribute__((aligned(16))) float ppq[2][DW][kCC][20];  // per band: Q S0^T, by chunk parity
+    __shared__ __attribute__((aligned(16))) float uu[kCC][20];           // U
+    __shared__ __attribute__((aligned(16))) float ww[2][kCC][20];        // W, by chunk parity
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int i16 = lane & 15, g4 = lane >> 4;
+    const int h = blockIdx.x / (DV / kRS), r0 = (blockIdx.x % (DV / kRS)) * kRS;
+    const int hq = h / (hv / hk);
+    const uint32_t qk_bytes = (uint32_t)n * (uint32_t)hk * DK * 2u;
+    const uint32_t v_bytes = (uint32_t)n * (uint32_t)hv * DV * 2u;
+
+    // A chunk's k and q rows, the workgroup's v values and the record, issued
+    // by waves 2 and 3 alone (128 threads: tg = tid - 128), in phases where
+    // they would otherwise wait: a wave that finds the memory queue full
+    // stalls at the issue, which must not fall on the state's chain.
+    constexpr int NP = RW::NP;
+    auto issue = [&](int64_t ch, TG_LDS uint8_t* __restrict__ sb) {
+        const int64_t t0 = ch * kCC;
+        const int tg = tid - 128, wg = w - 2;
+#pragma unroll
+        for (int it = 0; it < KQ / (16 * 128); ++it) {
+            const int e = it * 128 + tg;  // piece slot
+            const int t = e / NP, p = (e % NP) ^ (t % NP);
+            const uint32_t go = ((uint32_t)(t0 + t) * (uint32_t)hk + (uint32_t)hq) * (DK * 2u) + 16u * p;
+            lds_load<16>(k, qk_bytes, sb + 16 * (it * 128 + wg * 64), go);
+            lds_load<16>(q, qk_bytes, sb + KQ + 16 * (it * 128 + wg * 64), go);
+        }
+#pragma unroll
+        for (int it = 0; it < C::VB / (4 * 128); ++it) {
+            const int e = it * 128 + tg, t = e >> 3, wd = e & 7;
+            const uint32_t go = ((uint32_t)(t0 + t) * (uint32_t)hv + (uint32_t)h) * (DV * 2u) + r0 * 2u + 4u * wd;
+            lds_load<4>(v, v_bytes, sb + 2 * KQ + 4 * (it * 128 + wg * 64), go);
+        }
+        const uint8_t* r = rec + ((int64_t)h * nch + ch) * kRecBytes;
+#pragma unroll
+        for (int it = 0; it < kRecBytes / (16 * 128); ++it)
+            lds_load<16>(r, kRecBytes, sb + 2 * KQ + C::VB + 16 * (it * 128 + wg * 64), 16u * (it * 128 + tg));
+    };
+
+    // The state: wave w < DW owns columns 32 w .. 32 w + 31 of the slice's
+    // rows, held transposed (lane: row i16, columns 32 w + 16 u + 4 g4 + j,
+    // u = 0, 1, j = 0..3), and, as the B operand of the chunk's products,
+    // split into three bf16 parts (k-group g4 of the band's 32 columns takes
+    // columns 4 g4 .. +3 and 16 + 4 g4 .. +3).
+    const bool owner = w < DW;
+    const int c0 = 32 * w;
+    float sr[2][4];
+    u32x4 sh, sm, sl;
+    if (owner) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            float4 x = float4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (state_in) x = *(const float4*)&state_in[((int64_t)h * DV + r0 + i16) * DK + c0 + 16 * u + 4 * g4];
+            sr[u][0] = x.x, sr[u][1] = x.y, sr[u][2] = x.z, sr[u][3] = x.w;
+        }
+        const float x8[8] = {sr[0][0], sr[0][1], sr[0][2], sr[0][3], sr[1][0], sr[1][1], sr[1][2], sr[1][3]};
+        split8(x8, sh, sm, sl);
+    }
+
+    // The outputs of chunk cc, O = diag(gamma) Q S0^T + M W (waves 2, 3: one
+    // 16-token block each).  They are formed one chunk late, while waves 0 and
+    // 1 form the next chunk's W: nothing later needs them, so they stay off
+    // the state's chain.  M's operands and gamma are taken from cc's stage
+    // into registers first (the stage is then refilled), its Q partials and W
+    // are kept by chunk parity.
+    struct OutOps {
+        u32x4 mh, mm, ml;
+        float gm[4];
+    };
+    auto out_ops = [&](const TG_LDS uint8_t* __restrict__ stage) {
+        const int tb = w - 2;
+        const TG_LDS uint8_t* rbc = stage + 2 * KQ + C::VB;
+        const TG_LDS u32x4* mp = (const TG_LDS u32x4*)(rbc + kRecM) + tb * 3 * 64 + lane;
+        const TG_LDS float* gamc = (const TG_LDS float*)(rbc + kRecGam);
+        OutOps o;
+        o.mh = mp[0], o.mm = mp[64], o.ml = mp[128];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o.gm[j] = gamc[16 * tb + 4 * g4 + j];
+        return o;
+    };
+    auto outputs = [&](int64_t cc, const OutOps& o) {
+        const int tb = w - 2;
+        const int64_t tc = cc * kCC;
+        const int tnc = n - tc < kCC ? (int)(n - tc) : kCC;
+        const int par = (int)(cc & 1);
+        f32x4 acc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = 16 * tb + 4 * g4 + j;
+            float p = ppq[par][0][t][i16];
+#pragma unroll
+            for (int b = 1; b < DW; ++b) p += ppq[par][b][t][i16];
+            acc[j] = o.gm[j] * p;
+        }
+        float b8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) b8[e] = ww[par][8 * g4 + e][i16];
+        acc = mfma16_x6s(o.mh, o.mm, o.ml, b8, acc);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = 16 * tb + 4 * g4 + j;
+            if (t < tnc) out[((tc + t) * hv + h) * DV + r0 + i16] = acc[j];
+        }
+    };
+
+    auto chunk = [&](int64_t ch, const TG_LDS uint8_t* __restrict__ cb, TG_LDS uint8_t* __restrict__ nb) {
+        TG_WAIT_VMCNT(0);  // this thread's loads of the chunk have landed (and its stores are done)
+        lds_barrier();     // ... every thread's; every wave is done with the other stage
+        const TG_LDS uint8_t* kb = cb;
+        const TG_LDS uint8_t* qb = cb + KQ;
+        const TG_LDS uint16_t* vb = (const TG_LDS uint16_t*)(cb + 2 * KQ);
+        const TG_LDS uint8_t* rb = cb + 2 * KQ + C::VB;
+        const TG_LDS float* gam = (const TG_LDS float*)(rb + kRecGam);
+        const TG_LDS float* bet = (const TG_LDS float*)(rb + kRecBet);
+        const TG_LDS float* rl = (const TG_LDS float*)(rb + kRecRl);
+
+        // ---- A. band partials of K S0^T and Q S0^T
+        if (owner) {
+            u32x4 a[4];  // K rows 0-15, 16-31, then Q's: this lane's row, the band's k-group columns
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const TG_LDS uint8_t* xb = x < 2 ? kb : qb;
+                const int t = 16 * (x & 1) + i16;
+                a[x] = u32x4{*(const TG_LDS uint32_t*)(xb + RW::boff(t, c0 + 4 * g4)),
+                             *(const TG_LDS uint32_t*)(xb + RW::boff(t, c0 + 4 * g4 + 2)),
+                             *(const TG_LDS uint32_t*)(xb + RW::boff(t, c0 + 16 + 4 * g4)),
+                             *(const TG_LDS uint32_t*)(xb + RW::boff(t, c0 + 16 + 4 * g4 + 2))};
+            }
+            f32x4 acc[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) acc[x] = mfma16(a[x], sl, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+            for (int x = 0; x < 4; ++x) acc[x] = mfma16(a[x], sm, acc[x]);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) acc[x] = mfma16(a[x], sh, acc[x]);
+            const int pq = (int)(ch & 1);
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int t = 16 * (x & 1) + 4 * g4 + j;
+                    if (x < 2)
+                        ppk[w][t][i16] = acc[x][j];
+                    else
+                        ppq[pq][w][t][i16] = acc[x][j];
+                }
+        }
+        lds_barrier();
+
+        // ---- B. U = diag(beta)(V - diag(gamma) K S0^T) (waves 0, 1); waves 2, 3
+        // take the previous chunk's output operands from its stage, then load
+        // the next chunk into that stage
+        static_assert(kCC * kRS / 4 == 128, "U in waves 0 and 1");
+        OutOps prev;
+        if (w >= 2) {
+            if (ch > 0) prev = out_ops(nb);
+            if (ch + 1 < nch) {
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // its reads of that stage are done
+                issue(ch + 1, nb);
+            }
+        } else {
+            const int t = tid >> 2, r4 = 4 * (tid & 3);
+            float4 p = *(const float4*)&ppk[0][t][r4];
+#pragma unroll
+            for (int b = 1; b < DW; ++b) {
+                const float4 y = *(const float4*)&ppk[b][t][r4];
+                p.x += y.x, p.y += y.y, p.z += y.z, p.w += y.w;
+            }
+            const u32x2 vw = *(const TG_LDS u32x2*)(vb + t * kRS + r4);
+            const float bt = bet[t], gm = gam[t];
+            float4 u;
+            u.x = bt * (tgd::bf16lo(vw[0]) - gm * p.x);
+            u.y = bt * (tgd::bf16hi(vw[0]) - gm * p.y);
+            u.z = bt * (tgd::bf16lo(vw[1]) - gm * p.z);
+            u.w = bt * (tgd::bf16hi(vw[1]) - gm * p.w);
+            *(float4*)&uu[t][r4] = u;
+        }
+        lds_barrier();
+
+        // ---- C. W = T U (waves 0, 1: one 16-token block each; T's parts from
+        // the record); waves 2, 3 form the previous chunk's outputs
+        const int par = (int)(ch & 1);
+        if (w >= 2) {
+            if (ch > 0) outputs(ch - 1, prev);
+        } else {
+            const int tb = w;
+            const TG_LDS u32x4* tp = (const TG_LDS u32x4*)(rb + kRecT) + tb * 3 * 64 + lane;
+            float b8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) b8[e] = uu[8 * g4 + e][i16];
+            const f32x4 acc = mfma16_x6s(tp[0], tp[64], tp[128], b8, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ww[par][16 * tb + 4 * g4 + j][i16] = acc[j];
+        }
+        lds_barrier();
+
+        // ---- D. each band's state update S^T <- gamma_last S^T + K^T diag(R(C-1, .)) W
+        if (owner) {
+            float b8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) b8[e] = rl[8 * g4 + e] * ww[par][8 * g4 + e][i16];
+            u32x4 bh, bm, bl;
+            split8(b8, bh, bm, bl);
+            const float gl = gam[kCC - 1];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                // A = K^T rows c0 + 16 u + i16, k = tokens 8 g4 .. +7 (two
+                // transposing reads: lane jj of a 16-lane group addresses
+                // token 8 g4 + 4 hh + jj / 4, columns 4 (jj % 4) .. +3)
+                u32x4 a;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int t = 8 * g4 + 4 * hh + (i16 >> 2);
+                    const bf16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (TG_LDS bf16x4_t*)(kb + RW::boff(t, c0 + 16 * u + 4 * (i16 & 3))));
+                    const u32x2 xw = __builtin_bit_cast(u32x2, x);
+                    a[2 * hh] = xw[0], a[2 * hh + 1] = xw[1];
+                }
+                f32x4 acc = {gl * sr[u][0], gl * sr[u][1], gl * sr[u][2], gl * sr[u][3]};
+                acc = mfma16(a, bl, acc);
+                acc = mfma16(a, bm, acc);
+                acc = mfma16(a, bh, acc);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sr[u][j] = acc[j];
+            }
+            const float x8[8] = {sr[0][0], sr[0][1], sr[0][2], sr[0][3], sr[1][0], sr[1][1], sr[1][2], sr[1][3]};
+            split8(x8, sh, sm, sl);
+        }
+    };
+    TG_LDS uint8_t* s0 = (TG_LDS uint8_t*)stg0;
+    TG_LDS uint8_t* s1 = (TG_LDS uint8_t*)stg1;
+    if (nch > 0 && w >= 2) issue(0, s0);
+    for (int64_t ch = 0; ch < nch; ch += 2) {
+        chunk(ch, s0, s1);
+        if (ch + 1 < nch) chunk(ch + 1, s1, s0);
+    }
+    if (nch > 0 && w >= 2) outputs(nch - 1, out_ops((nch - 1) & 1 ? s1 : s0));  // the last chunk's
+    if (owner && state_out) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            *(float4*)&state_out[((int64_t)h * DV + r0 + i16) * DK + c0 + 16 * u + 4 * g4] =
+                float4{sr[u][0], sr[u][1], sr[u][2], sr[u][3]};
+    }
+}
+
+template <int DK, int DV>
+int launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* alpha, const float* beta,
+           const float* state_in, int64_t n, int hk, int hv, float* out, float* state_out, uint8_t* rec,
+           hipStream_t s) {
+    const int64_t nch = (n + kCC - 1) / kCC;
+    if (nch > 0)
+        hipLaunchKernelGGL(gdn_prep<DK>, dim3((unsigned)(hv * nch)), dim3(256), 0, s, q, k, alpha, beta, n, hk, hv,
+                           nch, rec);
+    hipLaunchKernelGGL((gdn_seq<DK, DV>), dim3((unsigned)(hv * (DV / kRS))), dim3(256), 0, s, q, k, v, state_in, n,
+                       hk, hv, nch, rec, out, state_out);
+    return hipGetLastError() == hipSuccess ? TG_OK : TG_EDEVICE;
+}
+
+}  // namespace
+
+namespace tgi {
+
+size_t gdn_chunk_ws_bytes(int64_t n, int hv) {
+    const int64_t nch = (n + kCC - 1) / kCC;
+    return (size_t)(nch > 0 ? nch : 1) * (size_t)hv * kRecBytes;
+}
+
+int launch_gated_delta_rule_chunked(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* alpha,
+                                    const float* beta, const float* state_in, int64_t n, int hk, int hv, int dk,
+                                    int dv, float* out, float* state_out, void* ws, void* stream) {
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t* rec = static_cast<uint8_t*>(ws);
+    if (dk == 128 && dv == 128) return launch<128, 128>(q, k, v, alpha, beta, state_in, n, hk, hv, out, state_out, rec, s);
+    if (dk == 128 && dv == 64) return launch<128, 64>(q, k, v, alpha, beta, state_in, n, hk, hv, out, state_out, rec, s);
+    if (dk == 64 && dv == 128) return launch<64, 128>(q, k, v, alpha, beta, state_in, n, hk, hv, out, state_out, rec, s);
+    if (dk == 64 && dv == 64) return launch<64, 64>(q, k, v, alpha, beta, state_in, n, hk, hv, out, state_out, rec, s);
+    return TG_EUNSUPPORTED;
+}
+
+}  // namespace tgi

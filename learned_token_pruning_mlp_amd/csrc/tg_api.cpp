@@ -243,19 +243,47 @@ int tg_gate_score_bwd(void* blas, const tg_bf16* resid, const tg_bf16* w1, const
                                       kept_idx, k, dresid, dw1, db1, dw2, db2, workspace, stream);
 }
 
-int tg_gated_delta_rule(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, const float* alpha, const float* beta,
-                        const float* state_in, int64_t n, int32_t hk, int32_t hv, int32_t dk, int32_t dv, float* out,
-                        float* state_out, void* stream) {
+// The checks shared by both forms of the gated delta rule; 1 = nothing to do.
+static int gdn_checks(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, const float* alpha, const float* beta,
+                      const float* state_in, int64_t n, int32_t hk, int32_t hv, int32_t dk, int32_t dv,
+                      const float* out, const float* state_out) {
     if (n < 0 || n > kMaxRows || hk < 1 || hv < 1 || hv % hk != 0) return TG_EINVAL;
     if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return TG_EUNSUPPORTED;
     // (token rows are read through 32-bit buffer offsets)
     if (n * (int64_t)hk * dk * 2 >= (int64_t)1 << 31 || n * (int64_t)hv * dv * 2 >= (int64_t)1 << 31)
         return TG_EUNSUPPORTED;
-    if (n == 0 && !state_out) return TG_OK;
+    if (n == 0 && !state_out) return 1;
     if (n > 0 && (!q || !k || !v || !alpha || !beta || !out)) return TG_EINVAL;
     if ((n > 0 && (!aligned(q, 16) || !aligned(k, 16))) || !aligned(state_in, 16) || !aligned(state_out, 16))
         return TG_EALIGN;
+    return TG_OK;
+}
+
+int tg_gated_delta_rule(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, const float* alpha, const float* beta,
+                        const float* state_in, int64_t n, int32_t hk, int32_t hv, int32_t dk, int32_t dv, float* out,
+                        float* state_out, void* stream) {
+    const int rc = gdn_checks(q, k, v, alpha, beta, state_in, n, hk, hv, dk, dv, out, state_out);
+    if (rc != TG_OK) return rc == 1 ? TG_OK : rc;
     return tgi::launch_gated_delta_rule(q, k, v, alpha, beta, state_in, n, hk, hv, dk, dv, out, state_out, stream);
+}
+
+size_t tg_gated_delta_rule_workspace_bytes(int64_t n, int32_t hv) {
+    if (n < 0 || hv < 1) return 0;
+    return tgi::gdn_chunk_ws_bytes(n, hv);
+}
+
+int tg_gated_delta_rule_chunked(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, const float* alpha,
+                                const float* beta, const float* state_in, int64_t n, int32_t hk, int32_t hv,
+                                int32_t dk, int32_t dv, float* out, float* state_out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    const int rc = gdn_checks(q, k, v, alpha, beta, state_in, n, hk, hv, dk, dv, out, state_out);
+    if (rc != TG_OK) return rc == 1 ? TG_OK : rc;
+    if (n > 0) {
+        if (!workspace || workspace_bytes < tgi::gdn_chunk_ws_bytes(n, hv)) return TG_EWORKSPACE;
+        if (!aligned(workspace, 16)) return TG_EALIGN;
+    }
+    return tgi::launch_gated_delta_rule_chunked(q, k, v, alpha, beta, state_in, n, hk, hv, dk, dv, out, state_out,
+                                                workspace, stream);
 }
 
 int tg_rmsnorm(const tg_bf16* x, const tg_bf16* weight, tg_bf16* y, int64_t rows, int32_t dim, float eps,

@@ -263,6 +263,14 @@ int launch_gated_delta_rule(const uint16_t* q, const uint16_t* k, const uint16_t
                             const float* beta, const float* state_in, int64_t n, int hk, int hv, int dk, int dv,
                             float* out, float* state_out, void* stream);
 
+// The chunked form: a pre-pass writes each (v head, chunk of 32 tokens)'s
+// state-independent transform into a 16 KB record of ws, then the state walks
+// the chunks (gdn_chunk_ws_bytes(n, hv) bytes of workspace).
+size_t gdn_chunk_ws_bytes(int64_t n, int hv);
+int launch_gated_delta_rule_chunked(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* alpha,
+                                    const float* beta, const float* state_in, int64_t n, int hk, int hv, int dk,
+                                    int dv, float* out, float* state_out, void* ws, void* stream);
+
 int launch_rmsnorm(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t rows, int dim, float eps,
                    void* stream);
 

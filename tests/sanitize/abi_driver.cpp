@@ -92,6 +92,13 @@ int main() {
     // recurrent mixer
     EXPECT(tg_gated_delta_rule(A, A, A, F, F, nullptr, 16, 2, 4, 64, 64, F, F, nullptr), R);
     EXPECT(tg_gated_delta_rule(A, A, A, F, F, nullptr, 16, 2, 3, 64, 64, F, F, nullptr), TG_EINVAL);
+    {
+        const size_t gw = tg_gated_delta_rule_workspace_bytes(16, 4);
+        EXPECT(tg_gated_delta_rule_chunked(A, A, A, F, F, nullptr, 16, 2, 4, 64, 64, F, F, W, gw, nullptr), R);
+        EXPECT(tg_gated_delta_rule_chunked(A, A, A, F, F, nullptr, 16, 2, 4, 64, 64, F, F, W, gw - 1, nullptr),
+               TG_EWORKSPACE);
+        EXPECT(tg_gated_delta_rule_chunked(A, A, A, F, F, nullptr, 16, 2, 3, 64, 64, F, F, W, gw, nullptr), TG_EINVAL);
+    }
     // layer pieces
     EXPECT(tg_rmsnorm(A, A, A, 4, 128, 1e-6f, nullptr), R);
     EXPECT(tg_rmsnorm(A, A, A, 4, 7, 1e-6f, nullptr), TG_EINVAL);

@@ -34,6 +34,11 @@ int launch_gate_score_bwd(void*, const uint16_t*, const uint16_t*, const uint16_
                           float*, float*, void*, void*) { return kReached; }
 int launch_gated_delta_rule(const uint16_t*, const uint16_t*, const uint16_t*, const float*, const float*,
                             const float*, int64_t, int, int, int, int, float*, float*, void*) { return kReached; }
+size_t gdn_chunk_ws_bytes(int64_t n, int hv) { return (size_t)((n + 31) / 32 > 0 ? (n + 31) / 32 : 1) * (size_t)hv * 16384; }
+int launch_gated_delta_rule_chunked(const uint16_t*, const uint16_t*, const uint16_t*, const float*, const float*,
+                                    const float*, int64_t, int, int, int, int, float*, float*, void*, void*) {
+    return kReached;
+}
 int launch_rmsnorm(const uint16_t*, const uint16_t*, uint16_t*, int64_t, int, float, void*) { return kReached; }
 int launch_swiglu(const uint16_t*, uint16_t*, int64_t, int, void*) { return kReached; }
 int blas_create(void** h) { *h = (void*)0x1000; return 0; }

@@ -318,6 +318,32 @@ def test_gated_delta_rule_checks(lib):
     assert call(so=A + 8) == E.TG_EALIGN
 
 
+def test_gated_delta_rule_chunked_checks(lib):
+    """The chunked form takes the scan's checks, then its workspace's."""
+    E = binding
+    wsb = lib.tg_gated_delta_rule_workspace_bytes
+    assert wsb(-1, 4) == 0 and wsb(16, 0) == 0
+    assert wsb(0, 4) == wsb(32, 4) == 4 * 16384  # one 16 KB record per (v head, chunk of 32)
+    assert wsb(33, 4) == 2 * 4 * 16384
+    sizes = [wsb(n, 16) for n in range(0, 5000, 37)]
+    assert sizes == sorted(sizes)
+
+    def call(n=16, hk=2, hv=4, dk=128, dv=128, q=A, k=A, v=A, al=A, be=A, si=None, out=A, so=None, ws=A,
+             wsn=None):
+        wsn = wsb(max(n, 0), hv) if wsn is None else wsn
+        return lib.tg_gated_delta_rule_chunked(q, k, v, al, be, si, n, hk, hv, dk, dv, out, so, ws, wsn, None)
+    assert call(n=0, ws=None, wsn=0) == E.TG_OK  # no tokens, no state out: no-op
+    assert call(n=-1) == E.TG_EINVAL
+    assert call(hk=3, hv=4) == E.TG_EINVAL
+    assert call(dk=96) == E.TG_EUNSUPPORTED
+    assert call(q=None) == E.TG_EINVAL
+    assert call(k=M) == E.TG_EALIGN
+    assert call(so=A + 8) == E.TG_EALIGN
+    assert call(ws=None) == E.TG_EWORKSPACE
+    assert call(wsn=wsb(16, 4) - 1) == E.TG_EWORKSPACE
+    assert call(ws=M) == E.TG_EALIGN
+
+
 def test_kept_budget_semantics():
     """The user budget is a maximum: K = min(max_kept, n); the never-pruned
     question tokens must fit in it."""

@@ -1,6 +1,7 @@
-"""GPU parity of the gated delta rule (tg_gated_delta_rule) against the fp64
-oracle (oracle/gdn.py, pinned to the unrolled transition product, exact
-retrieval and pure decay).
+"""GPU parity of the gated delta rule against the fp64 oracle (oracle/gdn.py,
+pinned to the unrolled transition product, exact retrieval and pure decay),
+in both forms: the scan (tg_gated_delta_rule) and the chunked form on the
+matrix cores (tg_gated_delta_rule_chunked, with its workspace).
 
 Keys and queries are unit rows (rounded to bf16), alpha in [0.9, 1) and beta
 in [0, 1), so every step is non-expansive.  fp32 rounding adds about 6e-8 of
@@ -35,13 +36,25 @@ def _case(seed, T, hk, hv, dk, dv, with_state):
     return q, k, v, alpha, beta, s0
 
 
-def _run(q, k, v, alpha, beta, s0):
+FORMS = ["scan", "chunked"]
+
+
+def _mixer(form, q, k, v, alpha, beta, out, state_in=None, state_out=None):
+    """One call of the given form on device tensors."""
+    if form == "scan":
+        tg.tg_gated_delta_rule(q, k, v, alpha, beta, out, state_in, state_out)
+    else:
+        ws = tg.gdn_workspace(q.shape[0], v.shape[1], gu.dev())
+        tg.tg_gated_delta_rule_chunked(q, k, v, alpha, beta, out, ws, state_in, state_out)
+
+
+def _run(q, k, v, alpha, beta, s0, form="scan"):
     T, hk, dk = q.shape
     hv, dv = v.shape[1], v.shape[2]
     out = torch.empty(T, hv, dv, dtype=torch.float32, device=gu.dev())
     so = torch.empty(hv, dv, dk, dtype=torch.float32, device=gu.dev())
-    tg.tg_gated_delta_rule(gu.bf16(q), gu.bf16(k), gu.bf16(v), gu.f32(alpha), gu.f32(beta), out,
-                           None if s0 is None else gu.f32(s0), so)
+    _mixer(form, gu.bf16(q), gu.bf16(k), gu.bf16(v), gu.f32(alpha), gu.f32(beta), out,
+           None if s0 is None else gu.f32(s0), so)
     torch.cuda.synchronize()
     return out.cpu().numpy().astype(np.float64), so.cpu().numpy().astype(np.float64)
 
@@ -50,62 +63,88 @@ def _rel(a, b):
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
 
 
+@pytest.mark.parametrize("form", FORMS)
 @pytest.mark.parametrize("T,hk,hv,dk,dv,seed,with_state", [
     (200, 2, 4, 128, 128, 1, True), (333, 4, 4, 64, 128, 2, False), (97, 1, 2, 128, 64, 3, True),
-    (65, 2, 2, 64, 64, 4, False), (1, 2, 4, 128, 128, 5, True),
+    (65, 2, 2, 64, 64, 4, False), (1, 2, 4, 128, 128, 5, True), (32, 2, 2, 128, 128, 12, True),
     (2048, 16, 16, 128, 128, 6, False),  # 16 heads of 128 over the 2048 kept tokens of a 16K prompt
 ])
-def test_gated_delta_rule_matches_oracle(T, hk, hv, dk, dv, seed, with_state):
+def test_gated_delta_rule_matches_oracle(T, hk, hv, dk, dv, seed, with_state, form):
     q, k, v, alpha, beta, s0 = _case(seed, T, hk, hv, dk, dv, with_state)
     w = oracle.widen_bf16
     want_o, want_s = gdn.gated_delta_rule(w(q), w(k), w(v), alpha, beta, s0)
-    gu.say(f"gated delta rule T={T} hk={hk} hv={hv} dk={dk} dv={dv}")
-    got_o, got_s = _run(q, k, v, alpha, beta, s0)
+    gu.say(f"gated delta rule ({form}) T={T} hk={hk} hv={hv} dk={dk} dv={dv}")
+    got_o, got_s = _run(q, k, v, alpha, beta, s0, form)
     eo, es = _rel(got_o, want_o), _rel(got_s, want_s)
     gu.say(f"  out {eo:.2e} state {es:.2e}")
     assert eo <= TOL and es <= TOL
 
 
-def test_gated_delta_rule_empty_sequence_passes_state_through():
+@pytest.mark.parametrize("form", FORMS)
+def test_gated_delta_rule_empty_sequence_passes_state_through(form):
     _, _, _, _, _, s0 = _case(7, 1, 2, 4, 128, 64, True)
     hv, dv, dk = s0.shape
     so = torch.full((hv, dv, dk), 7.0, dtype=torch.float32, device=gu.dev())
     e = torch.empty(0, dtype=torch.bfloat16, device=gu.dev())
-    gu.say("gated delta rule T=0")
-    tg.tg_gated_delta_rule(e.view(0, 2, dk), e.view(0, 2, dk), e.view(0, hv, dv),
-                           torch.empty(0, hv, dtype=torch.float32, device=gu.dev()),
-                           torch.empty(0, hv, dtype=torch.float32, device=gu.dev()),
-                           torch.empty(0, hv, dv, dtype=torch.float32, device=gu.dev()), gu.f32(s0), so)
+    gu.say(f"gated delta rule ({form}) T=0")
+    _mixer(form, e.view(0, 2, dk), e.view(0, 2, dk), e.view(0, hv, dv),
+           torch.empty(0, hv, dtype=torch.float32, device=gu.dev()),
+           torch.empty(0, hv, dtype=torch.float32, device=gu.dev()),
+           torch.empty(0, hv, dv, dtype=torch.float32, device=gu.dev()), gu.f32(s0), so)
     torch.cuda.synchronize()
     assert np.array_equal(so.cpu().numpy(), s0)
 
 
-def test_gated_delta_rule_state_carries_over_a_split():
-    """Running tokens [0, m) then [m, T) from the carried state equals one run."""
+@pytest.mark.parametrize("form,m", [("scan", 123), ("chunked", 128)])
+def test_gated_delta_rule_state_carries_over_a_split(form, m):
+    """Running tokens [0, m) then [m, T) from the carried state equals one run
+    bit for bit (the chunked form at a multiple of its 32-token chunks)."""
     q, k, v, alpha, beta, s0 = _case(8, 300, 2, 4, 128, 128, True)
-    gu.say("gated delta rule split at 123")
-    o_all, s_all = _run(q, k, v, alpha, beta, s0)
-    m = 123
-    o1, s1 = _run(q[:m], k[:m], v[:m], alpha[:m], beta[:m], s0)
-    o2, s2 = _run(q[m:], k[m:], v[m:], alpha[m:], beta[m:], s1.astype(np.float32))
+    gu.say(f"gated delta rule ({form}) split at {m}")
+    o_all, s_all = _run(q, k, v, alpha, beta, s0, form)
+    o1, s1 = _run(q[:m], k[:m], v[:m], alpha[:m], beta[:m], s0, form)
+    o2, s2 = _run(q[m:], k[m:], v[m:], alpha[m:], beta[m:], s1.astype(np.float32), form)
     assert np.array_equal(np.concatenate([o1, o2]), o_all)
     assert np.array_equal(s2, s_all)
 
 
-def test_gated_delta_rule_state_in_place():
+def test_gated_delta_rule_chunked_split_off_the_chunk_grid():
+    """A split of the chunked form inside a chunk regroups the tokens into
+    other chunks: the same results to rounding (within 1e-6)."""
+    q, k, v, alpha, beta, s0 = _case(13, 300, 2, 4, 128, 128, True)
+    gu.say("gated delta rule (chunked) split at 123")
+    o_all, s_all = _run(q, k, v, alpha, beta, s0, "chunked")
+    m = 123
+    o1, s1 = _run(q[:m], k[:m], v[:m], alpha[:m], beta[:m], s0, "chunked")
+    o2, s2 = _run(q[m:], k[m:], v[m:], alpha[m:], beta[m:], s1.astype(np.float32), "chunked")
+    assert _rel(np.concatenate([o1, o2]), o_all) <= 1e-6
+    assert _rel(s2, s_all) <= 1e-6
+
+
+def test_gated_delta_rule_chunked_deterministic():
+    q, k, v, alpha, beta, s0 = _case(14, 777, 4, 8, 128, 128, True)
+    gu.say("gated delta rule (chunked) determinism")
+    a = _run(q, k, v, alpha, beta, s0, "chunked")
+    b = _run(q, k, v, alpha, beta, s0, "chunked")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("form", FORMS)
+def test_gated_delta_rule_state_in_place(form):
     """state_out may be the state_in buffer: the state is updated in place."""
     q, k, v, alpha, beta, s0 = _case(9, 150, 2, 4, 128, 128, True)
-    gu.say("gated delta rule in-place state")
-    want_o, want_s = _run(q, k, v, alpha, beta, s0)
+    gu.say(f"gated delta rule ({form}) in-place state")
+    want_o, want_s = _run(q, k, v, alpha, beta, s0, form)
     st = gu.f32(s0)
     out = torch.empty(150, 4, 128, dtype=torch.float32, device=gu.dev())
-    tg.tg_gated_delta_rule(gu.bf16(q), gu.bf16(k), gu.bf16(v), gu.f32(alpha), gu.f32(beta), out, st, st)
+    _mixer(form, gu.bf16(q), gu.bf16(k), gu.bf16(v), gu.f32(alpha), gu.f32(beta), out, st, st)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy().astype(np.float64), want_o)
     assert np.array_equal(st.cpu().numpy().astype(np.float64), want_s)
 
 
-def test_gated_delta_rule_over_compacted_kept_tokens():
+@pytest.mark.parametrize("form", FORMS)
+def test_gated_delta_rule_over_compacted_kept_tokens(form):
     """Above the gate the recurrent mixer sees only the kept tokens, in order:
     q, k, v and the gates gathered by tg_compact, then scanned, equal the
     oracle's scan over the kept subsequence (and, bit for bit, a scan over
@@ -116,14 +155,14 @@ def test_gated_delta_rule_over_compacted_kept_tokens():
     dev = gu.dev()
     src = [gu.bf16(q), gu.bf16(k), gu.bf16(v), gu.f32(alpha), gu.f32(beta)]
     dst = [torch.empty((K,) + tuple(t.shape[1:]), dtype=t.dtype, device=dev) for t in src]
-    gu.say("gated delta rule over compacted kept tokens n=1024 K=192")
+    gu.say(f"gated delta rule ({form}) over compacted kept tokens n=1024 K=192")
     tg.tg_compact(gu.i32(kept), n, None, None, None, None, None, None, extra=list(zip(src, dst)))
     out = torch.empty(K, 4, 128, dtype=torch.float32, device=dev)
-    tg.tg_gated_delta_rule(*dst, out)
+    _mixer(form, *dst, out)
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
     w = oracle.widen_bf16
     want, _ = gdn.gated_delta_rule(w(q[kept]), w(k[kept]), w(v[kept]), alpha[kept], beta[kept])
     assert _rel(got, want) <= TOL
-    host_o, _ = _run(q[kept], k[kept], v[kept], alpha[kept], beta[kept], None)
+    host_o, _ = _run(q[kept], k[kept], v[kept], alpha[kept], beta[kept], None, form)
     assert np.array_equal(got, host_o)
