@@ -418,9 +418,12 @@ __global__ __launch_bounds__(256) void gdn_seq(const uint16_t* __restrict__ q, c
             lds_load<4>(v, v_bytes, sb + 2 * KQ + 4 * (it * 128 + wg * 64), go);
         }
         const uint8_t* r = rec + ((int64_t)h * nch + ch) * kRecBytes;
+        constexpr int kUsed = (kRecRl + kCC * 4) / 16;  // 16-byte pieces of the record that hold data
 #pragma unroll
-        for (int it = 0; it < kRecBytes / (16 * 128); ++it)
-            lds_load<16>(r, kRecBytes, sb + 2 * KQ + C::VB + 16 * (it * 128 + wg * 64), 16u * (it * 128 + tg));
+        for (int it = 0; it < (kUsed + 127) / 128; ++it) {
+            if (it * 128 + 128 <= kUsed || it * 128 + tg < kUsed)
+                lds_load<16>(r, kRecBytes, sb + 2 * KQ + C::VB + 16 * (it * 128 + wg * 64), 16u * (it * 128 + tg));
+        }
     };
 
     // The state: wave w < DW owns columns 32 w .. 32 w + 31 of the slice's
@@ -451,17 +454,24 @@ __global__ __launch_bounds__(256) void gdn_seq(const uint16_t* __restrict__ q, c
     // are kept by chunk parity.
     struct OutOps {
         u32x4 mh, mm, ml;
-        float gm[4];
+        f32x4 acc;  // diag(gamma) Q S0^T, this lane's four tokens
     };
-    auto out_ops = [&](const TG_LDS uint8_t* __restrict__ stage) {
+    auto out_ops = [&](int64_t cc, const TG_LDS uint8_t* __restrict__ stage) {
         const int tb = w - 2;
         const TG_LDS uint8_t* rbc = stage + 2 * KQ + C::VB;
         const TG_LDS u32x4* mp = (const TG_LDS u32x4*)(rbc + kRecM) + tb * 3 * 64 + lane;
         const TG_LDS float* gamc = (const TG_LDS float*)(rbc + kRecGam);
+        const int par = (int)(cc & 1);
         OutOps o;
         o.mh = mp[0], o.mm = mp[64], o.ml = mp[128];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o.gm[j] = gamc[16 * tb + 4 * g4 + j];
+        for (int j = 0; j < 4; ++j) {
+            const int t = 16 * tb + 4 * g4 + j;
+            float p = ppq[par][0][t][i16];
+#pragma unroll
+            for (int b = 1; b < DW; ++b) p += ppq[par][b][t][i16];
+            o.acc[j] = gamc[t] * p;
+        }
         return o;
     };
     auto outputs = [&](int64_t cc, const OutOps& o) {
@@ -469,15 +479,7 @@ __global__ __launch_bounds__(256) void gdn_seq(const uint16_t* __restrict__ q, c
         const int64_t tc = cc * kCC;
         const int tnc = n - tc < kCC ? (int)(n - tc) : kCC;
         const int par = (int)(cc & 1);
-        f32x4 acc;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int t = 16 * tb + 4 * g4 + j;
-            float p = ppq[par][0][t][i16];
-#pragma unroll
-            for (int b = 1; b < DW; ++b) p += ppq[par][b][t][i16];
-            acc[j] = o.gm[j] * p;
-        }
+        f32x4 acc = o.acc;
         float b8[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) b8[e] = ww[par][8 * g4 + e][i16];
@@ -539,7 +541,7 @@ __global__ __launch_bounds__(256) void gdn_seq(const uint16_t* __restrict__ q, c
         static_assert(kCC * kRS / 4 == 128, "U in waves 0 and 1");
         OutOps prev;
         if (w >= 2) {
-            if (ch > 0) prev = out_ops(nb);
+            if (ch > 0) prev = out_ops(ch - 1, nb);
             if (ch + 1 < nch) {
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // its reads of that stage are done
                 issue(ch + 1, nb);
@@ -620,7 +622,7 @@ __global__ __launch_bounds__(256) void gdn_seq(const uint16_t* __restrict__ q, c
         chunk(ch, s0, s1);
         if (ch + 1 < nch) chunk(ch + 1, s1, s0);
     }
-    if (nch > 0 && w >= 2) outputs(nch - 1, out_ops((nch - 1) & 1 ? s1 : s0));  // the last chunk's
+    if (nch > 0 && w >= 2) outputs(nch - 1, out_ops(nch - 1, (nch - 1) & 1 ? s1 : s0));  // the last chunk's
     if (owner && state_out) {
 #pragma unroll
         for (int u = 0; u < 2; ++u)
