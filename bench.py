@@ -518,11 +518,13 @@ def gate_backward(tg, torch, dev, shape, reps=5):
 
 
 def hybrid_mixer(tg, torch, dev, shape, reps=5):
-    """tg_gated_delta_rule with 16 heads of 128 x 128 state over the kept
+    """The gated delta rule with 16 heads of 128 x 128 state over the kept
     tokens (K) and over the whole prompt (N): what pruning saves in an upper
-    recurrent layer of the hybrid backbone."""
+    recurrent layer of the hybrid backbone.  Both forms: the chunked one on
+    the matrix cores (tg_gated_delta_rule_chunked, the main figures) and the
+    scan (tg_gated_delta_rule, under "scan")."""
     heads, dk = 16, 128
-    res = {}
+    res, scan = {}, {}
     for name, t in (("kept", shape.k), ("full", shape.n)):
         g = torch.Generator(device=dev)
         g.manual_seed(t)
@@ -532,17 +534,24 @@ def hybrid_mixer(tg, torch, dev, shape, reps=5):
         alpha = 0.9 + 0.1 * torch.rand(t, heads, generator=g, device=dev)
         beta = torch.rand(t, heads, generator=g, device=dev)
         out = torch.empty(t, heads, dk, dtype=torch.float32, device=dev)
-        tg.tg_gated_delta_rule(q, k, v, alpha, beta, out)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            tg.tg_gated_delta_rule(q, k, v, alpha, beta, out)
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
-        res[name] = {"tokens": t, "us": round(us, 1), "ns_per_token": round(us * 1e3 / t, 1)}
+        ws = tg.gdn_workspace(t, heads, dev)
+        forms = (("chunked", lambda: tg.tg_gated_delta_rule_chunked(q, k, v, alpha, beta, out, ws)),
+                 ("scan", lambda: tg.tg_gated_delta_rule(q, k, v, alpha, beta, out)))
+        for form, fn in forms:
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            (res if form == "chunked" else scan)[name] = {"tokens": t, "us": round(us, 1),
+                                                          "ns_per_token": round(us * 1e3 / t, 1)}
+        del ws
     res["speedup"] = round(res["full"]["us"] / res["kept"]["us"], 2)
+    res["scan"] = scan
     return res
 
 
