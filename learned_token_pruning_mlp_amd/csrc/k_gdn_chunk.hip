@@ -57,14 +57,16 @@ constexpr int kRS = 16;  // state rows per workgroup of the sequential pass
 
 // One record per (v head, chunk), in bytes: the A operands of W = T U and of
 // M W (per 16-token row block tb, per part hi / mid / lo, per lane: 16 bytes),
-// then gamma, beta (0 past the last token) and R(C-1, i), 32 floats each.
+// then, per 16-token half of the chunk, gamma, beta (0 past the last token)
+// and R(C-1, i) of its tokens, 16 floats each (each half in 256 bytes).
 constexpr int kRecT = 0;
 constexpr int kRecM = 2 * 3 * 64 * 16;
-constexpr int kRecGam = 2 * kRecM;
-constexpr int kRecBet = kRecGam + kCC * 4;
-constexpr int kRecRl = kRecBet + kCC * 4;
-constexpr int kRecBytes = 16384;  // four 4 KB rounds of direct loads
-static_assert(kRecRl + kCC * 4 <= kRecBytes, "record layout");
+constexpr int kRecTail = 2 * kRecM;
+constexpr int kRecBytes = 16384;
+constexpr int kTailGam = 0, kTailBet = 1, kTailRl = 2;
+// byte offset in the record of gamma (a = kTailGam), beta or R(C-1, t) of token t
+__host__ __device__ constexpr int rec_tail(int a, int t) { return kRecTail + 256 * (t >> 4) + 64 * a + 4 * (t & 15); }
+static_assert(kRecTail + 512 <= kRecBytes, "record layout");
 
 constexpr int kBufferWord3 = 0x00020000;
 
@@ -355,87 +357,113 @@ __global__ __launch_bounds__(256) void gdn_prep(const uint16_t* __restrict__ q, 
         for (int p = 0; p < 3; ++p) *reinterpret_cast<u32x4*>(dst + ((tb * 3 + p) * 64 + lane) * 16) = parts[p];
     }
     if (tid < kCC) {
-        reinterpret_cast<float*>(r + kRecGam)[tid] = gam[tid];
-        reinterpret_cast<float*>(r + kRecBet)[tid] = bet[tid];
-        reinterpret_cast<float*>(r + kRecRl)[tid] = rl[tid];
+        *reinterpret_cast<float*>(r + rec_tail(kTailGam, tid)) = gam[tid];
+        *reinterpret_cast<float*>(r + rec_tail(kTailBet, tid)) = bet[tid];
+        *reinterpret_cast<float*>(r + rec_tail(kTailRl, tid)) = rl[tid];
     }
 }
 
-// ---- the sequential pass: one workgroup (4 waves) per kRS rows of a head's state
+// ---- the sequential pass: one workgroup per kRS rows of a head's state,
+// DK / 32 owner waves (each holds a 32-column band of the state) and two
+// helper waves
 template <int DK, int DV>
 struct Seq {
-    static constexpr int DW = DK / 32;           // waves that own a 32-column band of the state
-    static constexpr int VB = kCC * kRS * 2;     // bytes of the workgroup's v values of a chunk
-    static constexpr int STAGE = 2 * Rows<DK>::KQ + VB + kRecBytes;
-    static_assert(VB == 1024, "v chunk in one 4-byte load per thread");
+    static constexpr int DW = DK / 32;          // owner waves
+    static constexpr int NT = 64 * (DW + 2);    // threads: the owners', then the helpers'
+    static constexpr int BAND = kCC * 32 * 2;   // bytes of a band's k (or q) values of a chunk
+    static constexpr int VB = kCC * kRS * 2;    // bytes of the workgroup's v values of a chunk
+    static constexpr int RECB = kRecTail + 512;  // bytes of the record taken
+    static constexpr int OFF_V = DW * 2 * BAND;        // stage: the owners' bands (k, then q), v, the record
+    static constexpr int OFF_R = OFF_V + VB;
+    static constexpr int STAGE = OFF_R + RECB;
+    static_assert(VB == 2 * 4 * 128, "v chunk in two 4-byte rounds of the helpers");
+    static_assert(kRecM == 2 * 3 * 1024 && RECB <= kRecBytes, "a row block of T or M in three 1 KB loads");
     static_assert(DV % kRS == 0 && DW >= 1 && DW <= 4, "state slices");
+    static_assert(NT == 64 * (DK / 32 + 2), "the kernel's launch bounds");
 };
 
+// A band's k (or q) values of a chunk in LDS: token t's four 16-byte pieces
+// (band columns 8 p .. 8 p + 7) at slots 4 t + (p ^ (t / 4) % 4), so that the
+// operand reads of a product and the transposing reads hit distinct banks.
+__device__ __forceinline__ int band_off(int t, int cc) {
+    return 16 * (4 * t + ((cc >> 3) ^ ((t >> 2) & 3))) + 2 * (cc & 7);
+}
+
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void gdn_seq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                               const uint16_t* __restrict__ v, const float* state_in, int64_t n,
-                                               int hk, int hv, int64_t nch, const uint8_t* __restrict__ rec,
-                                               float* __restrict__ out,
-                                               float* state_out) {  // state_out may be state_in
-    using RW = Rows<DK>;
+__global__ __launch_bounds__(64 * (DK / 32 + 2)) void gdn_seq(const uint16_t* __restrict__ q,
+                                                          const uint16_t* __restrict__ k,
+                                                          const uint16_t* __restrict__ v, const float* state_in,
+                                                          int64_t n, int hk, int hv, int64_t nch,
+                                                          const uint8_t* __restrict__ rec, float* __restrict__ out,
+                                                          float* state_out) {  // state_out may be state_in
     using C = Seq<DK, DV>;
-    constexpr int DW = C::DW, KQ = RW::KQ;
+    constexpr int DW = C::DW, BAND = C::BAND;
     // one LDS object per stage, so the compiler can see that reads of one
     // stage never alias the loads in flight into the other
     __shared__ __attribute__((aligned(1024))) uint8_t stg0[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t stg1[C::STAGE];
-    __shared__ __attribute__((aligned(16))) float ppk[DW][kCC][20];     // per band: K S0^T
-    __shared__ __attribute__((aligned(16))) float ppq[2][DW][kCC][20];  // per band: Q S0^T, by chunk parity
-    __shared__ __attribute__((aligned(16))) float uu[kCC][20];           // U
-    __shared__ __attribute__((aligned(16))) float ww[2][kCC][20];        // W, by chunk parity
+    __shared__ __attribute__((aligned(16))) float ppk[DW][kRS][36];     // per band: (K S0^T)^T
+    __shared__ __attribute__((aligned(16))) float ppq[2][DW][kRS][36];  // per band: (Q S0^T)^T, by chunk parity
+    __shared__ __attribute__((aligned(16))) float ww[2][kRS][36];       // W^T, by chunk parity
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int i16 = lane & 15, g4 = lane >> 4;
     const int h = blockIdx.x / (DV / kRS), r0 = (blockIdx.x % (DV / kRS)) * kRS;
     const int hq = h / (hv / hk);
     const uint32_t qk_bytes = (uint32_t)n * (uint32_t)hk * DK * 2u;
     const uint32_t v_bytes = (uint32_t)n * (uint32_t)hv * DV * 2u;
+    const bool owner = w < DW;
+    const int tb = w - DW;  // a helper's 16-token block
 
-    // A chunk's k and q rows, the workgroup's v values and the record, issued
-    // by waves 2 and 3 alone (128 threads: tg = tid - 128), in phases where
-    // they would otherwise wait: a wave that finds the memory queue full
-    // stalls at the issue, which must not fall on the state's chain.
-    constexpr int NP = RW::NP;
-    auto issue = [&](int64_t ch, TG_LDS uint8_t* __restrict__ sb) {
-        const int64_t t0 = ch * kCC;
-        const int tg = tid - 128, wg = w - 2;
+    // Loads of a chunk: each owner takes its band of the k and q rows (four
+    // 1 KB direct loads into its own region of the stage, read by it alone,
+    // so it waits for them by itself); the helpers take the workgroup's v
+    // values and the record, issued in a phase where they would otherwise
+    // wait and waited for before the chunk's first barrier.  The loads into a
+    // stage start while the other helper may still be reading the output
+    // operands of the chunk the stage held (M's row block and gamma of its
+    // half): each helper loads exactly those parts of the record that it
+    // alone reads there (T and M's row block tb, the tail of half tb).
+    auto issue_band = [&](int64_t c, TG_LDS uint8_t* __restrict__ sb) {
+        const int64_t t0 = c * kCC;
+        TG_LDS uint8_t* bk = sb + w * 2 * BAND;
 #pragma unroll
-        for (int it = 0; it < KQ / (16 * 128); ++it) {
-            const int e = it * 128 + tg;  // piece slot
-            const int t = e / NP, p = (e % NP) ^ (t % NP);
-            const uint32_t go = ((uint32_t)(t0 + t) * (uint32_t)hk + (uint32_t)hq) * (DK * 2u) + 16u * p;
-            lds_load<16>(k, qk_bytes, sb + 16 * (it * 128 + wg * 64), go);
-            lds_load<16>(q, qk_bytes, sb + KQ + 16 * (it * 128 + wg * 64), go);
-        }
-#pragma unroll
-        for (int it = 0; it < C::VB / (4 * 128); ++it) {
-            const int e = it * 128 + tg, t = e >> 3, wd = e & 7;
-            const uint32_t go = ((uint32_t)(t0 + t) * (uint32_t)hv + (uint32_t)h) * (DV * 2u) + r0 * 2u + 4u * wd;
-            lds_load<4>(v, v_bytes, sb + 2 * KQ + 4 * (it * 128 + wg * 64), go);
-        }
-        const uint8_t* r = rec + ((int64_t)h * nch + ch) * kRecBytes;
-        constexpr int kUsed = (kRecRl + kCC * 4) / 16;  // 16-byte pieces of the record that hold data
-#pragma unroll
-        for (int it = 0; it < (kUsed + 127) / 128; ++it) {
-            if (it * 128 + 128 <= kUsed || it * 128 + tg < kUsed)
-                lds_load<16>(r, kRecBytes, sb + 2 * KQ + C::VB + 16 * (it * 128 + wg * 64), 16u * (it * 128 + tg));
+        for (int it = 0; it < 2; ++it) {
+            const int s = 64 * it + lane, t = s >> 2, p = (s & 3) ^ ((t >> 2) & 3);
+            const uint32_t go =
+                ((uint32_t)(t0 + t) * (uint32_t)hk + (uint32_t)hq) * (DK * 2u) + 64u * (uint32_t)w + 16u * p;
+            lds_load<16>(k, qk_bytes, bk + 1024 * it, go);
+            lds_load<16>(q, qk_bytes, bk + BAND + 1024 * it, go);
         }
     };
+    auto issue_rest = [&](int64_t c, TG_LDS uint8_t* __restrict__ sb) {
+        const int64_t t0 = c * kCC;
+        const int tg = tid - 64 * DW;
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int e = it * 128 + tg, t = e >> 3, wd = e & 7;
+            const uint32_t go = ((uint32_t)(t0 + t) * (uint32_t)hv + (uint32_t)h) * (DV * 2u) + r0 * 2u + 4u * wd;
+            lds_load<4>(v, v_bytes, sb + C::OFF_V + 4 * (it * 128 + tb * 64), go);
+        }
+        const uint8_t* r = rec + ((int64_t)h * nch + c) * kRecBytes;
+#pragma unroll
+        for (int it = 0; it < 3; ++it) {
+            const int ot = kRecT + 3072 * tb + 1024 * it, om = kRecM + 3072 * tb + 1024 * it;
+            lds_load<16>(r, kRecBytes, sb + C::OFF_R + ot, ot + 16u * lane);
+            lds_load<16>(r, kRecBytes, sb + C::OFF_R + om, om + 16u * lane);
+        }
+        const int otl = kRecTail + 256 * tb;
+        lds_load<4>(r, kRecBytes, sb + C::OFF_R + otl, otl + 4u * lane);
+    };
 
-    // The state: wave w < DW owns columns 32 w .. 32 w + 31 of the slice's
-    // rows, held transposed (lane: row i16, columns 32 w + 16 u + 4 g4 + j,
-    // u = 0, 1, j = 0..3), and, as the B operand of the chunk's products,
-    // split into three bf16 parts (k-group g4 of the band's 32 columns takes
-    // columns 4 g4 .. +3 and 16 + 4 g4 .. +3).
-    const bool owner = w < DW;
-    const int c0 = 32 * w;
+    // The state: owner w holds columns 32 w .. 32 w + 31 of the slice's rows,
+    // transposed (lane: row i16, columns 32 w + 16 u + 4 g4 + j, u = 0, 1,
+    // j = 0..3), and, as the B operand of the chunk's products, split into
+    // three bf16 parts (k-group g4 of the band takes band columns 4 g4 .. +3
+    // and 16 + 4 g4 .. +3).
     float sr[2][4];
     u32x4 sh, sm, sl;
     if (owner) {
+        const int c0 = 32 * w;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             float4 x = float4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -445,44 +473,53 @@ __global__ __launch_bounds__(256) void gdn_seq(const uint16_t* __restrict__ q, c
         const float x8[8] = {sr[0][0], sr[0][1], sr[0][2], sr[0][3], sr[1][0], sr[1][1], sr[1][2], sr[1][3]};
         split8(x8, sh, sm, sl);
     }
+    // a product's A operand from a band: this lane's token, k-group g4's columns
+    auto band_op = [&](const TG_LDS uint8_t* b, int t) {
+        const u32x2 lo = *(const TG_LDS u32x2*)(b + band_off(t, 4 * g4));
+        const u32x2 hi = *(const TG_LDS u32x2*)(b + band_off(t, 16 + 4 * g4));
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    // (X S0^T)^T of the band for both 16-token blocks of X (k or q rows) into dst
+    auto band_product = [&](const TG_LDS uint8_t* b, float (*dst)[36]) {
+        const u32x4 a0 = band_op(b, i16), a1 = band_op(b, 16 + i16);
+        f32x4 x0 = mfma16(a0, sl, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+        f32x4 x1 = mfma16(a1, sl, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+        x0 = mfma16(a0, sm, x0), x1 = mfma16(a1, sm, x1);
+        x0 = mfma16(a0, sh, x0), x1 = mfma16(a1, sh, x1);
+        *(float4*)&dst[i16][4 * g4] = float4{x0[0], x0[1], x0[2], x0[3]};
+        *(float4*)&dst[i16][16 + 4 * g4] = float4{x1[0], x1[1], x1[2], x1[3]};
+    };
 
-    // The outputs of chunk cc, O = diag(gamma) Q S0^T + M W (waves 2, 3: one
-    // 16-token block each).  They are formed one chunk late, while waves 0 and
-    // 1 form the next chunk's W: nothing later needs them, so they stay off
-    // the state's chain.  M's operands and gamma are taken from cc's stage
-    // into registers first (the stage is then refilled), its Q partials and W
-    // are kept by chunk parity.
+    // The outputs of chunk cc, O = diag(gamma) Q S0^T + M W (the helpers, one
+    // 16-token block each), formed one chunk late, off the state's chain: M's
+    // operands and gamma are taken into registers before cc's stage is
+    // refilled, the Q S0^T partials and W are kept by chunk parity.
     struct OutOps {
         u32x4 mh, mm, ml;
-        f32x4 acc;  // diag(gamma) Q S0^T, this lane's four tokens
+        lf4 gm;  // gamma of this lane's four tokens
     };
-    auto out_ops = [&](int64_t cc, const TG_LDS uint8_t* __restrict__ stage) {
-        const int tb = w - 2;
-        const TG_LDS uint8_t* rbc = stage + 2 * KQ + C::VB;
+    auto out_ops = [&](const TG_LDS uint8_t* __restrict__ stage) {
+        const TG_LDS uint8_t* rbc = stage + C::OFF_R;
         const TG_LDS u32x4* mp = (const TG_LDS u32x4*)(rbc + kRecM) + tb * 3 * 64 + lane;
-        const TG_LDS float* gamc = (const TG_LDS float*)(rbc + kRecGam);
-        const int par = (int)(cc & 1);
         OutOps o;
         o.mh = mp[0], o.mm = mp[64], o.ml = mp[128];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int t = 16 * tb + 4 * g4 + j;
-            float p = ppq[par][0][t][i16];
-#pragma unroll
-            for (int b = 1; b < DW; ++b) p += ppq[par][b][t][i16];
-            o.acc[j] = gamc[t] * p;
-        }
+        o.gm = *(const TG_LDS lf4*)(rbc + rec_tail(kTailGam, 16 * tb + 4 * g4));
         return o;
     };
     auto outputs = [&](int64_t cc, const OutOps& o) {
-        const int tb = w - 2;
         const int64_t tc = cc * kCC;
         const int tnc = n - tc < kCC ? (int)(n - tc) : kCC;
         const int par = (int)(cc & 1);
-        f32x4 acc = o.acc;
-        float b8[8];
+        float4 pq[DW];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) b8[e] = ww[par][8 * g4 + e][i16];
+        for (int b = 0; b < DW; ++b) pq[b] = *(const float4*)&ppq[par][b][i16][16 * tb + 4 * g4];
+        const float4 w0 = *(const float4*)&ww[par][i16][8 * g4], w1 = *(const float4*)&ww[par][i16][8 * g4 + 4];
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        float4 p = pq[0];
+#pragma unroll
+        for (int b = 1; b < DW; ++b) p.x += pq[b].x, p.y += pq[b].y, p.z += pq[b].z, p.w += pq[b].w;
+        f32x4 acc = {o.gm.x * p.x, o.gm.y * p.y, o.gm.z * p.z, o.gm.w * p.w};
+        const float b8[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
         acc = mfma16_x6s(o.mh, o.mm, o.ml, b8, acc);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -492,138 +529,141 @@ __global__ __launch_bounds__(256) void gdn_seq(const uint16_t* __restrict__ q, c
     };
 
     auto chunk = [&](int64_t ch, const TG_LDS uint8_t* __restrict__ cb, TG_LDS uint8_t* __restrict__ nb) {
-        TG_WAIT_VMCNT(0);  // this thread's loads of the chunk have landed (and its stores are done)
-        lds_barrier();     // ... every thread's; every wave is done with the other stage
-        const TG_LDS uint8_t* kb = cb;
-        const TG_LDS uint8_t* qb = cb + KQ;
-        const TG_LDS uint16_t* vb = (const TG_LDS uint16_t*)(cb + 2 * KQ);
-        const TG_LDS uint8_t* rb = cb + 2 * KQ + C::VB;
-        const TG_LDS float* gam = (const TG_LDS float*)(rb + kRecGam);
-        const TG_LDS float* bet = (const TG_LDS float*)(rb + kRecBet);
-        const TG_LDS float* rl = (const TG_LDS float*)(rb + kRecRl);
-
-        // ---- A. band partials of K S0^T and Q S0^T
-        if (owner) {
-            u32x4 a[4];  // K rows 0-15, 16-31, then Q's: this lane's row, the band's k-group columns
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const TG_LDS uint8_t* xb = x < 2 ? kb : qb;
-                const int t = 16 * (x & 1) + i16;
-                a[x] = u32x4{*(const TG_LDS uint32_t*)(xb + RW::boff(t, c0 + 4 * g4)),
-                             *(const TG_LDS uint32_t*)(xb + RW::boff(t, c0 + 4 * g4 + 2)),
-                             *(const TG_LDS uint32_t*)(xb + RW::boff(t, c0 + 16 + 4 * g4)),
-                             *(const TG_LDS uint32_t*)(xb + RW::boff(t, c0 + 16 + 4 * g4 + 2))};
-            }
-            f32x4 acc[4];
-#pragma unroll
-            for (int x = 0; x < 4; ++x) acc[x] = mfma16(a[x], sl, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
-#pragma unroll
-            for (int x = 0; x < 4; ++x) acc[x] = mfma16(a[x], sm, acc[x]);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) acc[x] = mfma16(a[x], sh, acc[x]);
-            const int pq = (int)(ch & 1);
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int t = 16 * (x & 1) + 4 * g4 + j;
-                    if (x < 2)
-                        ppk[w][t][i16] = acc[x][j];
-                    else
-                        ppq[pq][w][t][i16] = acc[x][j];
-                }
-        }
-        lds_barrier();
-
-        // ---- B. U = diag(beta)(V - diag(gamma) K S0^T) (waves 0, 1); waves 2, 3
-        // take the previous chunk's output operands from its stage, then load
-        // the next chunk into that stage
-        static_assert(kCC * kRS / 4 == 128, "U in waves 0 and 1");
-        OutOps prev;
-        if (w >= 2) {
-            if (ch > 0) prev = out_ops(ch - 1, nb);
-            if (ch + 1 < nch) {
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // its reads of that stage are done
-                issue(ch + 1, nb);
-            }
-        } else {
-            const int t = tid >> 2, r4 = 4 * (tid & 3);
-            float4 p = *(const float4*)&ppk[0][t][r4];
-#pragma unroll
-            for (int b = 1; b < DW; ++b) {
-                const float4 y = *(const float4*)&ppk[b][t][r4];
-                p.x += y.x, p.y += y.y, p.z += y.z, p.w += y.w;
-            }
-            const u32x2 vw = *(const TG_LDS u32x2*)(vb + t * kRS + r4);
-            const float bt = bet[t], gm = gam[t];
-            float4 u;
-            u.x = bt * (tgd::bf16lo(vw[0]) - gm * p.x);
-            u.y = bt * (tgd::bf16hi(vw[0]) - gm * p.y);
-            u.z = bt * (tgd::bf16lo(vw[1]) - gm * p.z);
-            u.w = bt * (tgd::bf16hi(vw[1]) - gm * p.w);
-            *(float4*)&uu[t][r4] = u;
-        }
-        lds_barrier();
-
-        // ---- C. W = T U (waves 0, 1: one 16-token block each; T's parts from
-        // the record); waves 2, 3 form the previous chunk's outputs
+        const TG_LDS uint8_t* rb = cb + C::OFF_R;
         const int par = (int)(ch & 1);
-        if (w >= 2) {
-            if (ch > 0) outputs(ch - 1, prev);
+
+        // ---- A. owners: (K S0^T)^T of the band (their k and q bands landed,
+        // the next chunk's issued); helpers: the previous chunk's output
+        // operands from its stage, then the next chunk's v and record into it
+        OutOps prev;
+        if (owner) {
+            TG_WAIT_VMCNT(0);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // done reading that stage's band
+            if (ch + 1 < nch) issue_band(ch + 1, nb);
+            band_product(cb + w * 2 * BAND, ppk[w]);
         } else {
-            const int tb = w;
-            const TG_LDS u32x4* tp = (const TG_LDS u32x4*)(rb + kRecT) + tb * 3 * 64 + lane;
-            float b8[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) b8[e] = uu[8 * g4 + e][i16];
-            const f32x4 acc = mfma16_x6s(tp[0], tp[64], tp[128], b8, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ww[par][16 * tb + 4 * g4 + j][i16] = acc[j];
+            if (ch > 0) prev = out_ops(nb);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // its reads of that stage are done
+            if (ch + 1 < nch) issue_rest(ch + 1, nb);
         }
         lds_barrier();
 
-        // ---- D. each band's state update S^T <- gamma_last S^T + K^T diag(R(C-1, .)) W
+        // ---- B. helpers: U = diag(beta)(V - diag(gamma) K S0^T) as the B
+        // operand, W = T U (one 16-token block each; T's parts from the
+        // record); owners: (Q S0^T)^T of the band, and the update's operands
+        float rl8[8], gl = 0.0f;
+        u32x4 kt[2];
         if (owner) {
-            float b8[8];
+            band_product(cb + w * 2 * BAND + BAND, ppq[par][w]);
+            const lf4 r0v = *(const TG_LDS lf4*)(rb + rec_tail(kTailRl, 8 * g4));
+            const lf4 r1v = *(const TG_LDS lf4*)(rb + rec_tail(kTailRl, 8 * g4 + 4));
+            rl8[0] = r0v.x, rl8[1] = r0v.y, rl8[2] = r0v.z, rl8[3] = r0v.w;
+            rl8[4] = r1v.x, rl8[5] = r1v.y, rl8[6] = r1v.z, rl8[7] = r1v.w;
+            gl = *(const TG_LDS float*)(rb + rec_tail(kTailGam, kCC - 1));
+            // K^T of the band (rows: band columns 16 u + i16, k: tokens 8 g4 ..
+            // 8 g4 + 7), two transposing reads each: lane jj of a 16-lane group
+            // addresses token 8 g4 + 4 hh + jj / 4, columns 4 (jj % 4) .. +3
+            const TG_LDS uint8_t* bk = cb + w * 2 * BAND;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) b8[e] = rl[8 * g4 + e] * ww[par][8 * g4 + e][i16];
-            u32x4 bh, bm, bl;
-            split8(b8, bh, bm, bl);
-            const float gl = gam[kCC - 1];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                // A = K^T rows c0 + 16 u + i16, k = tokens 8 g4 .. +7 (two
-                // transposing reads: lane jj of a 16-lane group addresses
-                // token 8 g4 + 4 hh + jj / 4, columns 4 (jj % 4) .. +3)
-                u32x4 a;
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     const int t = 8 * g4 + 4 * hh + (i16 >> 2);
                     const bf16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                        (TG_LDS bf16x4_t*)(kb + RW::boff(t, c0 + 16 * u + 4 * (i16 & 3))));
+                        (TG_LDS bf16x4_t*)(bk + band_off(t, 16 * u + 4 * (i16 & 3))));
                     const u32x2 xw = __builtin_bit_cast(u32x2, x);
-                    a[2 * hh] = xw[0], a[2 * hh + 1] = xw[1];
+                    kt[u][2 * hh] = xw[0], kt[u][2 * hh + 1] = xw[1];
                 }
+        } else {
+            // every operand first, in one round of LDS reads: the band
+            // partials, v of tokens 8 g4 .. +7 in row i16 (transposing reads as
+            // for K^T), beta and gamma of those tokens, T's parts
+            float4 pk[DW][2];
+#pragma unroll
+            for (int b = 0; b < DW; ++b)
+                pk[b][0] = *(const float4*)&ppk[b][i16][8 * g4], pk[b][1] = *(const float4*)&ppk[b][i16][8 * g4 + 4];
+            u32x2 vw[2];
+            const TG_LDS uint8_t* vb = cb + C::OFF_V;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int t = 8 * g4 + 4 * hh + (i16 >> 2);
+                vw[hh] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                                       (TG_LDS bf16x4_t*)(vb + 2 * (t * kRS + 4 * (i16 & 3)))));
+            }
+            lf4 bt[2], gm[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                bt[hh] = *(const TG_LDS lf4*)(rb + rec_tail(kTailBet, 8 * g4 + 4 * hh));
+                gm[hh] = *(const TG_LDS lf4*)(rb + rec_tail(kTailGam, 8 * g4 + 4 * hh));
+            }
+            const TG_LDS u32x4* tp = (const TG_LDS u32x4*)(rb + kRecT) + tb * 3 * 64 + lane;
+            const u32x4 th = tp[0], tm = tp[64], tl = tp[128];
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            float u8[8];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const float4 x = pk[0][hh];
+                float p4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+                for (int b = 1; b < DW; ++b) {
+                    const float4 y = pk[b][hh];
+                    p4[0] += y.x, p4[1] += y.y, p4[2] += y.z, p4[3] += y.w;
+                }
+                const float v4[4] = {tgd::bf16lo(vw[hh][0]), tgd::bf16hi(vw[hh][0]), tgd::bf16lo(vw[hh][1]),
+                                     tgd::bf16hi(vw[hh][1])};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) u8[4 * hh + e] = bt[hh][e] * (v4[e] - gm[hh][e] * p4[e]);
+            }
+            const f32x4 acc = mfma16_x6s(th, tm, tl, u8, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+            *(float4*)&ww[par][i16][16 * tb + 4 * g4] = float4{acc[0], acc[1], acc[2], acc[3]};
+        }
+        lds_barrier();
+
+        // ---- C. owners: the band's update S^T <- gamma_last S^T + K^T
+        // diag(R(C-1, .)) W; helpers: the previous chunk's outputs
+        if (owner) {
+            const float4 w0 = *(const float4*)&ww[par][i16][8 * g4], w1 = *(const float4*)&ww[par][i16][8 * g4 + 4];
+            const float b8[8] = {rl8[0] * w0.x, rl8[1] * w0.y, rl8[2] * w0.z, rl8[3] * w0.w,
+                                 rl8[4] * w1.x, rl8[5] * w1.y, rl8[6] * w1.z, rl8[7] * w1.w};
+            u32x4 bh, bm, bl;
+            split8(b8, bh, bm, bl);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
                 f32x4 acc = {gl * sr[u][0], gl * sr[u][1], gl * sr[u][2], gl * sr[u][3]};
-                acc = mfma16(a, bl, acc);
-                acc = mfma16(a, bm, acc);
-                acc = mfma16(a, bh, acc);
+                acc = mfma16(kt[u], bl, acc);
+                acc = mfma16(kt[u], bm, acc);
+                acc = mfma16(kt[u], bh, acc);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) sr[u][j] = acc[j];
             }
             const float x8[8] = {sr[0][0], sr[0][1], sr[0][2], sr[0][3], sr[1][0], sr[1][1], sr[1][2], sr[1][3]};
             split8(x8, sh, sm, sl);
+        } else {
+            TG_WAIT_VMCNT(0);  // the next chunk's v and record have landed (before the next barrier)
+            if (ch > 0) outputs(ch - 1, prev);
         }
     };
     TG_LDS uint8_t* s0 = (TG_LDS uint8_t*)stg0;
     TG_LDS uint8_t* s1 = (TG_LDS uint8_t*)stg1;
-    if (nch > 0 && w >= 2) issue(0, s0);
+    if (nch > 0) {
+        if (owner) {
+            issue_band(0, s0);
+        } else {
+            issue_rest(0, s0);
+            TG_WAIT_VMCNT(0);
+        }
+    }
     for (int64_t ch = 0; ch < nch; ch += 2) {
         chunk(ch, s0, s1);
         if (ch + 1 < nch) chunk(ch + 1, s1, s0);
     }
-    if (nch > 0 && w >= 2) outputs(nch - 1, out_ops(nch - 1, (nch - 1) & 1 ? s1 : s0));  // the last chunk's
+    if (nch > 0 && !owner) {
+        // the last chunk's outputs (its Q S0^T partials and W are behind the
+        // last barrier)
+        outputs(nch - 1, out_ops((nch - 1) & 1 ? s1 : s0));
+    }
     if (owner && state_out) {
+        const int c0 = 32 * w;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
             *(float4*)&state_out[((int64_t)h * DV + r0 + i16) * DK + c0 + 16 * u + 4 * g4] =
@@ -639,7 +679,7 @@ int launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float*
     if (nch > 0)
         hipLaunchKernelGGL(gdn_prep<DK>, dim3((unsigned)(hv * nch)), dim3(256), 0, s, q, k, alpha, beta, n, hk, hv,
                            nch, rec);
-    hipLaunchKernelGGL((gdn_seq<DK, DV>), dim3((unsigned)(hv * (DV / kRS))), dim3(256), 0, s, q, k, v, state_in, n,
+    hipLaunchKernelGGL((gdn_seq<DK, DV>), dim3((unsigned)(hv * (DV / kRS))), dim3(Seq<DK, DV>::NT), 0, s, q, k, v, state_in, n,
                        hk, hv, nch, rec, out, state_out);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_EDEVICE;
 }
