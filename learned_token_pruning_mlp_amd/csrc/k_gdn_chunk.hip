@@ -23,11 +23,16 @@
 //    the two products that use them, already split, and gamma, beta and
 //    R(C-1, .), into one record of the workspace per (v head, chunk);
 //  * gdn_seq, one workgroup per 16 rows of a head's state, walks the chunks
-//    in order: K S0^T and Q S0^T (each of DK/32 waves owns a 32-column band
-//    of the rows, held in registers), U = diag(beta)(V - diag(gamma) K S0^T),
-//    W = T U, the outputs and the state update.  Each chunk's k, q and v rows
-//    and its record go through LDS by direct loads, two stages, the next
-//    chunk's in flight while this one is applied.
+//    in order with one barrier each.  Each of DK/32 owner waves holds a
+//    32-column band of the rows in registers and forms its band's share of
+//    K S0^T; after the barrier every owner sums the shares and forms all of
+//    U = diag(beta)(V - diag(gamma) K S0^T) and W = T U itself, with the
+//    tokens of the k dimension in the order the matrix cores leave them, so
+//    W goes from the product straight into its band's state update; its
+//    band's share of Q S0^T runs on the matrix cores meanwhile.  Two helper
+//    waves form the outputs one chunk late, off the state's chain.  Each
+//    chunk's k, q and v rows and its record go through LDS by direct loads,
+//    three stages, issued two chunks ahead.
 // The products run on 16x16x32 bf16 MFMA with fp32 accumulation.  k, q and v
 // are bf16 already; every fp32 operand (the state, T, U, M, W) is split into
 // three bf16 parts (hi + mid + lo, each the nearest bf16 to what the ones
@@ -125,11 +130,10 @@ __device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& mid, u3
     }
 }
 
-// fp32 x fp32 product of 8-wide operands on a 16x16x32 tile, the A operand
-// already split: the six cross terms above 2^-24, smallest first
-__device__ __forceinline__ f32x4 mfma16_x6s(u32x4 ah, u32x4 am, u32x4 al, const float* b, f32x4 acc) {
-    u32x4 bh, bm, bl;
-    split8(b, bh, bm, bl);
+// fp32 x fp32 product of 8-wide operands on a 16x16x32 tile, both split:
+// the six cross terms above 2^-24, smallest first
+__device__ __forceinline__ f32x4 mfma16_x6p(u32x4 ah, u32x4 am, u32x4 al, u32x4 bh, u32x4 bm, u32x4 bl,
+                                            f32x4 acc) {
     acc = mfma16(am, bm, acc);
     acc = mfma16(al, bh, acc);
     acc = mfma16(ah, bl, acc);
@@ -137,6 +141,21 @@ __device__ __forceinline__ f32x4 mfma16_x6s(u32x4 ah, u32x4 am, u32x4 al, const 
     acc = mfma16(ah, bm, acc);
     return mfma16(ah, bh, acc);
 }
+
+// the same with the A operand split and B given as fp32
+__device__ __forceinline__ f32x4 mfma16_x6s(u32x4 ah, u32x4 am, u32x4 al, const float* b, f32x4 acc) {
+    u32x4 bh, bm, bl;
+    split8(b, bh, bm, bl);
+    return mfma16_x6p(ah, am, al, bh, bm, bl, acc);
+}
+
+// The token order of the k dimension in the products over a chunk's tokens
+// that use T or M: k-slot e (0..7) of k-group g4 is token 4 g4 + e for e < 4
+// and 16 + 4 g4 + e - 4 above, the order in which a 16x16 product leaves a
+// lane's values of two 16-token blocks (D rows 4 g4 .. 4 g4 + 3 of each).
+// So W, formed as two such blocks, is the B operand of the state update and
+// of M W as it leaves the matrix cores, without a trip through LDS.
+__host__ __device__ constexpr int kslot(int g4, int e) { return e < 4 ? 4 * g4 + e : 12 + 4 * g4 + e; }
 
 __device__ __forceinline__ f32x4 mfma16_x6(const float* a, const float* b, f32x4 acc) {
     u32x4 ah, am, al;
@@ -342,14 +361,14 @@ __global__ __launch_bounds__(256) void gdn_prep(const uint16_t* __restrict__ q, 
     __syncthreads();
 
     // The record: waves 0, 1 split T's 16-token row block w, waves 2, 3 M's
-    // block w - 2, as the A operands (row 16 tb + i16, k = 8 g4 .. 8 g4 + 7)
+    // block w - 2, as the A operands (row 16 tb + i16, k-slots of k-group g4)
     uint8_t* r = rec + ((int64_t)h * nch + ch) * kRecBytes;
     {
         const int tb = w & 1;
         float(*src)[36] = w < 2 ? tm : mm;
         float a8[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a8[e] = src[16 * tb + i16][8 * g4 + e];
+        for (int e = 0; e < 8; ++e) a8[e] = src[16 * tb + i16][kslot(g4, e)];
         u32x4 parts[3];
         split8(a8, parts[0], parts[1], parts[2]);
         uint8_t* dst = r + (w < 2 ? kRecT : kRecM);
@@ -365,17 +384,18 @@ __global__ __launch_bounds__(256) void gdn_prep(const uint16_t* __restrict__ q, 
 
 // ---- the sequential pass: one workgroup per kRS rows of a head's state,
 // DK / 32 owner waves (each holds a 32-column band of the state) and two
-// helper waves
+// helper waves, one barrier a chunk
 template <int DK, int DV>
 struct Seq {
-    static constexpr int DW = DK / 32;          // owner waves
-    static constexpr int NT = 64 * (DW + 2);    // threads: the owners', then the helpers'
-    static constexpr int BAND = kCC * 32 * 2;   // bytes of a band's k (or q) values of a chunk
-    static constexpr int VB = kCC * kRS * 2;    // bytes of the workgroup's v values of a chunk
+    static constexpr int DW = DK / 32;         // owner waves
+    static constexpr int NT = 64 * (DW + 2);   // threads: the owners', then the helpers'
+    static constexpr int BAND = kCC * 32 * 2;  // bytes of a band's k (or q) values of a chunk
+    static constexpr int VB = kCC * kRS * 2;   // bytes of the workgroup's v values of a chunk
     static constexpr int RECB = kRecTail + 512;  // bytes of the record taken
-    static constexpr int OFF_V = DW * 2 * BAND;        // stage: the owners' bands (k, then q), v, the record
+    static constexpr int OFF_V = DW * 2 * BAND;  // stage: the owners' bands (k, then q), v, the record
     static constexpr int OFF_R = OFF_V + VB;
     static constexpr int STAGE = OFF_R + RECB;
+    static constexpr int NLOAD = 9;  // direct loads a helper wave issues per chunk
     static_assert(VB == 2 * 4 * 128, "v chunk in two 4-byte rounds of the helpers");
     static_assert(kRecM == 2 * 3 * 1024 && RECB <= kRecBytes, "a row block of T or M in three 1 KB loads");
     static_assert(DV % kRS == 0 && DW >= 1 && DW <= 4, "state slices");
@@ -391,20 +411,23 @@ __device__ __forceinline__ int band_off(int t, int cc) {
 
 template <int DK, int DV>
 __global__ __launch_bounds__(64 * (DK / 32 + 2)) void gdn_seq(const uint16_t* __restrict__ q,
-                                                          const uint16_t* __restrict__ k,
-                                                          const uint16_t* __restrict__ v, const float* state_in,
-                                                          int64_t n, int hk, int hv, int64_t nch,
-                                                          const uint8_t* __restrict__ rec, float* __restrict__ out,
-                                                          float* state_out) {  // state_out may be state_in
+                                                             const uint16_t* __restrict__ k,
+                                                             const uint16_t* __restrict__ v, const float* state_in,
+                                                             int64_t n, int hk, int hv, int64_t nch,
+                                                             const uint8_t* __restrict__ rec,
+                                                             float* __restrict__ out,
+                                                             float* state_out) {  // state_out may be state_in
     using C = Seq<DK, DV>;
     constexpr int DW = C::DW, BAND = C::BAND;
-    // one LDS object per stage, so the compiler can see that reads of one
-    // stage never alias the loads in flight into the other
+    // three stages, one LDS object each (so the compiler can see that reads of
+    // one never alias the loads in flight into another)
     __shared__ __attribute__((aligned(1024))) uint8_t stg0[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t stg1[C::STAGE];
-    __shared__ __attribute__((aligned(16))) float ppk[DW][kRS][36];     // per band: (K S0^T)^T
-    __shared__ __attribute__((aligned(16))) float ppq[2][DW][kRS][36];  // per band: (Q S0^T)^T, by chunk parity
-    __shared__ __attribute__((aligned(16))) float ww[2][kRS][36];       // W^T, by chunk parity
+    __shared__ __attribute__((aligned(1024))) uint8_t stg2[C::STAGE];
+    // by chunk parity, per band: (K S0^T)^T and (Q S0^T)^T; W^T
+    __shared__ __attribute__((aligned(16))) float ppk[2][DW][kRS][36];
+    __shared__ __attribute__((aligned(16))) float ppq[2][DW][kRS][36];
+    __shared__ __attribute__((aligned(16))) float ww[2][kRS][36];
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int i16 = lane & 15, g4 = lane >> 4;
     const int h = blockIdx.x / (DV / kRS), r0 = (blockIdx.x % (DV / kRS)) * kRS;
@@ -414,15 +437,15 @@ __global__ __launch_bounds__(64 * (DK / 32 + 2)) void gdn_seq(const uint16_t* __
     const bool owner = w < DW;
     const int tb = w - DW;  // a helper's 16-token block
 
-    // Loads of a chunk: each owner takes its band of the k and q rows (four
-    // 1 KB direct loads into its own region of the stage, read by it alone,
-    // so it waits for them by itself); the helpers take the workgroup's v
-    // values and the record, issued in a phase where they would otherwise
-    // wait and waited for before the chunk's first barrier.  The loads into a
-    // stage start while the other helper may still be reading the output
-    // operands of the chunk the stage held (M's row block and gamma of its
-    // half): each helper loads exactly those parts of the record that it
-    // alone reads there (T and M's row block tb, the tail of half tb).
+    // Loads of a chunk, two chunks ahead: each owner takes its band of the k
+    // and q rows (four 1 KB direct loads into its own region of the stage,
+    // read by it alone, so it waits for them by itself); the helpers take the
+    // workgroup's v values and the record, and wait for them before the
+    // barrier that precedes their use.  A stage is refilled while the other
+    // helper may still be reading the output operands of the chunk it held
+    // (M's row block and gamma of its half): each helper loads exactly those
+    // parts of the record that it alone reads there (T and M's row block tb,
+    // the tail of half tb).
     auto issue_band = [&](int64_t c, TG_LDS uint8_t* __restrict__ sb) {
         const int64_t t0 = c * kCC;
         TG_LDS uint8_t* bk = sb + w * 2 * BAND;
@@ -479,16 +502,6 @@ __global__ __launch_bounds__(64 * (DK / 32 + 2)) void gdn_seq(const uint16_t* __
         const u32x2 hi = *(const TG_LDS u32x2*)(b + band_off(t, 16 + 4 * g4));
         return u32x4{lo[0], lo[1], hi[0], hi[1]};
     };
-    // (X S0^T)^T of the band for both 16-token blocks of X (k or q rows) into dst
-    auto band_product = [&](const TG_LDS uint8_t* b, float (*dst)[36]) {
-        const u32x4 a0 = band_op(b, i16), a1 = band_op(b, 16 + i16);
-        f32x4 x0 = mfma16(a0, sl, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
-        f32x4 x1 = mfma16(a1, sl, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
-        x0 = mfma16(a0, sm, x0), x1 = mfma16(a1, sm, x1);
-        x0 = mfma16(a0, sh, x0), x1 = mfma16(a1, sh, x1);
-        *(float4*)&dst[i16][4 * g4] = float4{x0[0], x0[1], x0[2], x0[3]};
-        *(float4*)&dst[i16][16 + 4 * g4] = float4{x1[0], x1[1], x1[2], x1[3]};
-    };
 
     // The outputs of chunk cc, O = diag(gamma) Q S0^T + M W (the helpers, one
     // 16-token block each), formed one chunk late, off the state's chain: M's
@@ -513,13 +526,13 @@ __global__ __launch_bounds__(64 * (DK / 32 + 2)) void gdn_seq(const uint16_t* __
         float4 pq[DW];
 #pragma unroll
         for (int b = 0; b < DW; ++b) pq[b] = *(const float4*)&ppq[par][b][i16][16 * tb + 4 * g4];
-        const float4 w0 = *(const float4*)&ww[par][i16][8 * g4], w1 = *(const float4*)&ww[par][i16][8 * g4 + 4];
+        const float4 w0 = *(const float4*)&ww[par][i16][4 * g4], w1 = *(const float4*)&ww[par][i16][16 + 4 * g4];
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         float4 p = pq[0];
 #pragma unroll
         for (int b = 1; b < DW; ++b) p.x += pq[b].x, p.y += pq[b].y, p.z += pq[b].z, p.w += pq[b].w;
         f32x4 acc = {o.gm.x * p.x, o.gm.y * p.y, o.gm.z * p.z, o.gm.w * p.w};
-        const float b8[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        const float b8[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};  // W, tokens in k-slot order
         acc = mfma16_x6s(o.mh, o.mm, o.ml, b8, acc);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -528,103 +541,101 @@ __global__ __launch_bounds__(64 * (DK / 32 + 2)) void gdn_seq(const uint16_t* __
         }
     };
 
-    auto chunk = [&](int64_t ch, const TG_LDS uint8_t* __restrict__ cb, TG_LDS uint8_t* __restrict__ nb) {
+    // One chunk.  cb: its stage; ob: the stage of the chunk before, which
+    // takes the chunk two ahead.
+    auto chunk = [&](int64_t ch, const TG_LDS uint8_t* __restrict__ cb, TG_LDS uint8_t* __restrict__ ob) {
         const TG_LDS uint8_t* rb = cb + C::OFF_R;
         const int par = (int)(ch & 1);
-
-        // ---- A. owners: (K S0^T)^T of the band (their k and q bands landed,
-        // the next chunk's issued); helpers: the previous chunk's output
-        // operands from its stage, then the next chunk's v and record into it
-        OutOps prev;
         if (owner) {
-            TG_WAIT_VMCNT(0);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // done reading that stage's band
-            if (ch + 1 < nch) issue_band(ch + 1, nb);
-            band_product(cb + w * 2 * BAND, ppk[w]);
-        } else {
-            if (ch > 0) prev = out_ops(nb);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // its reads of that stage are done
-            if (ch + 1 < nch) issue_rest(ch + 1, nb);
-        }
-        lds_barrier();
-
-        // ---- B. helpers: U = diag(beta)(V - diag(gamma) K S0^T) as the B
-        // operand, W = T U (one 16-token block each; T's parts from the
-        // record); owners: (Q S0^T)^T of the band, and the update's operands
-        float rl8[8], gl = 0.0f;
-        u32x4 kt[2];
-        if (owner) {
-            band_product(cb + w * 2 * BAND + BAND, ppq[par][w]);
-            const lf4 r0v = *(const TG_LDS lf4*)(rb + rec_tail(kTailRl, 8 * g4));
-            const lf4 r1v = *(const TG_LDS lf4*)(rb + rec_tail(kTailRl, 8 * g4 + 4));
-            rl8[0] = r0v.x, rl8[1] = r0v.y, rl8[2] = r0v.z, rl8[3] = r0v.w;
-            rl8[4] = r1v.x, rl8[5] = r1v.y, rl8[6] = r1v.z, rl8[7] = r1v.w;
-            gl = *(const TG_LDS float*)(rb + rec_tail(kTailGam, kCC - 1));
-            // K^T of the band (rows: band columns 16 u + i16, k: tokens 8 g4 ..
-            // 8 g4 + 7), two transposing reads each: lane jj of a 16-lane group
-            // addresses token 8 g4 + 4 hh + jj / 4, columns 4 (jj % 4) .. +3
+            // ---- the band's (K S0^T)^T and its operands of Q S0^T, before the barrier
+            if (ch + 1 < nch)
+                TG_WAIT_VMCNT(4);  // this chunk's bands have landed (the next chunk's may be in flight)
+            else
+                TG_WAIT_VMCNT(0);
             const TG_LDS uint8_t* bk = cb + w * 2 * BAND;
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int t = 8 * g4 + 4 * hh + (i16 >> 2);
-                    const bf16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                        (TG_LDS bf16x4_t*)(bk + band_off(t, 16 * u + 4 * (i16 & 3))));
-                    const u32x2 xw = __builtin_bit_cast(u32x2, x);
-                    kt[u][2 * hh] = xw[0], kt[u][2 * hh + 1] = xw[1];
-                }
-        } else {
-            // every operand first, in one round of LDS reads: the band
-            // partials, v of tokens 8 g4 .. +7 in row i16 (transposing reads as
-            // for K^T), beta and gamma of those tokens, T's parts
+            const u32x4 ak0 = band_op(bk, i16), ak1 = band_op(bk, 16 + i16);
+            const u32x4 aq0 = band_op(bk + BAND, i16), aq1 = band_op(bk + BAND, 16 + i16);
+            if (ch + 2 < nch) issue_band(ch + 2, ob);  // its own reads of that stage ended a chunk ago
+            f32x4 x0 = mfma16(ak0, sl, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+            f32x4 x1 = mfma16(ak1, sl, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+            x0 = mfma16(ak0, sm, x0), x1 = mfma16(ak1, sm, x1);
+            x0 = mfma16(ak0, sh, x0), x1 = mfma16(ak1, sh, x1);
+            *(float4*)&ppk[par][w][i16][4 * g4] = float4{x0[0], x0[1], x0[2], x0[3]};
+            *(float4*)&ppk[par][w][i16][16 + 4 * g4] = float4{x1[0], x1[1], x1[2], x1[3]};
+            lds_barrier();
+
+            // ---- every owner forms all of U and W = T U itself, the k
+            // dimension (tokens) in k-slot order, so that W as it leaves the
+            // matrix cores is the B operand of the update.  All operands in one
+            // round of LDS reads: the band partials, v (transposing reads as
+            // for K^T), beta, gamma and R(C-1, .), T's parts, K^T of the band.
             float4 pk[DW][2];
 #pragma unroll
             for (int b = 0; b < DW; ++b)
-                pk[b][0] = *(const float4*)&ppk[b][i16][8 * g4], pk[b][1] = *(const float4*)&ppk[b][i16][8 * g4 + 4];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) pk[b][hh] = *(const float4*)&ppk[par][b][i16][4 * g4 + 16 * hh];
             u32x2 vw[2];
+            lf4 bt[2], gm[2], rv[2];
+            u32x4 kt[2];
             const TG_LDS uint8_t* vb = cb + C::OFF_V;
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                const int t = 8 * g4 + 4 * hh + (i16 >> 2);
+                const int t = 4 * g4 + 16 * hh + (i16 >> 2);  // the token this lane addresses
                 vw[hh] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                                                        (TG_LDS bf16x4_t*)(vb + 2 * (t * kRS + 4 * (i16 & 3)))));
-            }
-            lf4 bt[2], gm[2];
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                bt[hh] = *(const TG_LDS lf4*)(rb + rec_tail(kTailBet, 8 * g4 + 4 * hh));
-                gm[hh] = *(const TG_LDS lf4*)(rb + rec_tail(kTailGam, 8 * g4 + 4 * hh));
+                for (int u = 0; u < 2; ++u) {
+                    const u32x2 xw = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                                                   (TG_LDS bf16x4_t*)(bk + band_off(t, 16 * u + 4 * (i16 & 3)))));
+                    kt[u][2 * hh] = xw[0], kt[u][2 * hh + 1] = xw[1];
+                }
+                bt[hh] = *(const TG_LDS lf4*)(rb + rec_tail(kTailBet, 4 * g4 + 16 * hh));
+                gm[hh] = *(const TG_LDS lf4*)(rb + rec_tail(kTailGam, 4 * g4 + 16 * hh));
+                rv[hh] = *(const TG_LDS lf4*)(rb + rec_tail(kTailRl, 4 * g4 + 16 * hh));
             }
-            const TG_LDS u32x4* tp = (const TG_LDS u32x4*)(rb + kRecT) + tb * 3 * 64 + lane;
-            const u32x4 th = tp[0], tm = tp[64], tl = tp[128];
+            const float gl = *(const TG_LDS float*)(rb + rec_tail(kTailGam, kCC - 1));
+            u32x4 tpt[2][3];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const TG_LDS u32x4* tp = (const TG_LDS u32x4*)(rb + kRecT) + b * 3 * 64 + lane;
+                tpt[b][0] = tp[0], tpt[b][1] = tp[64], tpt[b][2] = tp[128];
+            }
+            // (Q S0^T)^T of the band meanwhile, for the outputs
+            f32x4 y0 = mfma16(aq0, sl, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+            f32x4 y1 = mfma16(aq1, sl, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+            y0 = mfma16(aq0, sm, y0), y1 = mfma16(aq1, sm, y1);
+            y0 = mfma16(aq0, sh, y0), y1 = mfma16(aq1, sh, y1);
+            __builtin_amdgcn_sched_barrier(0);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+
+            // U = diag(beta)(V - diag(gamma) K S0^T), this lane's eight (token, row i16)
             float u8[8];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                const float4 x = pk[0][hh];
-                float p4[4] = {x.x, x.y, x.z, x.w};
+                float p4[4] = {pk[0][hh].x, pk[0][hh].y, pk[0][hh].z, pk[0][hh].w};
 #pragma unroll
-                for (int b = 1; b < DW; ++b) {
-                    const float4 y = pk[b][hh];
-                    p4[0] += y.x, p4[1] += y.y, p4[2] += y.z, p4[3] += y.w;
-                }
+                for (int b = 1; b < DW; ++b)
+                    p4[0] += pk[b][hh].x, p4[1] += pk[b][hh].y, p4[2] += pk[b][hh].z, p4[3] += pk[b][hh].w;
                 const float v4[4] = {tgd::bf16lo(vw[hh][0]), tgd::bf16hi(vw[hh][0]), tgd::bf16lo(vw[hh][1]),
                                      tgd::bf16hi(vw[hh][1])};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) u8[4 * hh + e] = bt[hh][e] * (v4[e] - gm[hh][e] * p4[e]);
             }
-            const f32x4 acc = mfma16_x6s(th, tm, tl, u8, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
-            *(float4*)&ww[par][i16][16 * tb + 4 * g4] = float4{acc[0], acc[1], acc[2], acc[3]};
-        }
-        lds_barrier();
+            u32x4 uh, um, ul;
+            split8(u8, uh, um, ul);
+            // W's two 16-token blocks: lane (i16, g4) takes W(4 g4 + j, i16) and W(16 + 4 g4 + j, i16)
+            f32x4 wb0 = mfma16_x6p(tpt[0][0], tpt[0][1], tpt[0][2], uh, um, ul, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+            f32x4 wb1 = mfma16_x6p(tpt[1][0], tpt[1][1], tpt[1][2], uh, um, ul, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+            *(float4*)&ppq[par][w][i16][4 * g4] = float4{y0[0], y0[1], y0[2], y0[3]};
+            *(float4*)&ppq[par][w][i16][16 + 4 * g4] = float4{y1[0], y1[1], y1[2], y1[3]};
+            if (w == 0) {
+                *(float4*)&ww[par][i16][4 * g4] = float4{wb0[0], wb0[1], wb0[2], wb0[3]};
+                *(float4*)&ww[par][i16][16 + 4 * g4] = float4{wb1[0], wb1[1], wb1[2], wb1[3]};
+            }
 
-        // ---- C. owners: the band's update S^T <- gamma_last S^T + K^T
-        // diag(R(C-1, .)) W; helpers: the previous chunk's outputs
-        if (owner) {
-            const float4 w0 = *(const float4*)&ww[par][i16][8 * g4], w1 = *(const float4*)&ww[par][i16][8 * g4 + 4];
-            const float b8[8] = {rl8[0] * w0.x, rl8[1] * w0.y, rl8[2] * w0.z, rl8[3] * w0.w,
-                                 rl8[4] * w1.x, rl8[5] * w1.y, rl8[6] * w1.z, rl8[7] * w1.w};
+            // ---- the band's update S^T <- gamma_last S^T + K^T diag(R(C-1, .)) W
+            const float b8[8] = {rv[0][0] * wb0[0], rv[0][1] * wb0[1], rv[0][2] * wb0[2], rv[0][3] * wb0[3],
+                                 rv[1][0] * wb1[0], rv[1][1] * wb1[1], rv[1][2] * wb1[2], rv[1][3] * wb1[3]};
             u32x4 bh, bm, bl;
             split8(b8, bh, bm, bl);
 #pragma unroll
@@ -639,28 +650,49 @@ __global__ __launch_bounds__(64 * (DK / 32 + 2)) void gdn_seq(const uint16_t* __
             const float x8[8] = {sr[0][0], sr[0][1], sr[0][2], sr[0][3], sr[1][0], sr[1][1], sr[1][2], sr[1][3]};
             split8(x8, sh, sm, sl);
         } else {
-            TG_WAIT_VMCNT(0);  // the next chunk's v and record have landed (before the next barrier)
+            // ---- helpers: the previous chunk's output operands from its stage,
+            // the chunk two ahead into it, then that chunk's outputs
+            lds_barrier();
+            OutOps prev;
+            if (ch > 0) prev = out_ops(ob);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // its reads of that stage are done
+            if (ch + 2 < nch) {
+                issue_rest(ch + 2, ob);
+                TG_WAIT_VMCNT(C::NLOAD);  // the next chunk's v and record have landed
+            } else {
+                TG_WAIT_VMCNT(0);
+            }
             if (ch > 0) outputs(ch - 1, prev);
         }
     };
     TG_LDS uint8_t* s0 = (TG_LDS uint8_t*)stg0;
     TG_LDS uint8_t* s1 = (TG_LDS uint8_t*)stg1;
+    TG_LDS uint8_t* s2 = (TG_LDS uint8_t*)stg2;
     if (nch > 0) {
         if (owner) {
             issue_band(0, s0);
+            if (nch > 1) issue_band(1, s1);
         } else {
             issue_rest(0, s0);
-            TG_WAIT_VMCNT(0);
+            if (nch > 1) {
+                issue_rest(1, s1);
+                TG_WAIT_VMCNT(C::NLOAD);
+            } else {
+                TG_WAIT_VMCNT(0);
+            }
         }
     }
-    for (int64_t ch = 0; ch < nch; ch += 2) {
-        chunk(ch, s0, s1);
+    for (int64_t ch = 0; ch < nch; ch += 3) {
+        chunk(ch, s0, s2);
         if (ch + 1 < nch) chunk(ch + 1, s1, s0);
+        if (ch + 2 < nch) chunk(ch + 2, s2, s1);
     }
-    if (nch > 0 && !owner) {
-        // the last chunk's outputs (its Q S0^T partials and W are behind the
-        // last barrier)
-        outputs(nch - 1, out_ops((nch - 1) & 1 ? s1 : s0));
+    if (nch > 0) {
+        lds_barrier();  // the last chunk's Q S0^T partials and W
+        if (!owner) {
+            const int64_t cl = nch - 1;
+            outputs(cl, out_ops(cl % 3 == 0 ? s0 : (cl % 3 == 1 ? s1 : s2)));
+        }
     }
     if (owner && state_out) {
         const int c0 = 32 * w;
