@@ -651,8 +651,12 @@ __global__ __launch_bounds__(64 * (DK / 32 + 2)) void gdn_seq(const uint16_t* __
             split8(x8, sh, sm, sl);
         } else {
             // ---- helpers: the previous chunk's output operands from its stage,
-            // the chunk two ahead into it, then that chunk's outputs
+            // the chunk two ahead into it, then that chunk's outputs.  They
+            // start ~512 cycles after the barrier: their LDS reads and the
+            // loads they issue would otherwise land in the owners' round of LDS
+            // reads, which bounds the chunk.
             lds_barrier();
+            __builtin_amdgcn_s_sleep(8);
             OutOps prev;
             if (ch > 0) prev = out_ops(ob);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // its reads of that stage are done
