@@ -196,14 +196,18 @@ __global__ __launch_bounds__(256) void gdn_prep(const uint16_t* __restrict__ q, 
                                                 const float* __restrict__ alpha, const float* __restrict__ beta,
                                                 int64_t n, int hk, int hv, int64_t nch, uint8_t* __restrict__ rec) {
     using RW = Rows<DK>;
+    // LDS reused as the phases go (so that six workgroups fit on a CU): the
+    // chunk's k and q rows, then T and L10 T00 over them; the Gram products,
+    // then L and M in place
     __shared__ __attribute__((aligned(1024))) uint8_t stg[2 * RW::KQ + 2 * kCC * 4];
-    __shared__ __attribute__((aligned(16))) float gkk[kCC][36];  // k_t . k_i
-    __shared__ __attribute__((aligned(16))) float gqk[kCC][36];  // q_t . k_i
-    __shared__ __attribute__((aligned(16))) float lm[kCC][36];   // L
-    __shared__ __attribute__((aligned(16))) float mm[kCC][36];   // M
-    __shared__ __attribute__((aligned(16))) float tm[kCC][36];   // T = (I + L)^{-1}
-    __shared__ __attribute__((aligned(16))) float xx[16][20];    // L10 T00
+    __shared__ __attribute__((aligned(16))) float gkk[kCC][36];  // k_t . k_i, then L
+    __shared__ __attribute__((aligned(16))) float gqk[kCC][36];  // q_t . k_i, then M
     __shared__ __attribute__((aligned(16))) float gam[kCC], bet[kCC], rl[kCC];
+    static_assert(kCC * 36 * 4 + 16 * 20 * 4 <= 2 * RW::KQ, "T and L10 T00 over the k and q rows");
+    float(*const lm)[36] = gkk;
+    float(*const mm)[36] = gqk;
+    float(*const tm)[36] = reinterpret_cast<float(*)[36]>(stg);
+    float(*const xx)[20] = reinterpret_cast<float(*)[20]>(stg + kCC * 36 * 4);
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int i16 = lane & 15, g4 = lane >> 4;
     const int h = (int)(blockIdx.x / nch);
@@ -282,7 +286,8 @@ __global__ __launch_bounds__(256) void gdn_prep(const uint16_t* __restrict__ q, 
     }
     __syncthreads();
 
-    // L and M, a row quad a thread
+    // L and M, a row quad a thread, each over the Gram products it is formed
+    // from (a thread reads and writes only its own quad)
     {
         const int t = rt_t, c4 = rt_c;
         const float4 k4 = *(const float4*)&gkk[t][c4];
