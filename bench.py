@@ -517,12 +517,14 @@ def gate_backward(tg, torch, dev, shape, reps=5):
             "hbm_frac": round(byts / us / 1e3 / PEAK_HBM_GBS, 4)}
 
 
-def hybrid_mixer(tg, torch, dev, shape, reps=5):
+def hybrid_mixer(tg, torch, dev, shape, rounds=3):
     """The gated delta rule with 16 heads of 128 x 128 state over the kept
     tokens (K) and over the whole prompt (N): what pruning saves in an upper
     recurrent layer of the hybrid backbone.  Both forms: the chunked one on
     the matrix cores (tg_gated_delta_rule_chunked, the main figures) and the
-    scan (tg_gated_delta_rule, under "scan")."""
+    scan (tg_gated_delta_rule, under "scan").  Each figure is the median of
+    three rounds of back-to-back calls (20 over the kept tokens, 5 over the
+    prompt) after three warm-up calls."""
     heads, dk = 16, 128
     res, scan = {}, {}
     for name, t in (("kept", shape.k), ("full", shape.n)):
@@ -537,16 +539,21 @@ def hybrid_mixer(tg, torch, dev, shape, reps=5):
         ws = tg.gdn_workspace(t, heads, dev)
         forms = (("chunked", lambda: tg.tg_gated_delta_rule_chunked(q, k, v, alpha, beta, out, ws)),
                  ("scan", lambda: tg.tg_gated_delta_rule(q, k, v, alpha, beta, out)))
+        reps = 20 if name == "kept" else 5
         for form, fn in forms:
-            fn()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(reps):
+            for _ in range(3):
                 fn()
-            e1.record()
             torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / reps
+            per_round = []
+            for _ in range(rounds):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    fn()
+                e1.record()
+                torch.cuda.synchronize()
+                per_round.append(e0.elapsed_time(e1) * 1e3 / reps)
+            us = sorted(per_round)[len(per_round) // 2]
             (res if form == "chunked" else scan)[name] = {"tokens": t, "us": round(us, 1),
                                                           "ns_per_token": round(us * 1e3 / t, 1)}
         del ws
