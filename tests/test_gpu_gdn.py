@@ -129,26 +129,27 @@ def test_gated_delta_rule_chunked_deterministic():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
-def test_gated_delta_rule_chunked_deterministic_at_length():
+@pytest.mark.parametrize("T,hk,hv,dk,dv", [(16384, 16, 16, 128, 128), (8191, 2, 8, 64, 64)])
+def test_gated_delta_rule_chunked_deterministic_at_length(T, hk, hv, dk, dv):
     """At the hybrid mixer's full shape (16384 kept tokens, 16 heads of 128,
-    512 chunks, inputs far beyond the caches) three chunked calls agree bit
-    for bit, and with the scan to the relative RMS bound above."""
-    T, h, d = 16384, 16, 128
-    gu.say(f"gated delta rule (chunked) determinism at T={T}, {h} heads")
+    512 chunks, inputs far beyond the caches), and with 64-wide heads shared
+    four ways over a ragged 8191 tokens, three chunked calls agree bit for
+    bit, and with the scan to the relative RMS bound above."""
+    gu.say(f"gated delta rule (chunked) determinism at T={T}, hk={hk}, hv={hv}, dk={dk}, dv={dv}")
     g = torch.Generator(device=gu.dev())
-    g.manual_seed(16384)
+    g.manual_seed(T)
 
     def unit(*shape):
         x = torch.randn(*shape, generator=g, device=gu.dev())
         return (x / x.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
-    q, k = unit(T, h, d), unit(T, h, d)
-    v = torch.randn(T, h, d, generator=g, device=gu.dev()).to(torch.bfloat16)
-    alpha = torch.rand(T, h, generator=g, device=gu.dev()) * 0.1 + 0.9
-    beta = torch.rand(T, h, generator=g, device=gu.dev())
+    q, k = unit(T, hk, dk), unit(T, hk, dk)
+    v = torch.randn(T, hv, dv, generator=g, device=gu.dev()).to(torch.bfloat16)
+    alpha = torch.rand(T, hv, generator=g, device=gu.dev()) * 0.1 + 0.9
+    beta = torch.rand(T, hv, generator=g, device=gu.dev())
     outs = []
     for form in ("chunked", "chunked", "chunked", "scan"):
-        out = torch.empty(T, h, d, dtype=torch.float32, device=gu.dev())
-        so = torch.empty(h, d, d, dtype=torch.float32, device=gu.dev())
+        out = torch.empty(T, hv, dv, dtype=torch.float32, device=gu.dev())
+        so = torch.empty(hv, dv, dk, dtype=torch.float32, device=gu.dev())
         _mixer(form, q, k, v, alpha, beta, out, None, so)
         outs.append((out, so))
     torch.cuda.synchronize()
